@@ -1,0 +1,170 @@
+"""Seeded synthetic workloads: shapes, lengths and random rows.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+holds no step of the method (no attention, no block allocation, no append):
+only the sizes of each workload and the random numbers that fill it, so that
+the HIP path and the CPU oracle are fed bit-identical inputs.
+
+Random streams: every array is drawn from
+``numpy.random.default_rng([seed, stream, *ids])`` so any one sequence can be
+regenerated alone.  Stream ids: 0 lengths, 1 pool permutation, 2 cached keys,
+3 cached values, 4 queries, 5 new keys, 6 new values.  Values are float32
+N(0, 1) draws, stored as bfloat16 by rounding to nearest even where the
+workload is bf16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+S_LENGTHS, S_POOL, S_KCACHE, S_VCACHE, S_Q, S_KNEW, S_VNEW = range(7)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str  # "bf16" | "f32"
+    block_size: int  # 0 = contiguous cache
+    n_q: int  # query rows (= new tokens) per sequence per step
+    len_lo: int  # attended length range after the step's append, inclusive
+    len_hi: int
+    steps: int = 1  # successive decode steps (the cache grows by n_q each step)
+    description: str = ""
+
+    @property
+    def esize(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+WORKLOADS = {w.name: w for w in [
+    Workload("gptlite-f32-b2-h4-d64-ctx256-32steps", seed=1, B=2, Hq=4, Hkv=4, D=64, dtype="f32",
+             block_size=0, n_q=1, len_lo=257, len_hi=257, steps=32,
+             description="tiny GPTlite-shaped layer: 256 cached tokens + 1, then 32 decode "
+                         "steps, contiguous fp32 cache"),
+    Workload("llama2-13b-layer-contig-b16-ctx2048", seed=2, B=16, Hq=40, Hkv=40, D=128,
+             dtype="bf16", block_size=0, n_q=1, len_lo=2048, len_hi=2048,
+             description="Llama-2-13B-shaped layer decode, contiguous bf16 cache, batch 16, "
+                         "context 2048"),
+    Workload("mha40-paged-b64-ctx128to4096", seed=3, B=64, Hq=40, Hkv=40, D=128, dtype="bf16",
+             block_size=16, n_q=1, len_lo=128, len_hi=4096,
+             description="40-head MHA paged decode, block 16, batch 64, lengths U[128, 4096]"),
+    Workload("gqa32x8-paged-b128-ctx256to8192", seed=4, B=128, Hq=32, Hkv=8, D=128,
+             dtype="bf16", block_size=16, n_q=1, len_lo=256, len_hi=8192,
+             description="GQA 32 q / 8 kv heads paged decode, block 16, batch 128, lengths "
+                         "U[256, 8192]"),
+    Workload("verify5-gqa32x8-paged-b32-ctx1024to4096", seed=5, B=32, Hq=32, Hkv=8, D=128,
+             dtype="bf16", block_size=16, n_q=5, len_lo=1024 + 5, len_hi=4096 + 5,
+             description="speculative verify: 4 drafts + 1, GQA 32/8, paged block 16, batch 32, "
+                         "cached lengths U[1024, 4096]"),
+]}
+
+# short aliases, in the order the workloads are listed above
+ALIASES = {"C%d" % (i + 1): n for i, n in enumerate(WORKLOADS)}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[ALIASES.get(name, name)]
+
+
+def rng(w: Workload, stream: int, *ids: int) -> np.random.Generator:
+    return np.random.default_rng([w.seed, stream, *ids])
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def normal(w: Workload, shape, stream: int, *ids: int) -> np.ndarray:
+    return encode(rng(w, stream, *ids).standard_normal(shape, dtype=np.float32), w.dtype)
+
+
+def final_lengths(w: Workload) -> np.ndarray:
+    """Attended length of every sequence after the first step's append."""
+    if w.len_lo == w.len_hi:
+        return np.full(w.B, w.len_lo, dtype=np.int32)
+    return rng(w, S_LENGTHS).integers(w.len_lo, w.len_hi + 1, size=w.B).astype(np.int32)
+
+
+def cached_lengths(w: Workload) -> np.ndarray:
+    """Tokens already in the cache before the first step."""
+    return final_lengths(w) - w.n_q
+
+
+def capacity_tokens(w: Workload) -> int:
+    """Longest sequence after all steps: the contiguous cache's S_max."""
+    return int(final_lengths(w).max()) + (w.steps - 1) * w.n_q
+
+
+def max_blocks_per_seq(w: Workload) -> int:
+    bs = w.block_size
+    return (capacity_tokens(w) + bs - 1) // bs
+
+
+def pool_blocks(w: Workload) -> int:
+    """Pool size: every sequence's blocks after all steps, plus one spare each."""
+    bs = w.block_size
+    last = final_lengths(w) + (w.steps - 1) * w.n_q
+    return int(((last + bs - 1) // bs).sum()) + w.B
+
+
+def free_list(w: Workload) -> np.ndarray:
+    return rng(w, S_POOL).permutation(pool_blocks(w)).astype(np.int32)
+
+
+def cache_rows(w: Workload, which: str, b: int, n: int) -> np.ndarray:
+    """The n cached key (which='k') or value ('v') rows of sequence b: [n, Hkv, D]."""
+    return normal(w, (n, w.Hkv, w.D), S_KCACHE if which == "k" else S_VCACHE, b)
+
+
+def new_rows(w: Workload, which: str, b: int, step: int = 0) -> np.ndarray:
+    """The n_q new key/value rows of sequence b at a decode step: [n_q, Hkv, D]."""
+    return normal(w, (w.n_q, w.Hkv, w.D), S_KNEW if which == "k" else S_VNEW, b, step)
+
+
+def queries(w: Workload, b: int, step: int = 0) -> np.ndarray:
+    """Sequence b's query rows at a decode step: [n_q, Hq, D]."""
+    return normal(w, (w.n_q, w.Hq, w.D), S_Q, b, step)
+
+
+def cu_from_counts(counts) -> np.ndarray:
+    """[B] token counts -> [B+1] offsets into a packed token array."""
+    cu = np.zeros(len(counts) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(counts, dtype=np.int64))
+    return cu
+
+
+def packed_cache_rows(w: Workload, which: str, lengths) -> np.ndarray:
+    """All sequences' cached rows packed in batch order: [sum(lengths), Hkv, D]."""
+    parts = [cache_rows(w, which, b, int(n)) for b, n in enumerate(lengths)]
+    return np.concatenate(parts, axis=0) if parts else np.zeros((0, w.Hkv, w.D))
+
+
+def packed_new_rows(w: Workload, which: str, step: int = 0) -> np.ndarray:
+    return np.concatenate([new_rows(w, which, b, step) for b in range(w.B)], axis=0)
+
+
+def packed_queries(w: Workload, step: int = 0) -> np.ndarray:
+    """[B, n_q, Hq, D]"""
+    return np.stack([queries(w, b, step) for b in range(w.B)], axis=0)
+
+
+def custom(name="custom", seed=0, B=2, Hq=4, Hkv=4, D=64, dtype="bf16", block_size=0, n_q=1,
+           len_lo=16, len_hi=16, steps=1) -> Workload:
+    """A small workload for tests (same generators, other sizes)."""
+    return Workload(name, seed, B, Hq, Hkv, D, dtype, block_size, n_q, len_lo, len_hi, steps)

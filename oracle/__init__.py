@@ -1,0 +1,214 @@
+"""CPU oracle for KV-cache decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library never does: it shares no
+code with the oracle, and the oracle shares none with it.
+
+The arithmetic lives in ``kvc_oracle.c`` (plain C, double precision); this
+module only marshals numpy arrays into it through ctypes and builds the shared
+object with gcc when it is missing.  Each wrapper names the C function it
+calls; the citations of the pages are at those C functions.
+
+Element types: ``"bf16"`` arrays are passed as their raw 16-bit patterns
+(``numpy.uint16``), ``"f32"`` arrays as ``numpy.float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvc_oracle.c")
+_LIB = os.path.join(_HERE, "libkvc_oracle.so")
+
+DTYPES = {"bf16": 0, "f32": 1}
+NP_DTYPES = {"bf16": np.uint16, "f32": np.float32}
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc into ``out`` (plain -O2, no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+             "-Wall", "-Werror", src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle shared object."""
+
+    def __init__(self, path: str | None = None):
+        if path is None:
+            path = build(force=False)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.kvc_ref_round_bf16.argtypes = [ctypes.c_double]
+        lib.kvc_ref_round_bf16.restype = ctypes.c_uint16
+        lib.kvc_ref_block_table.argtypes = [I, I, I, I, P, P, P, P, P, P]
+        lib.kvc_ref_append.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        lib.kvc_ref_gather.argtypes = [I, I, I, I, I, I, I, I, I, P, P, P]
+        lib.kvc_ref_attention.argtypes = [I, I, I, I, I, I, P, P, P, ctypes.c_double, P]
+        lib.kvc_ref_cache_attention.argtypes = [I, I, I, I, I, I, I, I, I, I, P, P, P, P, P,
+                                                ctypes.c_double, P, P]
+        lib.kvc_ref_attention_split.argtypes = [I, I, I, I, I, I, P, P, P, ctypes.c_double,
+                                                I, P]
+        for name in ("kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
+                     "kvc_ref_attention", "kvc_ref_cache_attention",
+                     "kvc_ref_attention_split"):
+            getattr(lib, name).restype = ctypes.c_int
+        self.lib = lib
+
+    # -- helpers --------------------------------------------------------
+    @staticmethod
+    def _p(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    @staticmethod
+    def _c(a, dtype):
+        a = np.ascontiguousarray(a)
+        if a.dtype != dtype:
+            raise TypeError("expected %s, got %s" % (np.dtype(dtype), a.dtype))
+        return a
+
+    # -- kvc_ref_round_bf16 -------------------------------------------------
+    def round_bf16(self, x) -> np.ndarray:
+        """Round doubles once (nearest, ties to even) to bf16 bit patterns."""
+        x = np.asarray(x, dtype=np.float64)
+        flat = [self.lib.kvc_ref_round_bf16(float(v)) for v in x.ravel()]
+        return np.array(flat, dtype=np.uint16).reshape(x.shape)
+
+    # -- kvc_ref_block_table ------------------------------------------------
+    def block_table(self, seq_lens, cu_new, table, free_list, head, bs):
+        """Returns (status, table', head', slots); inputs are not modified."""
+        seq_lens = self._c(seq_lens, np.int32)
+        cu_new = self._c(cu_new, np.int32)
+        table = self._c(table, np.int32).copy()
+        free_list = self._c(free_list, np.int32)
+        B, max_blocks = table.shape
+        h = np.array([head], dtype=np.int32)
+        slots = np.full(max(int(cu_new[-1]), 1), -1, dtype=np.int32)
+        st = self.lib.kvc_ref_block_table(B, bs, max_blocks, len(free_list), self._p(seq_lens),
+                                          self._p(cu_new), self._p(table), self._p(free_list),
+                                          self._p(h), self._p(slots))
+        return st, table, int(h[0]), slots[:int(cu_new[-1])]
+
+    # -- kvc_ref_append -----------------------------------------------------
+    def append(self, k_new, v_new, seq_lens, cu_new, k_cache, v_cache, bs=0, slots=None):
+        """In-place append into k_cache/v_cache (numpy); returns (status, seq_lens_out).
+
+        contiguous: caches [B, Hkv, S_max, D]; paged: pools [N, Hkv, bs, D]."""
+        seq_lens = self._c(seq_lens, np.int32)
+        cu_new = self._c(cu_new, np.int32)
+        k_new = np.ascontiguousarray(k_new)
+        v_new = np.ascontiguousarray(v_new)
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        B = len(seq_lens)
+        Hkv, D = k_cache.shape[1], k_cache.shape[3]
+        esize = k_cache.dtype.itemsize
+        if bs == 0:
+            S_max, N = k_cache.shape[2], 0
+        else:
+            S_max, N = 0, k_cache.shape[0]
+            slots = self._c(slots, np.int32)
+        out = np.zeros(B, dtype=np.int32)
+        st = self.lib.kvc_ref_append(B, Hkv, D, esize, bs, S_max, N, self._p(k_new),
+                                     self._p(v_new), self._p(seq_lens), self._p(cu_new),
+                                     self._p(slots), self._p(k_cache), self._p(v_cache),
+                                     self._p(out))
+        return st, out
+
+    # -- kvc_ref_gather -----------------------------------------------------
+    def gather(self, cache, b, L, bs=0, table=None):
+        """Sequence b's first L rows as a [Hkv, L, D] array (same dtype)."""
+        Hkv, D = cache.shape[1], cache.shape[3]
+        if bs == 0:
+            S_max, max_blocks, N = cache.shape[2], 1, 0
+        else:
+            table = self._c(table, np.int32)
+            S_max, max_blocks, N = 0, table.shape[1], cache.shape[0]
+        out = np.zeros((Hkv, L, D), dtype=cache.dtype)
+        st = self.lib.kvc_ref_gather(b, L, Hkv, D, cache.dtype.itemsize, bs, S_max, max_blocks,
+                                     N, self._p(table), self._p(np.ascontiguousarray(cache)),
+                                     self._p(out))
+        if st != 0:
+            raise ValueError("gather failed: %d" % st)
+        return out
+
+    # -- kvc_ref_attention --------------------------------------------------
+    def attention(self, q, k, v, scale, dtype):
+        """q [n_q, Hq, D], k/v [Hkv, L, D] -> out [n_q, Hq, D] float64."""
+        nd = NP_DTYPES[dtype]
+        q, k, v = self._c(q, nd), self._c(k, nd), self._c(v, nd)
+        n_q, Hq, D = q.shape
+        Hkv, L, _ = k.shape
+        out = np.zeros((n_q, Hq, D), dtype=np.float64)
+        st = self.lib.kvc_ref_attention(n_q, Hq, Hkv, D, L, DTYPES[dtype], self._p(q),
+                                        self._p(k), self._p(v), float(scale), self._p(out))
+        if st != 0:
+            raise ValueError("attention failed: %d" % st)
+        return out
+
+    # -- kvc_ref_attention_split --------------------------------------------
+    def attention_split(self, q, k, v, scale, dtype, P):
+        nd = NP_DTYPES[dtype]
+        q, k, v = self._c(q, nd), self._c(k, nd), self._c(v, nd)
+        n_q, Hq, D = q.shape
+        Hkv, L, _ = k.shape
+        out = np.zeros((n_q, Hq, D), dtype=np.float64)
+        st = self.lib.kvc_ref_attention_split(n_q, Hq, Hkv, D, L, DTYPES[dtype], self._p(q),
+                                              self._p(k), self._p(v), float(scale), int(P),
+                                              self._p(out))
+        if st != 0:
+            raise ValueError("attention_split failed: %d" % st)
+        return out
+
+    # -- kvc_ref_cache_attention --------------------------------------------
+    def cache_attention(self, q, k_cache, v_cache, seq_lens, scale, dtype, bs=0, table=None,
+                        rows_only=None):
+        """q [B, n_q, Hq, D] over a contiguous [B,Hkv,S_max,D] or paged [N,Hkv,bs,D]
+        cache -> (status, out [B, n_q, Hq, D] float64)."""
+        nd = NP_DTYPES[dtype]
+        q = self._c(q, nd)
+        B, n_q, Hq, D = q.shape
+        Hkv = k_cache.shape[1]
+        seq_lens = self._c(seq_lens, np.int32)
+        if bs == 0:
+            S_max, max_blocks, N = k_cache.shape[2], 1, 0
+        else:
+            table = self._c(table, np.int32)
+            S_max, max_blocks, N = 0, table.shape[1], k_cache.shape[0]
+        ro = None
+        if rows_only is not None:
+            ro = self._c(np.asarray(rows_only, dtype=np.uint8).reshape(B, Hq), np.uint8)
+        out = np.zeros((B, n_q, Hq, D), dtype=np.float64)
+        st = self.lib.kvc_ref_cache_attention(
+            B, n_q, Hq, Hkv, D, DTYPES[dtype], bs, S_max, max_blocks, N, self._p(q),
+            self._p(self._c(k_cache, nd)), self._p(self._c(v_cache, nd)), self._p(seq_lens),
+            self._p(table), float(scale), self._p(ro), self._p(out))
+        return st, out
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built from this directory's source (compiled on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def widen(a, dtype) -> np.ndarray:
+    """Exact float64 view of stored elements (bf16 bit patterns or float32)."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

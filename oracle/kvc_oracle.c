@@ -1,0 +1,410 @@
+/*
+ * kvc_oracle.c -- plain, slow CPU oracle for KV-cache decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library links, includes or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg load it.  It shares no code, header, table or constant with the HIP
+ * path.
+ *
+ * Every floating-point step runs in double precision on the exact input
+ * values (bf16 inputs are widened exactly).  There is no blocking, fusion or
+ * reordering beyond the definitions cited at each function.
+ *
+ * Sources (the four web pages this library follows):
+ *   [I1] "Inference-1", brunomaga.github.io -- sections "KV cache",
+ *        "PagedAttention: memory management for the KV cache", "FlashAttention",
+ *        "FlashDecoding", "Smaller KV caches: MQA, GQA and MLA".
+ *   [VN] "Inference o quy mo lon: KV cache, prefill va decode",
+ *        blog.truongducdung.dev -- section 05 "PagedAttention va prefix
+ *        caching" (sub-section "Block table") and section 07 "FlashAttention"
+ *        (sub-section "Online softmax").
+ *   [I2] "Inference-2", brunomaga.github.io -- sections "Draft-model
+ *        speculative decoding" and "CUDA graphs".
+ *   [EI] "Efficient Inference", learn.obvix.io -- the KV-cache passage (static
+ *        cache written in place) and the paged-attention passage (block table).
+ *
+ * Parity pins: every function here is pinned by CPU tests against closed
+ * forms, brute force, library routines and the pages' printed numbers; none is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* status codes (the same integers the library returns; values restated here) */
+#define REF_OK 0
+#define REF_ERR_ARG (-1)
+#define REF_ERR_CAPACITY (-5)
+#define REF_ERR_NO_BLOCKS (-6)
+#define REF_ERR_DATA (-8)
+
+/* element types: 0 = bfloat16 (1 sign, 8 exponent, 7 mantissa bits), 1 = IEEE float32 */
+#define REF_BF16 0
+#define REF_F32 1
+
+/* Exact widening of one stored element to double.  A bf16 value is the upper
+ * half of the float32 with the same bits ([I2] "Quantization", number-format
+ * table: bf16 keeps float32's 8-bit exponent and 7 of its mantissa bits). */
+static double load_elem(const void* base, size_t idx, int dtype) {
+  if (dtype == REF_F32) return (double)((const float*)base)[idx];
+  uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a double once, to nearest with ties to even, to bf16 (8 significant
+ * bits, exponent range of float32).  Returns the raw 16-bit pattern. */
+uint16_t kvc_ref_round_bf16(double x) {
+  if (isnan(x)) return 0x7FC0;
+  double ax = fabs(x);
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (ax == 0.0) return sign;
+  int e;
+  frexp(ax, &e); /* ax in [2^(e-1), 2^e) */
+  int eq = e < -125 ? -125 : e; /* below 2^-126 the spacing stays 2^-133 */
+  double ulp = ldexp(1.0, eq - 8);
+  double r = nearbyint(ax / ulp) * ulp; /* default rounding mode: ties to even */
+  if (r > 3.38953138925153547590470800371487866880e+38) return sign | 0x7F80; /* +-inf */
+  float f = (float)r; /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block table: on-demand allocation of fixed-size blocks.
+ *
+ * [I1] "PagedAttention": the cache is split into fixed-size blocks allocated
+ * on demand, and a per-sequence table maps logical blocks to physical ones.
+ * [VN] 05 "Block table": a new block is taken only when the last one is full,
+ * so at most the tail of the last block is wasted; default 16 tokens.
+ * [EI] paged-attention passage: the table maps logical token positions to
+ * physical block indices; blocks come from a free pool.
+ *
+ * Reading of the unstated order: sequences in batch order, each sequence's
+ * missing logical blocks in increasing order, the free list consumed front to
+ * back.  All or nothing: on any error nothing is written.
+ *
+ * seq_lens[b] tokens are already held in ceil(seq_lens[b]/bs) blocks; the new
+ * tokens of sequence b are cu_new[b] .. cu_new[b+1]-1.  The token at logical
+ * position pos lives in slot table[b][pos/bs]*bs + pos%bs.
+ */
+int kvc_ref_block_table(int B, int bs, int max_blocks, int N, const int32_t* seq_lens,
+                        const int32_t* cu_new, int32_t* table, const int32_t* free_list,
+                        int32_t* head, int32_t* slots) {
+  if (B < 0 || bs <= 0 || max_blocks <= 0 || N < 0) return REF_ERR_ARG;
+  long need = 0;
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b];
+    long n = (long)cu_new[b + 1] - cu_new[b];
+    if (len < 0 || n < 0) return REF_ERR_DATA;
+    long have = (len + bs - 1) / bs;
+    long want = (len + n + bs - 1) / bs;
+    if (want > max_blocks) return REF_ERR_CAPACITY;
+    need += want - have;
+  }
+  if (*head < 0 || (long)*head + need > N) return REF_ERR_NO_BLOCKS;
+
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b];
+    long n = (long)cu_new[b + 1] - cu_new[b];
+    long have = (len + bs - 1) / bs;
+    long want = (len + n + bs - 1) / bs;
+    for (long i = have; i < want; ++i) {
+      table[(long)b * max_blocks + i] = free_list[*head];
+      *head += 1;
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b];
+    long n = (long)cu_new[b + 1] - cu_new[b];
+    for (long t = 0; t < n; ++t) {
+      long pos = len + t;
+      long blk = table[(long)b * max_blocks + pos / bs];
+      slots[cu_new[b] + t] = (int32_t)(blk * bs + pos % bs);
+    }
+  }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Append: write the new tokens' key and value rows into the cache in place.
+ *
+ * [EI] KV-cache passage: the static cache is preallocated for the maximum
+ * length, the new rows are written into the slice at the current length, the
+ * length grows by the number of new tokens, and writing past the capacity is
+ * an error.  [I2] "CUDA graphs": the static cache is written in place at the
+ * new tokens' positions.  [I1] "KV cache": only the new token's key and value
+ * are computed and appended; everything cached stays untouched.
+ *
+ * Layouts (element = esize bytes, copied bit for bit, no conversion):
+ *   new rows  k_new, v_new : [total_new][Hkv][D], sequence b owns rows
+ *                            cu_new[b] .. cu_new[b+1]-1
+ *   contiguous (bs == 0)   : cache [B][Hkv][S_max][D]
+ *   paged      (bs  > 0)   : pool  [N][Hkv][bs][D], token i goes to slot slots[i]
+ * seq_lens_out[b] = seq_lens[b] + n_new_b, or seq_lens[b] when sequence b was
+ * refused.  Returns the first error met (other sequences are still written).
+ */
+int kvc_ref_append(int B, int Hkv, int D, int esize, int bs, int S_max, int N, const void* k_new,
+                   const void* v_new, const int32_t* seq_lens, const int32_t* cu_new,
+                   const int32_t* slots, void* k_cache, void* v_cache, int32_t* seq_lens_out) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || esize <= 0 || bs < 0) return REF_ERR_ARG;
+  int status = REF_OK;
+  size_t row = (size_t)D * esize;
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b];
+    long n = (long)cu_new[b + 1] - cu_new[b];
+    seq_lens_out[b] = (int32_t)len;
+    if (len < 0 || n < 0) {
+      if (status == REF_OK) status = REF_ERR_DATA;
+      continue;
+    }
+    if (bs == 0 && len + n > S_max) {
+      if (status == REF_OK) status = REF_ERR_CAPACITY;
+      continue;
+    }
+    int ok = 1;
+    if (bs > 0)
+      for (long t = 0; t < n; ++t) {
+        long s = slots[cu_new[b] + t];
+        if (s < 0 || s >= (long)N * bs) ok = 0;
+      }
+    if (!ok) {
+      if (status == REF_OK) status = REF_ERR_DATA;
+      continue;
+    }
+    for (long t = 0; t < n; ++t) {
+      long src_tok = cu_new[b] + t;
+      for (int g = 0; g < Hkv; ++g) {
+        size_t src = ((size_t)src_tok * Hkv + g) * row;
+        size_t dst;
+        if (bs == 0) {
+          dst = (((size_t)b * Hkv + g) * S_max + (size_t)(len + t)) * row;
+        } else {
+          long s = slots[src_tok];
+          dst = (((size_t)(s / bs) * Hkv + g) * bs + (size_t)(s % bs)) * row;
+        }
+        memcpy((char*)k_cache + dst, (const char*)k_new + src, row);
+        memcpy((char*)v_cache + dst, (const char*)v_new + src, row);
+      }
+    }
+    seq_lens_out[b] = (int32_t)(len + n);
+  }
+  return status;
+}
+
+/* Element index of key/value j of sequence b, KV head g, in a contiguous or
+ * paged cache; -1 when the block table points outside the pool. */
+static long cache_row(int b, int g, long j, int Hkv, int D, int bs, int S_max, int max_blocks,
+                      int N, const int32_t* table) {
+  if (bs == 0) return (((long)b * Hkv + g) * S_max + j) * D;
+  long blk = table[(long)b * max_blocks + j / bs];
+  if (blk < 0 || blk >= N) return -1;
+  return ((blk * Hkv + g) * bs + j % bs) * D;
+}
+
+/* Gather sequence b's first L logical rows, in token order, out of a cache
+ * into a plain [Hkv][L][D] array (bytes copied unchanged).  Used to compare a
+ * paged cache with a contiguous one. */
+int kvc_ref_gather(int b, int L, int Hkv, int D, int esize, int bs, int S_max, int max_blocks,
+                   int N, const int32_t* table, const void* cache, void* out) {
+  size_t row = (size_t)D * esize;
+  for (int g = 0; g < Hkv; ++g)
+    for (long j = 0; j < L; ++j) {
+      long e = cache_row(b, g, j, Hkv, D, bs, S_max, max_blocks, N, table);
+      if (e < 0) return REF_ERR_DATA;
+      memcpy((char*)out + (((size_t)g * L + j) * row), (const char*)cache + (size_t)e * esize, row);
+    }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention of n_q new query rows over L cached keys of one sequence.
+ *
+ * Definition ([I1] "Why attention matters"): softmax(Q K^T / sqrt(d)) V, with
+ * the scale passed in.  Mask ([I1] "KV cache", the function that attends Sq new
+ * tokens over Sk keys): when Sq > 1, new row r sees keys 0 .. Sk - Sq + r (a
+ * lower-triangular mask shifted by Sk - Sq); a single row sees every key,
+ * including its own just-appended one.  Grouping ([I1] "Smaller KV caches",
+ * the GQA class; [EI] minimal GQA forward): with G = Hq / Hkv, query head h
+ * reads KV head h / G (consecutive heads share a group).
+ *
+ * Layouts: q [n_q][Hq][D], k and v [Hkv][L][D] (elements of type dtype),
+ * out [n_q][Hq][D] in double.  Every step in double: scores, maximum,
+ * exponentials, sum, weighted sum, one division.
+ */
+int kvc_ref_attention(int n_q, int Hq, int Hkv, int D, int L, int dtype, const void* q,
+                      const void* k, const void* v, double scale, double* out) {
+  if (n_q <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return REF_ERR_ARG;
+  if (Hq % Hkv != 0) return REF_ERR_ARG;
+  if (L < n_q) return REF_ERR_DATA;
+  int G = Hq / Hkv;
+  double* p = (double*)malloc(sizeof(double) * (size_t)L);
+  if (!p) return REF_ERR_ARG;
+  for (int r = 0; r < n_q; ++r)
+    for (int h = 0; h < Hq; ++h) {
+      int g = h / G;
+      long last = (long)L - n_q + r; /* keys 0..last are visible */
+      double m = -INFINITY;
+      for (long j = 0; j <= last; ++j) {
+        double s = 0.0;
+        for (int d = 0; d < D; ++d)
+          s += load_elem(q, ((size_t)r * Hq + h) * D + d, dtype) *
+               load_elem(k, ((size_t)g * L + j) * D + d, dtype);
+        p[j] = s * scale;
+        if (p[j] > m) m = p[j];
+      }
+      double l = 0.0;
+      for (long j = 0; j <= last; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+      }
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (long j = 0; j <= last; ++j) acc += p[j] * load_elem(v, ((size_t)g * L + j) * D + d, dtype);
+        out[((size_t)r * Hq + h) * D + d] = acc / l;
+      }
+    }
+  free(p);
+  return REF_OK;
+}
+
+/* The same definition evaluated straight out of a cache (contiguous or paged),
+ * reading each sequence's keys in logical order through its block table.
+ *   q   [B][n_q][Hq][D]          out [B][n_q][Hq][D] (double)
+ *   seq_lens[b] keys attended (already appended), n_q <= seq_lens[b] <= capacity
+ * With rows_only != NULL only the (b, h) pairs with rows_only[b*Hq+h] != 0 are
+ * computed (the others are left untouched): used to check sampled outputs of a
+ * full-size workload. */
+int kvc_ref_cache_attention(int B, int n_q, int Hq, int Hkv, int D, int dtype, int bs, int S_max,
+                            int max_blocks, int N, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* seq_lens, const int32_t* table,
+                            double scale, const uint8_t* rows_only, double* out) {
+  if (B < 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return REF_ERR_ARG;
+  int G = Hq / Hkv;
+  long cap = bs == 0 ? S_max : (long)max_blocks * bs;
+  long maxL = 0;
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens[b] < n_q || seq_lens[b] > cap) return REF_ERR_DATA;
+    if (seq_lens[b] > maxL) maxL = seq_lens[b];
+  }
+  double* p = (double*)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+  if (!p) return REF_ERR_ARG;
+  int status = REF_OK;
+  for (int b = 0; b < B && status == REF_OK; ++b)
+    for (int h = 0; h < Hq && status == REF_OK; ++h) {
+      if (rows_only && !rows_only[(size_t)b * Hq + h]) continue;
+      int g = h / G;
+      long L = seq_lens[b];
+      for (int r = 0; r < n_q; ++r) {
+        long last = L - n_q + r;
+        size_t qo = (((size_t)b * n_q + r) * Hq + h) * D;
+        double m = -INFINITY;
+        for (long j = 0; j <= last; ++j) {
+          long e = cache_row(b, g, j, Hkv, D, bs, S_max, max_blocks, N, table);
+          if (e < 0) {
+            status = REF_ERR_DATA;
+            break;
+          }
+          double s = 0.0;
+          for (int d = 0; d < D; ++d)
+            s += load_elem(q, qo + d, dtype) * load_elem(k_cache, (size_t)e + d, dtype);
+          p[j] = s * scale;
+          if (p[j] > m) m = p[j];
+        }
+        if (status != REF_OK) break;
+        double l = 0.0;
+        for (long j = 0; j <= last; ++j) {
+          p[j] = exp(p[j] - m);
+          l += p[j];
+        }
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (long j = 0; j <= last; ++j) {
+            long e = cache_row(b, g, j, Hkv, D, bs, S_max, max_blocks, N, table);
+            acc += p[j] * load_elem(v_cache, (size_t)e + d, dtype);
+          }
+          out[qo + d] = acc / l;
+        }
+      }
+    }
+  free(p);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Split-KV evaluation with the online softmax -- the algorithm, not the
+ * definition.  It is pinned against kvc_ref_attention (they must agree to
+ * rounding) to show that a partitioned pass is exact attention.
+ *
+ * [VN] 07 "Online softmax": one pass keeps a running maximum m and a running
+ * sum l; when m grows, the sum so far is multiplied by exp(m_old - m_new).
+ * [I1] "FlashAttention": the unnormalised output O is corrected by the same
+ * factor, and the result is O / l after the last key.
+ * [I1] "FlashDecoding": the keys are split into chunks, each chunk yields a
+ * partial output with its maximum and sum, and a final reduction combines them
+ * with the same rescaling.
+ *
+ * Chunks hold P consecutive keys; a row's chunk with no visible key keeps
+ * m = -inf, l = 0, O = 0 and gets weight 0 in the combine.
+ */
+int kvc_ref_attention_split(int n_q, int Hq, int Hkv, int D, int L, int dtype, const void* q,
+                            const void* k, const void* v, double scale, int P, double* out) {
+  if (n_q <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || Hq % Hkv != 0) return REF_ERR_ARG;
+  if (L < n_q) return REF_ERR_DATA;
+  int G = Hq / Hkv;
+  long n_chunks = (L + P - 1) / P;
+  double* cm = (double*)malloc(sizeof(double) * (size_t)n_chunks);
+  double* cl = (double*)malloc(sizeof(double) * (size_t)n_chunks);
+  double* cO = (double*)malloc(sizeof(double) * (size_t)n_chunks * D);
+  if (!cm || !cl || !cO) {
+    free(cm);
+    free(cl);
+    free(cO);
+    return REF_ERR_ARG;
+  }
+  for (int r = 0; r < n_q; ++r)
+    for (int h = 0; h < Hq; ++h) {
+      int g = h / G;
+      long last = (long)L - n_q + r;
+      for (long c = 0; c < n_chunks; ++c) {
+        double m = -INFINITY, l = 0.0;
+        double* O = cO + c * D;
+        for (int d = 0; d < D; ++d) O[d] = 0.0;
+        for (long j = c * P; j < (c + 1) * P && j <= last; ++j) {
+          double s = 0.0;
+          for (int d = 0; d < D; ++d)
+            s += load_elem(q, ((size_t)r * Hq + h) * D + d, dtype) *
+                 load_elem(k, ((size_t)g * L + j) * D + d, dtype);
+          s *= scale;
+          double m_new = s > m ? s : m;
+          double corr = exp(m - m_new); /* exp(-inf) = 0 on the first key */
+          double e = exp(s - m_new);
+          l = l * corr + e;
+          for (int d = 0; d < D; ++d)
+            O[d] = O[d] * corr + e * load_elem(v, ((size_t)g * L + j) * D + d, dtype);
+          m = m_new;
+        }
+        cm[c] = m;
+        cl[c] = l;
+      }
+      double M = -INFINITY;
+      for (long c = 0; c < n_chunks; ++c)
+        if (cm[c] > M) M = cm[c];
+      double den = 0.0;
+      for (long c = 0; c < n_chunks; ++c)
+        if (cm[c] != -INFINITY) den += exp(cm[c] - M) * cl[c];
+      for (int d = 0; d < D; ++d) {
+        double num = 0.0;
+        for (long c = 0; c < n_chunks; ++c)
+          if (cm[c] != -INFINITY) num += exp(cm[c] - M) * cO[c * D + d];
+        out[((size_t)r * Hq + h) * D + d] = num / den;
+      }
+    }
+  free(cm);
+  free(cl);
+  free(cO);
+  return REF_OK;
+}

@@ -1,0 +1,563 @@
+"""Pins of the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError when
+the oracle disagrees with something other than itself: a closed form, brute
+force on tiny inputs, a library routine (torch / scipy) on a special case, or a
+value printed by the pages (fixtures under ``tests/golden/``).  The same
+functions run against the real oracle (test_oracle_pins.py) and against
+deliberately broken copies of it (test_oracle_mutants.py), which must fail at
+least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from kv_cached_decode_kvc_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+F32 = np.float32
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _int_inputs(rng, shape, lo=-3, hi=3):
+    """Small integers: exact in bf16 and fp32, so scores are exact in any order."""
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def _sdpa64(q, k, v, scale, causal):
+    """torch's scaled_dot_product_attention in float64 on the CPU.
+    q [Hq, Sq, D], k/v [Hq, Sk, D] (already one KV row set per query head)."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(q, np.float64))[None],
+        torch.from_numpy(np.asarray(k, np.float64))[None],
+        torch.from_numpy(np.asarray(v, np.float64))[None],
+        is_causal=causal, scale=float(scale))
+    return out[0].numpy()
+
+
+def _brute(q, k, v, scale, G):
+    """Pure-Python evaluation of softmax(q k^T * scale) v with the shifted causal
+    mask, one scalar at a time (math.fsum sums, math.exp)."""
+    n_q, Hq, D = q.shape
+    _, L, _ = k.shape
+    out = np.zeros((n_q, Hq, D))
+    for r in range(n_q):
+        for h in range(Hq):
+            g = h // G
+            keys = range(L - n_q + r + 1)
+            s = [scale * math.fsum(float(q[r, h, d]) * float(k[g, j, d]) for d in range(D))
+                 for j in keys]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            den = math.fsum(e)
+            for d in range(D):
+                out[r, h, d] = math.fsum(e[j] * float(v[g, j, d]) for j in keys) / den
+    return out
+
+
+# ---------------------------------------------------------------------------
+# attention definition
+# ---------------------------------------------------------------------------
+def pin_single_key_returns_its_value(o):
+    """L = 1: the only weight is 1, so the output is that value row, exactly."""
+    rng = np.random.default_rng(11)
+    for D in (1, 4, 64):
+        q = _f32(rng.standard_normal((1, 2, D)))
+        k1 = _f32(rng.standard_normal((1, 1, D)))
+        v1 = _f32(rng.standard_normal((1, 1, D)))
+        out = o.attention(q, k1, v1, 0.3, "f32")
+        for h in range(2):
+            assert np.array_equal(out[0, h], v1[0, 0].astype(np.float64)), "L=1 must return v0"
+
+
+def pin_equal_scores_give_mean(o):
+    """Identical keys give identical scores: the output is the plain mean of V."""
+    rng = np.random.default_rng(12)
+    L, D = 7, 8
+    q = _f32(rng.standard_normal((1, 1, D)))
+    k = _f32(np.repeat(rng.standard_normal((1, 1, D)), L, axis=1))
+    v = _f32(rng.standard_normal((1, L, D)))
+    out = o.attention(q, k, v, 0.5, "f32")
+    assert np.allclose(out[0, 0], v[0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-15)
+
+
+def pin_two_keys_sigmoid(o):
+    """Two keys: weights are sigmoid(scale*(s0 - s1)) and its complement."""
+    rng = np.random.default_rng(13)
+    from scipy.special import expit
+    for trial in range(5):
+        D = 4
+        q = _int_inputs(rng, (1, 1, D))
+        k = _int_inputs(rng, (1, 2, D))
+        v = _f32(rng.standard_normal((1, 2, D)))
+        scale = 0.25 + trial * 0.1
+        dlt = scale * float(q[0, 0] @ k[0, 0] - q[0, 0] @ k[0, 1])
+        w0 = expit(dlt)
+        want = w0 * v[0, 0].astype(np.float64) + (1 - w0) * v[0, 1].astype(np.float64)
+        out = o.attention(q, k, v, scale, "f32")
+        assert np.allclose(out[0, 0], want, rtol=0, atol=1e-14), (out[0, 0], want)
+
+
+def pin_rows_sum_to_one(o):
+    """Softmax rows sum to 1: with every value equal to 1 the output is 1."""
+    rng = np.random.default_rng(14)
+    q = _f32(rng.standard_normal((3, 4, 16)))
+    k = _f32(rng.standard_normal((2, 40, 16)))
+    v = np.ones((2, 40, 16), dtype=F32)
+    out = o.attention(q, k, v, 1.0 / 4.0, "f32")
+    assert np.abs(out - 1.0).max() <= 1e-14
+
+
+def pin_one_hot_values_give_softmax(o):
+    """With v_j = e_j the output is the probability vector itself; compared with
+    scipy's softmax of the scores (numpy matmul), masked for verify rows."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(15)
+    n_q, L, D = 3, 9, 12
+    q = _f32(rng.standard_normal((n_q, 1, D)))
+    k = _f32(rng.standard_normal((1, L, D)))
+    v = np.zeros((1, L, D), dtype=F32)
+    v[0, np.arange(L), np.arange(L)] = 1.0
+    scale = 0.37
+    out = o.attention(q, k, v, scale, "f32")
+    s = (q[:, 0].astype(np.float64) @ k[0].astype(np.float64).T) * scale  # [n_q, L]
+    for r in range(n_q):
+        vis = L - n_q + r + 1
+        p = softmax(s[r, :vis])
+        assert np.allclose(out[r, 0, :vis], p, rtol=0, atol=1e-15)
+        assert np.all(out[r, 0, vis:] == 0.0), "masked keys must get weight 0"
+
+
+def pin_brute_force_tiny(o):
+    """Every shape with B=1, Hq, Hkv, D, L <= 4 (and n_q <= L) against the
+    pure-Python brute force, on small-integer inputs in both element types."""
+    rng = np.random.default_rng(16)
+    for dtype in ("f32", "bf16"):
+        for Hkv in (1, 2):
+            for G in (1, 2):
+                for D in (1, 3, 4):
+                    for L in (1, 2, 4):
+                        for n_q in sorted({1, L}):
+                            Hq = Hkv * G
+                            qf = _int_inputs(rng, (n_q, Hq, D))
+                            kf = _int_inputs(rng, (Hkv, L, D))
+                            vf = _int_inputs(rng, (Hkv, L, D), -5, 5)
+                            scale = 0.5
+                            want = _brute(qf, kf, vf, scale, G)
+                            enc = (lambda a: synth.encode(a, dtype))
+                            got = o.attention(enc(qf), enc(kf), enc(vf), scale, dtype)
+                            assert np.allclose(got, want, rtol=0, atol=1e-13), \
+                                (dtype, Hkv, G, D, L, n_q)
+
+
+def pin_large_scores_stay_finite(o):
+    """Scores in the hundreds (exp would overflow without the max shift): the
+    result is still the exact softmax average, here the arg-max key's value."""
+    D = 4
+    q = np.full((1, 1, D), 30.0, dtype=F32)
+    k = np.zeros((1, 3, D), dtype=F32)
+    k[0, 0] = 10.0
+    k[0, 1] = 9.0
+    k[0, 2] = -10.0
+    v = np.array([[[1, 2, 3, 4], [5, 6, 7, 8], [9, 9, 9, 9]]], dtype=F32)
+    out = o.attention(q, k, v, 1.0, "f32")  # scores 1200, 1080, -1200
+    assert np.all(np.isfinite(out))
+    assert np.allclose(out[0, 0], v[0, 0], rtol=0, atol=1e-40)
+
+
+def pin_causal_matches_sdpa(o):
+    """Verify from an empty cache (n_q = L) is ordinary causal attention: equal to
+    torch's scaled_dot_product_attention(is_causal=True) in float64."""
+    rng = np.random.default_rng(17)
+    for (Hq, Hkv, L, D) in ((2, 2, 33, 16), (4, 1, 20, 8), (6, 3, 17, 32)):
+        G = Hq // Hkv
+        q = _f32(rng.standard_normal((L, Hq, D)))
+        k = _f32(rng.standard_normal((Hkv, L, D)))
+        v = _f32(rng.standard_normal((Hkv, L, D)))
+        scale = 1.0 / math.sqrt(D)
+        got = o.attention(q, k, v, scale, "f32")  # [L, Hq, D]
+        kk = np.repeat(k, G, axis=0)  # consecutive query heads share a KV head
+        vv = np.repeat(v, G, axis=0)
+        want = _sdpa64(q.transpose(1, 0, 2), kk, vv, scale, causal=True).transpose(1, 0, 2)
+        assert np.abs(got - want).max() <= 1e-12
+
+
+def pin_decode_matches_sdpa_noncausal(o):
+    """A single new row attends to every key: torch SDPA without a mask."""
+    rng = np.random.default_rng(18)
+    Hq, Hkv, L, D = 8, 2, 50, 16
+    q = _f32(rng.standard_normal((1, Hq, D)))
+    k = _f32(rng.standard_normal((Hkv, L, D)))
+    v = _f32(rng.standard_normal((Hkv, L, D)))
+    got = o.attention(q, k, v, 0.25, "f32")
+    want = _sdpa64(q.transpose(1, 0, 2), np.repeat(k, 4, 0), np.repeat(v, 4, 0), 0.25, False)
+    assert np.abs(got - want.transpose(1, 0, 2)).max() <= 1e-12
+
+
+def pin_gqa_is_mha_on_repeated_heads(o):
+    """GQA equals MHA over repeat_interleave'd K/V; Hkv = 1 is MQA."""
+    rng = np.random.default_rng(19)
+    for Hkv in (1, 2, 4):
+        Hq, L, D, n_q = 8, 24, 8, 3
+        G = Hq // Hkv
+        q = _f32(rng.standard_normal((n_q, Hq, D)))
+        k = _f32(rng.standard_normal((Hkv, L, D)))
+        v = _f32(rng.standard_normal((Hkv, L, D)))
+        kr = torch.from_numpy(k).repeat_interleave(G, dim=0).numpy()
+        vr = torch.from_numpy(v).repeat_interleave(G, dim=0).numpy()
+        a = o.attention(q, k, v, 0.3, "f32")
+        b = o.attention(q, kr, vr, 0.3, "f32")
+        assert np.array_equal(a, b)
+        # and head h must not read KV head h % Hkv unless that equals h // G
+        if Hkv > 1 and G > 1:
+            wrong = np.stack([k[h % Hkv] for h in range(Hq)])
+            c = o.attention(q, wrong, np.stack([v[h % Hkv] for h in range(Hq)]), 0.3, "f32")
+            assert not np.allclose(a, c)
+
+
+def pin_shift_invariance(o):
+    """Adding the same vector c to every key adds q.c to each score of a row:
+    the output does not change."""
+    rng = np.random.default_rng(20)
+    q = _int_inputs(rng, (2, 2, 8))
+    k = _int_inputs(rng, (1, 30, 8))
+    v = _f32(rng.standard_normal((1, 30, 8)))
+    c = _int_inputs(rng, (8,))
+    a = o.attention(q, k, v, 0.5, "f32")
+    b = o.attention(q, _f32(k + c[None, None, :]), v, 0.5, "f32")
+    assert np.abs(a - b).max() <= 1e-13
+
+
+def pin_split_equals_definition(o):
+    """Chunked online softmax with the cross-chunk combine equals the definition."""
+    rng = np.random.default_rng(21)
+    n_q, Hq, Hkv, L, D = 5, 4, 2, 300, 16
+    q = synth.to_bf16_bits(rng.standard_normal((n_q, Hq, D)).astype(F32))
+    k = synth.to_bf16_bits(rng.standard_normal((Hkv, L, D)).astype(F32))
+    v = synth.to_bf16_bits(rng.standard_normal((Hkv, L, D)).astype(F32))
+    ref = o.attention(q, k, v, 0.25, "bf16")
+    for P in (1, 7, 16, 256, L, 4 * L):
+        got = o.attention_split(q, k, v, 0.25, "bf16", P)
+        assert np.abs(got - ref).max() <= 1e-12, P
+
+
+def pin_page_code3a_magnitude(o):
+    """The page's worked example (section 07, sample code 3a): causal attention of
+    torch.manual_seed(0) randn(8, 2048, 128) inputs.  The oracle must agree with
+    torch's float64 attention to 1e-12, and the float32 standard attention must
+    sit at the printed distance (8.70e-07) from it, to within a factor of two
+    (only the magnitude is portable: summation order differs by BLAS)."""
+    fx = dict(line.split(" = ") for line in open(os.path.join(GOLDEN, "online_softmax_code3a.txt"))
+              if "=" in line and not line.startswith("#"))
+    printed = float(fx["standard_fp32_vs_fp64"])
+    torch.manual_seed(0)
+    q, k, v = (torch.randn(8, 2048, 128) for _ in range(3))
+    scale = 1.0 / math.sqrt(128)
+    got = o.attention(q.numpy().transpose(1, 0, 2).copy(), k.numpy(), v.numpy(), scale, "f32")
+    got = got.transpose(1, 0, 2)  # [H, S, D]
+
+    def standard(qq, kk, vv):
+        s = qq @ kk.transpose(-1, -2) / qq.shape[-1] ** 0.5
+        mask = torch.ones(s.shape[-2:], dtype=torch.bool).triu(1)
+        return torch.softmax(s.masked_fill(mask, float("-inf")), dim=-1) @ vv
+
+    ref64 = standard(q.double(), k.double(), v.double()).numpy()
+    assert np.abs(got - ref64).max() <= 1e-12
+    err32 = np.abs(standard(q, k, v).double().numpy() - got).max()
+    assert printed / 2 <= err32 <= printed * 2, (err32, printed)
+
+
+# ---------------------------------------------------------------------------
+# cache: block table, append, paged reads
+# ---------------------------------------------------------------------------
+def _simulate_tokenwise(seq_lens, n_new, table, free, head, bs):
+    """Token-at-a-time allocation, the way the pages describe it: before writing a
+    token at position pos, take a fresh block from the pool iff pos % bs == 0."""
+    table = [list(r) for r in table]
+    slots = []
+    for b, (L, n) in enumerate(zip(seq_lens, n_new)):
+        for t in range(n):
+            pos = L + t
+            if pos % bs == 0:
+                table[b][pos // bs] = int(free[head])
+                head += 1
+            slots.append(table[b][pos // bs] * bs + pos % bs)
+    return table, head, slots
+
+
+def pin_block_table_tokenwise(o):
+    """Brute force on tiny pools (bs = 4, B = 3): the batched allocator equals a
+    token-at-a-time walk; entries are distinct, each sequence holds ceil(L/bs)
+    blocks (waste < bs), every slot is unique."""
+    rng = np.random.default_rng(22)
+    bs, B, maxb = 4, 3, 8
+    for trial in range(200):
+        N = int(rng.integers(8, 20))
+        free = rng.permutation(N).astype(np.int32)
+        seq0 = rng.integers(0, 9, size=B).astype(np.int32)
+        # first give every sequence its existing blocks with the same walk
+        table0, head0, _ = _simulate_tokenwise([0] * B, list(seq0), [[-1] * maxb] * B, free, 0, bs)
+        n_new = rng.integers(0, 7, size=B)
+        cu = synth.cu_from_counts(n_new)
+        st, table, head, slots = o.block_table(seq0, cu, np.array(table0, np.int32), free, head0, bs)
+        need = sum(-(-(int(L) + int(n)) // bs) - (-(-int(L) // bs)) for L, n in zip(seq0, n_new))
+        if head0 + need > N:
+            assert st == -6 and np.array_equal(table, np.array(table0, np.int32)) and head == head0
+            continue
+        assert st == 0
+        t2, h2, s2 = _simulate_tokenwise(list(seq0), list(n_new), table0, free, head0, bs)
+        assert np.array_equal(table, np.array(t2, np.int32)) and head == h2
+        assert list(slots) == s2
+        assert len(set(slots)) == len(slots)
+        used = [x for row in table for x in row if x >= 0]
+        assert len(used) == len(set(used))
+        for b in range(B):
+            L = int(seq0[b] + n_new[b])
+            held = sum(1 for x in table[b] if x >= 0)
+            assert held == -(-L // bs) and held * bs - L < bs
+
+
+def pin_block_table_errors(o):
+    """Exhaustion and capacity are all-or-nothing: nothing changes."""
+    bs = 16
+    table = np.full((2, 2), -1, np.int32)
+    free = np.arange(3, dtype=np.int32)
+    st, t, h, _ = o.block_table(np.array([0, 0], np.int32), np.array([0, 20, 40], np.int32),
+                                table, free, 0, bs)
+    assert st == -6 and h == 0 and np.all(t == -1)  # needs 4 blocks, pool has 3
+    st, t, h, _ = o.block_table(np.array([0, 0], np.int32), np.array([0, 33, 34], np.int32),
+                                table, np.arange(8, dtype=np.int32), 0, bs)
+    assert st == -5 and h == 0 and np.all(t == -1)  # 3 blocks > 2 per sequence
+    st, t, h, s = o.block_table(np.array([0, 0], np.int32), np.array([0, 17, 18], np.int32),
+                                table, np.arange(8, dtype=np.int32), 0, bs)
+    assert st == 0 and h == 3 and list(t[0]) == [0, 1] and list(t[1]) == [2, -1]
+    assert list(s[:17]) == list(range(17)) and s[17] == 32
+
+
+def pin_append_contiguous_is_slice_write(o):
+    """Contiguous append equals numpy's in-place slice assignment
+    cache[b, :, L:L+n, :] = new rows; appending past S_max is refused."""
+    rng = np.random.default_rng(23)
+    B, Hkv, S, D = 3, 2, 10, 4
+    for dtype in ("bf16", "f32"):
+        k = synth.encode(rng.standard_normal((B, Hkv, S, D)).astype(F32), dtype)
+        v = synth.encode(rng.standard_normal((B, Hkv, S, D)).astype(F32), dtype)
+        lens = np.array([0, 4, 7], np.int32)
+        n = np.array([2, 6, 3], np.int64)
+        cu = synth.cu_from_counts(n)
+        kn = synth.encode(rng.standard_normal((cu[-1], Hkv, D)).astype(F32), dtype)
+        vn = synth.encode(rng.standard_normal((cu[-1], Hkv, D)).astype(F32), dtype)
+        kw, vw = k.copy(), v.copy()
+        for b in range(B):
+            if lens[b] + n[b] <= S:
+                kw[b, :, lens[b]:lens[b] + n[b]] = kn[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+                vw[b, :, lens[b]:lens[b] + n[b]] = vn[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+        kc, vc = k.copy(), v.copy()
+        st, out = o.append(kn, vn, lens, cu, kc, vc)
+        assert st == 0 and list(out) == list(lens + n)
+        assert np.array_equal(kc, kw) and np.array_equal(vc, vw)
+
+
+def pin_append_capacity(o):
+    B, Hkv, S, D = 2, 1, 8, 2
+    k = np.zeros((B, Hkv, S, D), np.float32)
+    v = np.zeros((B, Hkv, S, D), np.float32)
+    lens = np.array([5, 2], np.int32)
+    cu = synth.cu_from_counts([4, 6])
+    kn = np.arange(cu[-1] * D, dtype=np.float32).reshape(cu[-1], 1, D) + 1
+    st, out = o.append(kn, kn, lens, cu, k, v)
+    assert st == -5 and list(out) == [5, 8]
+    assert np.all(k[0] == 0)  # refused sequence untouched
+    assert np.array_equal(k[1, 0, 2:8], kn[4:10, 0])
+
+
+def pin_paged_equals_contiguous(o):
+    """A paged cache built through a permuted block table holds, in logical
+    order, the same bytes as the contiguous cache built from the same rows, and
+    attention over both is bitwise equal."""
+    w = synth.custom(seed=7, B=4, Hq=4, Hkv=2, D=16, dtype="bf16", block_size=4, n_q=2,
+                     len_lo=3, len_hi=23)
+    _paged_vs_contig(o, w)
+
+
+def _build_caches(o, w, lengths, bs_override=None):
+    """(contiguous caches, paged pools, table) holding every sequence's first
+    lengths[b] cached rows, both built by the oracle's own append."""
+    B = w.B
+    bs = bs_override or w.block_size
+    S = int(max(lengths)) + w.n_q
+    nd = np.uint16 if w.dtype == "bf16" else np.float32
+    kc = np.zeros((B, w.Hkv, S, w.D), nd)
+    vc = np.zeros((B, w.Hkv, S, w.D), nd)
+    kr = synth.packed_cache_rows(w, "k", lengths)
+    vr = synth.packed_cache_rows(w, "v", lengths)
+    cu = synth.cu_from_counts(lengths)
+    zeros = np.zeros(B, np.int32)
+    st, _ = o.append(kr, vr, zeros, cu, kc, vc)
+    assert st == 0
+    maxb = -(-S // bs)
+    N = B * maxb + B
+    free = synth.rng(w, synth.S_POOL).permutation(N).astype(np.int32)
+    table = np.full((B, maxb), -1, np.int32)
+    st, table, head, slots = o.block_table(zeros, cu, table, free, 0, bs)
+    assert st == 0
+    kp = np.zeros((N, w.Hkv, bs, w.D), nd)
+    vp = np.zeros((N, w.Hkv, bs, w.D), nd)
+    st, _ = o.append(kr, vr, zeros, cu, kp, vp, bs=bs, slots=slots)
+    assert st == 0
+    return (kc, vc), (kp, vp), table, free, head
+
+
+def _paged_vs_contig(o, w):
+    lengths = synth.final_lengths(w)
+    (kc, vc), (kp, vp), table, _, _ = _build_caches(o, w, lengths)
+    bs = w.block_size
+    for b in range(w.B):
+        L = int(lengths[b])
+        assert np.array_equal(o.gather(kc, b, L), o.gather(kp, b, L, bs=bs, table=table))
+        assert np.array_equal(o.gather(vc, b, L), o.gather(vp, b, L, bs=bs, table=table))
+    q = synth.packed_queries(w)
+    st1, a = o.cache_attention(q, kc, vc, lengths, 0.25, w.dtype)
+    st2, b_ = o.cache_attention(q, kp, vp, lengths, 0.25, w.dtype, bs=bs, table=table)
+    assert st1 == 0 and st2 == 0 and np.array_equal(a, b_)
+    # and equal to the per-sequence definition on the gathered rows
+    for b in range(w.B):
+        L = int(lengths[b])
+        ref = o.attention(q[b], o.gather(kc, b, L), o.gather(vc, b, L), 0.25, w.dtype)
+        assert np.array_equal(ref, a[b])
+
+
+def pin_poisoned_slots_ignored(o):
+    """Slots beyond each sequence's length (and unassigned pool blocks) filled
+    with NaN change nothing: the mask stops at the exact length."""
+    w = synth.custom(seed=8, B=3, Hq=2, Hkv=1, D=8, dtype="f32", block_size=4, n_q=1,
+                     len_lo=5, len_hi=13)
+    lengths = synth.final_lengths(w)
+    (kc, vc), (kp, vp), table, _, _ = _build_caches(o, w, lengths)
+    q = synth.packed_queries(w)
+    _, a = o.cache_attention(q, kc, vc, lengths, 0.3, "f32")
+    _, ap = o.cache_attention(q, kp, vp, lengths, 0.3, "f32", bs=4, table=table)
+    kc2, vc2, kp2, vp2 = kc.copy(), vc.copy(), kp.copy(), vp.copy()
+    for b in range(w.B):
+        kc2[b, :, lengths[b]:] = np.nan
+        vc2[b, :, lengths[b]:] = np.nan
+    live = {int(table[b, j // 4]) * 4 + j % 4 for b in range(w.B) for j in range(lengths[b])}
+    for blk in range(kp.shape[0]):
+        for off in range(4):
+            if blk * 4 + off not in live:
+                kp2[blk, :, off] = np.nan
+                vp2[blk, :, off] = np.nan
+    _, b_ = o.cache_attention(q, kc2, vc2, lengths, 0.3, "f32")
+    _, bp = o.cache_attention(q, kp2, vp2, lengths, 0.3, "f32", bs=4, table=table)
+    assert np.array_equal(a, b_) and np.array_equal(ap, bp)
+
+
+def pin_verify_equals_repeated_decode(o):
+    """Verify row r is the decode of a sequence cut to L - n_q + r + 1 keys."""
+    w = synth.custom(seed=9, B=2, Hq=4, Hkv=2, D=16, dtype="bf16", block_size=0, n_q=5,
+                     len_lo=9, len_hi=30)
+    lengths = synth.final_lengths(w)
+    (kc, vc), _, _, _, _ = _build_caches(o, w, lengths, bs_override=4)
+    q = synth.packed_queries(w)
+    _, ver = o.cache_attention(q, kc, vc, lengths, 0.25, "bf16")
+    for r in range(w.n_q):
+        cut = lengths - w.n_q + r + 1
+        _, dec = o.cache_attention(np.ascontiguousarray(q[:, r:r + 1]), kc, vc, cut.astype(np.int32),
+                                   0.25, "bf16")
+        assert np.array_equal(dec[:, 0], ver[:, r])
+
+
+def pin_cached_decode_equals_recompute(o):
+    """The tiny GPTlite-shaped workload: 32 decode steps, each appending one row
+    and attending over the cache, equal row 256 + s of causal attention recomputed
+    over the whole sequence without a cache (torch SDPA, float64)."""
+    w = synth.get("C1")
+    cached = synth.cached_lengths(w)
+    S = synth.capacity_tokens(w)
+    kc = np.zeros((w.B, w.Hkv, S, w.D), np.float32)
+    vc = np.zeros_like(kc)
+    zeros = np.zeros(w.B, np.int32)
+    st, lens = o.append(synth.packed_cache_rows(w, "k", cached), synth.packed_cache_rows(w, "v", cached),
+                        zeros, synth.cu_from_counts(cached), kc, vc)
+    assert st == 0
+    scale = 1.0 / math.sqrt(w.D)
+    outs = []
+    for s in range(w.steps):
+        cu = synth.cu_from_counts([w.n_q] * w.B)
+        st, lens = o.append(synth.packed_new_rows(w, "k", s), synth.packed_new_rows(w, "v", s), lens, cu,
+                            kc, vc)
+        assert st == 0
+        st, out = o.cache_attention(synth.packed_queries(w, s), kc, vc, lens, scale, "f32")
+        assert st == 0
+        outs.append(out[:, 0])
+    for b in range(w.B):
+        qfull = np.zeros((w.Hq, S, w.D), np.float32)
+        for s in range(w.steps):
+            qfull[:, cached[b] + s] = synth.queries(w, b, s)[0]
+        want = _sdpa64(qfull, kc[b], vc[b], scale, causal=True)  # MHA: head h uses KV head h
+        for s in range(w.steps):
+            assert np.abs(outs[s][b] - want[:, cached[b] + s]).max() <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# byte accounting and output rounding
+# ---------------------------------------------------------------------------
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.strip() and not line.startswith("#"):
+            out.append([c.strip() for c in line.split("|")])
+    return out
+
+
+def pin_kv_bytes_printed(o=None):
+    """The KV-size formula reproduces every figure the pages print."""
+    from kv_cached_decode_kvc_amd.metrics import kv_bytes_per_token, kv_cache_bytes
+    for model, L, nq, nkv, hd, kib, gib128k in _rows("kv_bytes_per_token.txt"):
+        per = kv_bytes_per_token(int(L), int(nkv), int(hd), 2)
+        assert round(per / 1024, 1) == float(kib), model
+        assert round(per * 131072 / 1024 ** 3, 2) == float(gib128k), model
+    units = {"GB": 1e9, "KiB": 1024.0, "GiB": 1024.0 ** 3}
+    for name, L, nkv, hd, bpv, toks, val, unit, _src in _rows("kv_cache_sizes.txt"):
+        total = kv_cache_bytes(int(L), int(nkv), int(hd), int(bpv), int(toks))
+        digits = len(val.split(".")[1]) if "." in val else 0
+        assert round(total / units[unit], digits) == float(val), name
+    assert kv_cache_bytes(40, 40, 128, 2, 2048) == 1_677_721_600
+    per = kv_bytes_per_token(32, 8, 128, 2)
+    for ctx, gb, nmax in _rows("kv_budget_llama31_8b.txt"):
+        assert round(per * int(ctx) / 1e9, 2) == float(gb)
+        assert int(55.9e9 // (per * int(ctx))) == int(nmax)
+
+
+def pin_round_bf16_exhaustive_neighbours(o):
+    """Output rounding: for random doubles, the oracle's bf16 is the nearest of
+    the two bf16 neighbours (ties to the even pattern), found by exact search."""
+    rng = np.random.default_rng(24)
+    xs = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-6, 6, 3000),
+                         np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0,
+                                   -0.0, 1.0 + 2.0 ** -8 + 2.0 ** -40])])
+    got = o.round_bf16(xs)
+    for x, g in zip(xs, got):
+        f32 = np.float32(x)
+        lo_bits = int(np.array([f32], np.float32).view(np.uint32)[0]) >> 16
+        cands = {lo_bits, lo_bits + 1, lo_bits - 1}
+        best = None
+        for c in cands:
+            c &= 0xFFFF
+            val = float((np.array([c << 16], np.uint32)).view(np.float32)[0])
+            d = abs(val - x)
+            key = (d, c & 1)
+            if best is None or key < best[0]:
+                best = (key, c)
+        assert int(g) == best[1] or (x == 0.0), (x, hex(int(g)), hex(best[1]))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+FAST_PINS = [p for p in ALL_PINS if p.__name__ not in ("pin_page_code3a_magnitude",)]
