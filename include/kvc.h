@@ -1,0 +1,211 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) KV-cache decode-attention library.
+ *
+ * The memory-bound decode step of attention over a KV cache, as described by
+ *   [I1] "Inference-1" (brunomaga.github.io): sections "KV cache",
+ *        "PagedAttention: memory management for the KV cache",
+ *        "FlashAttention", "FlashDecoding", "Smaller KV caches: MQA, GQA and MLA";
+ *   [VN] "Inference o quy mo lon: KV cache, prefill va decode"
+ *        (blog.truongducdung.dev): section 05 "PagedAttention va prefix
+ *        caching" / "Block table", section 07 "FlashAttention" / "Online softmax";
+ *   [I2] "Inference-2" (brunomaga.github.io): "Draft-model speculative
+ *        decoding", "CUDA graphs";
+ *   [EI] "Efficient Inference" (learn.obvix.io): the KV-cache passage and the
+ *        paged-attention passage.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are device memory; (host) are host memory.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns without synchronising.  The library never
+ *     allocates, frees or copies host<->device, keeps no pointer after it
+ *     returns and holds no global state: calls are re-entrant.
+ *   - The caller owns every buffer, including the attention workspace.
+ *   - Problems visible on the host (null pointers, shapes, unsupported
+ *     sizes, a workspace too small) return a negative kvc_status before any
+ *     launch and change nothing.
+ *   - Problems only visible in device data (a length beyond the capacity, a
+ *     block id outside the pool, an exhausted free list) never fault: the
+ *     kernels skip the offending work and, when `dev_status` is not NULL,
+ *     store a negative kvc_status there with an atomic minimum (the caller
+ *     zeroes it beforehand and reads it after synchronising).
+ *   - A failed launch returns KVC_ERR_HIP.
+ *
+ * Layouts (element = 2 bytes for KVC_BF16, 4 for KVC_F32; row-major)
+ *   contiguous cache (block_size == 0): k_cache, v_cache [batch][num_kv_heads][max_seq_len][head_dim]
+ *   paged pool       (block_size  > 0): k_cache, v_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_table  [batch][max_blocks_per_seq] int32, -1 = unassigned
+ *   new rows     k_new, v_new [total_new][num_kv_heads][head_dim], sequence b
+ *                owns rows cu_new[b] .. cu_new[b+1]-1 (projection order)
+ *   queries      q   [batch][n_q][num_q_heads][head_dim]
+ *   outputs      out [batch][n_q][num_q_heads][head_dim]
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_ARG = -1,          /* null pointer, aliasing that is not allowed, bad count   */
+  KVC_ERR_SHAPE = -2,        /* inconsistent sizes, e.g. num_q_heads % num_kv_heads     */
+  KVC_ERR_UNSUPPORTED = -3,  /* head_dim not 64/128, block_size not a multiple of 16... */
+  KVC_ERR_WORKSPACE = -4,    /* workspace_bytes < kvc_attn_workspace_bytes()            */
+  KVC_ERR_CAPACITY = -5,     /* a sequence would grow past its capacity                 */
+  KVC_ERR_NO_BLOCKS = -6,    /* the free list cannot cover the new blocks               */
+  KVC_ERR_HIP = -7,          /* a kernel launch failed                                  */
+  KVC_ERR_DATA = -8          /* device data out of range (length, slot, block id)      */
+} kvc_status;
+
+/* Shape of one layer's cache (host struct, passed by pointer). */
+typedef struct {
+  int32_t batch;              /* B sequences                                            */
+  int32_t num_q_heads;        /* Hq                                                     */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, query head h reads KV head h/(Hq/Hkv)
+                                 ([I1] "Smaller KV caches": consecutive heads share)    */
+  int32_t head_dim;           /* D in {64, 128}                                         */
+  int32_t dtype;              /* kvc_dtype of q, caches and new rows                    */
+  int32_t block_size;         /* 0: contiguous cache; else paged, a multiple of 16 and a
+                                 power of two ([VN] 05 "Block table": 16 by default)     */
+  int32_t max_seq_len;        /* contiguous: capacity S_max per sequence                */
+  int32_t max_blocks_per_seq; /* paged: row stride of block_table; capacity is
+                                 max_blocks_per_seq * block_size tokens                 */
+  int32_t num_blocks;         /* paged: pool size N                                     */
+  int32_t partition_tokens;   /* split-KV partition length in tokens: 0 = library
+                                 default, else a multiple of 16                         */
+} kvc_cache_desc;
+
+/*
+ * kvc_block_table -- give every sequence the blocks its new tokens need and
+ * emit the physical slot of every new token (paged caches only).
+ *
+ * [I1] "PagedAttention" and [EI] paged-attention passage: fixed-size blocks,
+ * allocated on demand from a free pool, with a per-sequence table from logical
+ * to physical blocks.  [VN] 05 "Block table": a block is taken only when the
+ * last one is full.  Order: sequences in batch order, missing logical blocks in
+ * increasing order, free_list consumed from index *free_head_in upward.
+ *
+ *   seq_lens      (device) [B]   tokens already held (ceil(len/bs) blocks)
+ *   cu_new        (device) [B+1] offsets of the new tokens
+ *   total_new     (host)         cu_new[B]
+ *   block_table   (device) [B][max_blocks_per_seq], in/out
+ *   free_list     (device) [num_blocks] physical block ids
+ *   free_head_in  (device) [1]   first unused free_list index
+ *   free_head_out (device) [1]   receives free_head_in + blocks taken; may alias
+ *                                free_head_in (a distinct pointer makes the call
+ *                                repeatable with identical effect)
+ *   slot_mapping  (device) [total_new] out: table[b][pos/bs]*bs + pos%bs for the
+ *                                new token at logical position pos
+ * All or nothing: when any sequence would exceed max_blocks_per_seq
+ * (KVC_ERR_CAPACITY), a length is negative (KVC_ERR_DATA) or the free list runs
+ * out (KVC_ERR_NO_BLOCKS), nothing is written except free_head_out =
+ * free_head_in and the status.  One workgroup: microseconds.
+ */
+int kvc_block_table(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_new,
+                    int32_t total_new, int32_t* block_table, const int32_t* free_list,
+                    const int32_t* free_head_in, int32_t* free_head_out, int32_t* slot_mapping,
+                    int32_t* dev_status, void* stream);
+
+/*
+ * kvc_append -- copy the new tokens' key and value rows into the cache, bit
+ * for bit, and advance the lengths.
+ *
+ * [EI] KV-cache passage: a preallocated cache written in place at the current
+ * length, which then grows by the number of new tokens; writing past the
+ * capacity is an error.  [I2] "CUDA graphs": in-place writes at the new
+ * positions.  [I1] "KV cache": only the new rows are written.
+ *
+ *   seq_lens      (device) [B] lengths before the append
+ *   cu_new        (device) [B+1]
+ *   total_new     (host)   cu_new[B]
+ *   max_new       (host)   an upper bound of cu_new[b+1]-cu_new[b] (sizes the grid)
+ *   slot_mapping  (device) paged: [total_new] from kvc_block_table; contiguous: NULL
+ *                 (token t of sequence b goes to position seq_lens[b] + t)
+ *   seq_lens_out  (device) [B] = seq_lens + new counts; must not alias seq_lens
+ * Contiguous: a sequence that would pass max_seq_len is not written, keeps its
+ * length and reports KVC_ERR_CAPACITY.  Paged: a token whose slot lies outside
+ * the pool is not written and reports KVC_ERR_DATA; lengths still advance.
+ */
+int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+               const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new, int32_t max_new,
+               const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t* seq_lens_out,
+               int32_t* dev_status, void* stream);
+
+/*
+ * kvc_decode_attn -- one new query row per sequence attends over all of its
+ * seq_lens[b] cached keys (its own key already appended), no mask.
+ *
+ * [I1] "Why attention matters": softmax(q K^T * scale) V; [I1] "KV cache": a
+ * single new row sees every cached key; [I1] "FlashDecoding": split-KV --
+ * partitions of the keys processed in parallel, each yielding a partial output
+ * with its running maximum and sum ([VN] 07 "Online softmax"), then a separate
+ * reduction combines them.  Equivalent to kvc_verify_attn with n_q = 1.
+ *
+ *   q            (device) [B][1][Hq][D], dtype d->dtype
+ *   seq_lens     (device) [B], 1 <= seq_lens[b] <= capacity
+ *   block_table  (device) paged: [B][max_blocks_per_seq]; contiguous: NULL
+ *   scale        (host)   score scale, normally 1/sqrt(D)
+ *   out          (device) [B][1][Hq][D] of out_dtype (KVC_BF16 rounds to nearest even)
+ *   workspace    (device) >= kvc_attn_workspace_bytes(d, 1) bytes, 16-byte aligned
+ * A sequence with invalid data produces zeros and reports KVC_ERR_DATA.
+ */
+int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                    float scale, void* out, int32_t out_dtype, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * kvc_verify_attn -- n_q query rows per sequence (the last accepted token and
+ * n_q - 1 drafts, already appended as the last n_q keys) attend over the cache
+ * with a causal mask among themselves: row r sees keys 0 .. seq_lens[b]-n_q+r.
+ *
+ * [I2] "Draft-model speculative decoding": the target model checks K drafts in
+ * one pass over the context plus the drafts; [I1] "KV cache": several new
+ * tokens on top of a cache use a shifted causal mask, each new token attending
+ * every cached token and the new ones up to itself.
+ *
+ *   n_q (host) 1..16; q, out [B][n_q][Hq][D]; seq_lens[b] >= n_q; other
+ *   arguments as kvc_decode_attn; workspace >= kvc_attn_workspace_bytes(d, n_q).
+ */
+int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                    float scale, void* out, int32_t out_dtype, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * The two stages kvc_verify_attn runs, exported so that each can be timed on
+ * its own: kvc_attn_partition writes every (row, partition) partial -- running
+ * maximum (base-2 logarithm domain), sum and unnormalised output -- into the
+ * workspace; kvc_attn_reduce combines them into `out` ([I1] "FlashDecoding").
+ * Same arguments and rules as kvc_verify_attn; reduce must follow partition
+ * on the same workspace with the same desc, n_q and seq_lens.
+ */
+int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
+                       const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                       float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                       void* stream);
+int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_lens,
+                    const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                    int32_t* dev_status, void* stream);
+
+/* Workspace bytes the attention calls need for this desc and n_q (0 on a bad desc). */
+size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
+
+/* Partition length in tokens the attention calls use for this desc and n_q
+ * (negative kvc_status on a bad desc). */
+int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
+
+/* Static text for a kvc_status value. */
+const char* kvc_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -144,8 +144,10 @@ int kvc_ref_block_table(int B, int bs, int max_blocks, int N, const int32_t* seq
  *                            cu_new[b] .. cu_new[b+1]-1
  *   contiguous (bs == 0)   : cache [B][Hkv][S_max][D]
  *   paged      (bs  > 0)   : pool  [N][Hkv][bs][D], token i goes to slot slots[i]
- * seq_lens_out[b] = seq_lens[b] + n_new_b, or seq_lens[b] when sequence b was
- * refused.  Returns the first error met (other sequences are still written).
+ * seq_lens_out[b] = seq_lens[b] + n_new_b, or seq_lens[b] when a contiguous
+ * sequence would pass S_max (then none of its rows is written).  A paged token
+ * whose slot lies outside the pool is skipped alone; lengths still advance.
+ * Returns the first error met (everything else is still written).
  */
 int kvc_ref_append(int B, int Hkv, int D, int esize, int bs, int S_max, int N, const void* k_new,
                    const void* v_new, const int32_t* seq_lens, const int32_t* cu_new,
@@ -165,18 +167,12 @@ int kvc_ref_append(int B, int Hkv, int D, int esize, int bs, int S_max, int N, c
       if (status == REF_OK) status = REF_ERR_CAPACITY;
       continue;
     }
-    int ok = 1;
-    if (bs > 0)
-      for (long t = 0; t < n; ++t) {
-        long s = slots[cu_new[b] + t];
-        if (s < 0 || s >= (long)N * bs) ok = 0;
-      }
-    if (!ok) {
-      if (status == REF_OK) status = REF_ERR_DATA;
-      continue;
-    }
     for (long t = 0; t < n; ++t) {
       long src_tok = cu_new[b] + t;
+      if (bs > 0 && (slots[src_tok] < 0 || slots[src_tok] >= (long)N * bs)) {
+        if (status == REF_OK) status = REF_ERR_DATA; /* this token is not written */
+        continue;
+      }
       for (int g = 0; g < Hkv; ++g) {
         size_t src = ((size_t)src_tok * Hkv + g) * row;
         size_t dst;

@@ -378,6 +378,19 @@ def pin_append_capacity(o):
     assert np.array_equal(k[1, 0, 2:8], kn[4:10, 0])
 
 
+def pin_append_paged_bad_slot_skipped(o):
+    """Paged append: a slot outside the pool is skipped alone, lengths advance."""
+    N, Hkv, bs, D = 3, 1, 4, 2
+    k = np.zeros((N, Hkv, bs, D), np.float32)
+    v = np.zeros_like(k)
+    rows = np.arange(3 * D, dtype=np.float32).reshape(3, 1, D) + 1
+    st, out = o.append(rows, rows, np.array([0, 5], np.int32), synth.cu_from_counts([2, 1]), k, v,
+                       bs=bs, slots=np.array([1, N * bs, 6], np.int32))
+    assert st == -8 and list(out) == [2, 6]
+    assert np.array_equal(k[0, 0, 1], rows[0, 0]) and np.array_equal(k[1, 0, 2], rows[2, 0])
+    assert np.count_nonzero(k) == 2 * D
+
+
 def pin_paged_equals_contiguous(o):
     """A paged cache built through a permuted block table holds, in logical
     order, the same bytes as the contiguous cache built from the same rows, and
