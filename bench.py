@@ -1,0 +1,225 @@
+"""Decode-attention benchmark on one MI355X: KV HBM GB/s and sequences x steps / s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: kvc_block_table (paged
+caches), kvc_append of every sequence's new rows, kvc_attn_partition and
+kvc_attn_reduce.  The prepared step reads its lengths and free-list head from
+buffers it never writes, so replaying it K times does identical work each
+time; the cache and all inputs are resident in HBM before the timed region.
+
+Printed: one JSON line.  value = KV bytes attended per step / time per step
+(GB/s); roofline.achieved = the same bytes / the partition kernel's average
+duration, measured with HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV HBM GB/s (% of peak) + sequences·steps/sec at given ctx"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "kv_cached_decode_kvc_amd", "csrc")
+
+
+def kernel_of(w, mfma: bool) -> tuple[str, list[str]]:
+    """Name of the dominant kernel and the sources that define it."""
+    if mfma:
+        return "partition_mfma", ["attn_mfma.hip", "common.hpp"]
+    return "partition_valu", ["attn_valu.hip", "common.hpp"]
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != src_hash:
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds: float, gpu_out=None):
+    """The oracle (single thread, float64) on a bounded sample of the same
+    workload: whole sequences, cycled until `seconds` of oracle time."""
+    import numpy as np
+
+    import oracle
+    from kv_cached_decode_kvc_amd import metrics, synth
+
+    ref = oracle.get()
+    cached = synth.cached_lengths(w)
+    lens = synth.final_lengths(w)
+    scale = 1.0 / math.sqrt(w.D)
+    spent, nbytes, nseq, worst = 0.0, 0, 0, 0.0
+    b = 0
+    while spent < seconds and nseq < 4 * w.B:
+        k = np.concatenate([synth.cache_rows(w, "k", b, int(cached[b])),
+                            synth.new_rows(w, "k", b)]).transpose(1, 0, 2).copy()
+        v = np.concatenate([synth.cache_rows(w, "v", b, int(cached[b])),
+                            synth.new_rows(w, "v", b)]).transpose(1, 0, 2).copy()
+        q = synth.queries(w, b)
+        t0 = time.perf_counter()
+        want = ref.attention(q, k, v, scale, w.dtype)
+        spent += time.perf_counter() - t0
+        nbytes += metrics.attended_kv_bytes([lens[b]], w.Hkv, w.D, w.esize)
+        nseq += 1
+        if gpu_out is not None and nseq <= w.B:
+            worst = max(worst, float(np.abs(gpu_out[b] - want).max()))
+        b = (b + 1) % w.B
+    return {
+        "value": round(nbytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d whole sequences of the workload (batch order, cycled), float64, one thread; "
+                  "%.1f s of oracle time; %.4g sequence-steps/s" % (nseq, spent, nseq / spent),
+        "sample_max_abs_err_vs_gpu": worst if gpu_out is not None else None,
+    }
+
+
+def calibrate_copy(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library's path runs on a single MI355X "
+              "(sequences and KV heads shard across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cached_decode_kvc_amd import kvc, metrics, runner, synth
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    w = synth.get(args.workload)
+    print("# building %s on the device" % w.name, file=sys.stderr, flush=True)
+    lc = runner.build(w, partition_tokens=args.partition_tokens)
+    torch.cuda.synchronize()
+    P = kvc.kvc_attn_partition_tokens(lc.desc, w.n_q)
+    mfma = w.dtype == "bf16" and w.G * w.n_q >= 2
+
+    for _ in range(args.warmup):
+        lc.step()
+    torch.cuda.synchronize()
+    assert lc.dev_status() == 0, "device status %d" % lc.dev_status()
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        lc.step_front()
+        ev0[i].record()
+        lc.step_partition()
+        ev1[i].record()
+        lc.step_reduce()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    assert lc.dev_status() == 0
+
+    lens = synth.final_lengths(w)
+    kv_bytes = metrics.attended_kv_bytes(lens, w.Hkv, w.D, w.esize)
+    ms_per_step = wall / K * 1e3
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = kv_bytes / (part_ms / 1e3) / 1e9
+    kname, ksrc = kernel_of(w, mfma)
+    shash = source_hash(ksrc)
+    traffic = stored_traffic(w.name, kname, shash)
+
+    gpu_out = lc.s_out.cpu().numpy()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) rows; lengths and block permutation from the seed)",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "context": [int(lens.min()), int(lens.max())],
+            "block_size": w.block_size, "query_rows": w.n_q, "partition_tokens": P,
+            "accumulate": "f32",
+        },
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(w.B / (ms_per_step / 1e3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kname,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_kernel_us": round(part_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "source_sha256": shash,
+        },
+    }
+    if args.no_cpu_baseline:
+        line["cpu_baseline"] = None
+    else:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, gpu_out)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,76 @@
+// attn_reduce.hip -- the cross-partition combine of split-KV attention.
+//
+// "Inference-1" (brunomaga.github.io), section "FlashDecoding": every chunk of
+// keys leaves a partial output with its softmax maximum and sum, and a final
+// reduction combines them with the online-softmax rescaling (section
+// "FlashAttention": factor exp(m_p - m*)).  With maxima kept in the base-2
+// domain: m* = max_p m_p, w_p = 2^(m_p - m*) (0 for an empty partition),
+// out = sum_p w_p O_p / sum_p w_p l_p, then one rounding to the output type.
+//
+// One wavefront per output row (sequence, query head, query row); each lane
+// owns D/64 consecutive columns.
+#include "launch.hpp"
+
+namespace kvc {
+
+template <int D, bool BF16_OUT>
+__global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
+  constexpr int CPL = D / kWave;  // columns per lane
+  const long row = blockIdx.x;    // (b * Hq + h) * n_q + r
+  const int lane = threadIdx.x;
+  const int r = (int)(row % p.n_q);
+  const long bh = row / p.n_q;
+  const int h = (int)(bh % p.Hq);
+  const int b = (int)(bh / p.Hq);
+  const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + lane * CPL;
+
+  const int L = p.seq_lens[b];
+  float acc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
+  float den = 0.f;
+  if (L >= p.n_q && L <= p.cap) {
+    const int nparts = (L + p.P - 1) / p.P;
+    const float* ml = p.ws_ml + row * p.max_parts * 2;
+    const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
+    float mstar = -INFINITY;
+    for (int q = 0; q < nparts; ++q) mstar = fmaxf(mstar, ml[2 * q]);
+    for (int q = 0; q < nparts; ++q) {
+      const float mq = ml[2 * q];
+      if (mq == -INFINITY) continue;  // partition with no visible key
+      const float w = fast_exp2(mq - mstar);
+      den += w * ml[2 * q + 1];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) acc[j] += w * po[(long)q * D + j];
+    }
+  } else if (lane == 0 && h == 0 && r == 0) {
+    report(p.status, KVC_ERR_DATA);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;  // invalid data: zeros
+  if constexpr (BF16_OUT) {
+    uint16_t* out = (uint16_t*)p.out + ooff;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) out[j] = (uint16_t)f32_to_bf16_bits(acc[j] * inv);
+  } else {
+    float* out = (float*)p.out + ooff;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) out[j] = acc[j] * inv;
+  }
+}
+
+hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s) {
+  const long rows = (long)p.B * p.Hq * p.n_q;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)rows), block(kWave);
+  const bool bf = out_dtype == KVC_BF16;
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((reduce_kernel<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((reduce_kernel<128, false>), grid, block, 0, s, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((reduce_kernel<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((reduce_kernel<64, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,189 @@
+// attn_valu.hip -- split-KV partition kernel on the vector ALUs: one query row
+// per wavefront.
+//
+// Computes, for one (sequence b, query head h, query row r, partition p), the
+// running maximum m, running sum l and unnormalised output O over the keys
+// [p*P, min((p+1)*P, visible)) -- the online-softmax recurrence of "Inference-1"
+// (brunomaga.github.io), section "FlashAttention", and of "Inference o quy mo lon"
+// (truongducdung.dev), 07 "Online softmax"; the partitioning is the split-KV of
+// "Inference-1", section "FlashDecoding".  Row r of n_q sees keys
+// 0 .. L - n_q + r ("Inference-1", "KV cache": shifted causal mask).
+//
+// Used for MHA (one query row per KV row, so there is no dense contraction to
+// give to the matrix cores) and for every fp32 cache.
+//
+// Layout of the work: a wavefront streams 16-key tiles.  A key row of D
+// elements is split over LPR lanes holding 16 bytes each, so one 16-byte load
+// per lane fetches RPL = 64/LPR whole rows (1 KiB, fully coalesced); U = 16/RPL
+// loads cover a tile for K and U for V.  Dot products are reduced inside the
+// LPR lanes with DPP; the tile maximum and, at the end, the sum and output are
+// reduced across the RPL row groups with lane shuffles.
+#include "launch.hpp"
+
+namespace kvc {
+
+template <typename T, int D>
+struct ValuShape {
+  static constexpr int VE = 16 / (int)sizeof(T);  // elements per lane per load
+  static constexpr int LPR = D / VE;                // lanes per key row
+  static constexpr int RPL = kWave / LPR;           // key rows per wave load
+  static constexpr int U = kTile / RPL;             // loads per tile (each of K, V)
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row split");
+};
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bf16: a 16-byte load holds 8 elements in 4 words
+  static __device__ __forceinline__ float dot(const uint4& q, const uint4& k) {
+    float a = dot2_bf16(k.x, q.x, 0.f);
+    a = dot2_bf16(k.y, q.y, a);
+    a = dot2_bf16(k.z, q.z, a);
+    return dot2_bf16(k.w, q.w, a);
+  }
+  static __device__ __forceinline__ void axpy(float p, const uint4& v, float* o) {
+    o[0] += p * bf16_lo(v.x);
+    o[1] += p * bf16_hi(v.x);
+    o[2] += p * bf16_lo(v.y);
+    o[3] += p * bf16_hi(v.y);
+    o[4] += p * bf16_lo(v.z);
+    o[5] += p * bf16_hi(v.z);
+    o[6] += p * bf16_lo(v.w);
+    o[7] += p * bf16_hi(v.w);
+  }
+};
+
+template <>
+struct Elem<float> {  // fp32: 4 elements per 16-byte load
+  static __device__ __forceinline__ float dot(const uint4& q, const uint4& k) {
+    float a = __uint_as_float(q.x) * __uint_as_float(k.x);
+    a = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), a);
+    a = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), a);
+    return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), a);
+  }
+  static __device__ __forceinline__ void axpy(float p, const uint4& v, float* o) {
+    o[0] += p * __uint_as_float(v.x);
+    o[1] += p * __uint_as_float(v.y);
+    o[2] += p * __uint_as_float(v.z);
+    o[3] += p * __uint_as_float(v.w);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
+  using S = ValuShape<T, D>;
+  constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
+  const int lane = threadIdx.x & 63;
+  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
+  if (item >= n_items) return;
+  // item = ((b * Hq + h) * n_q + r) * max_parts + part
+  const int part = (int)(item % p.max_parts);
+  long t = item / p.max_parts;
+  const int r = (int)(t % p.n_q);
+  t /= p.n_q;
+  const int h = (int)(t % p.Hq);
+  const int b = (int)(t / p.Hq);
+
+  const int L = p.seq_lens[b];
+  if (L < p.n_q || L > p.cap) {
+    if (part == 0 && h == 0 && r == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
+    return;
+  }
+  const int nparts = (L + p.P - 1) / p.P;
+  if (part >= nparts) return;
+  const int start = part * p.P;
+  const int end = min(start + p.P, L - p.n_q + r + 1);  // visible keys of row r
+  const long row = ((long)b * p.Hq + h) * p.n_q + r;
+  float* wo = p.ws_o + (row * p.max_parts + part) * D;
+  float* wml = p.ws_ml + (row * p.max_parts + part) * 2;
+  const int c = lane % LPR;   // which 16-byte column chunk of a key row
+  const int r0 = lane / LPR;  // which row of a wave load
+
+  float o[VE];
+#pragma unroll
+  for (int j = 0; j < VE; ++j) o[j] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  if (start < end) {
+    const int g = h / p.G;
+    const T* kbase = (const T*)p.k;
+    const T* vbase = (const T*)p.v;
+    const uint4 qv = *reinterpret_cast<const uint4*>(
+        (const T*)p.q + (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
+    for (int tile = start; tile < end; tile += kTile) {
+      long tbase;  // element offset of key `tile` of (b, g)
+      if (p.table == nullptr) {
+        tbase = (((long)b * p.Hkv + g) * p.S_max + tile) * D;
+      } else {
+        const int blk = p.table[(long)b * p.max_blocks + tile / p.bs];
+        if (blk < 0 || blk >= p.N) {
+          if (lane == 0) report(p.status, KVC_ERR_DATA);
+          continue;
+        }
+        tbase = (((long)blk * p.Hkv + g) * p.bs + (tile % p.bs)) * D;
+      }
+      const int nvalid = min(kTile, end - tile);  // >= 1
+      uint4 kr[U], vr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int tt = u * RPL + r0;
+        tt = tt < nvalid ? tt : nvalid - 1;  // masked lanes re-read a visible row
+        const long off = tbase + (long)tt * D + c * VE;
+        kr[u] = *reinterpret_cast<const uint4*>(kbase + off);
+        vr[u] = *reinterpret_cast<const uint4*>(vbase + off);
+      }
+      float s[U];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[u]));
+        s[u] = (u * RPL + r0 < nvalid) ? dotp * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[u]);
+      }
+      mx = cross_max<LPR>(mx);  // finite: the tile has a visible key
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < VE; ++j) o[j] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pu = fast_exp2(s[u] - m_new);
+        l += pu;
+        Elem<T>::axpy(pu, vr[u], o);
+      }
+      m = m_new;
+    }
+    // every row group holds part of the sum and output: add them up
+    l = cross_sum<LPR>(l);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) o[j] = cross_sum<LPR>(o[j]);
+  }
+  if (r0 == 0) {
+#pragma unroll
+    for (int j = 0; j < VE; j += 4)
+      *reinterpret_cast<float4*>(wo + c * VE + j) = make_float4(o[j], o[j + 1], o[j + 2], o[j + 3]);
+  }
+  if (lane == 0) {
+    wml[0] = m;
+    wml[1] = l;
+  }
+}
+
+hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) {
+  const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_items + 3) / 4)), block(256);
+  if (dtype == KVC_BF16) {
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<uint16_t, 64>), grid, block, 0, s, p);
+  } else {
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<float, 64>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,115 @@
+// common.hpp -- device helpers shared by the kvc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kWave = 64;
+constexpr int kTile = 16;  // keys per inner-loop tile; every block_size is a multiple
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Everything the attention partition kernels need, passed by value.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* table;  // NULL for a contiguous cache
+  float* ws_o;           // [rows][max_parts][D]
+  float* ws_ml;          // [rows][max_parts][2]: running max (log2 domain), running sum
+  int32_t* status;
+  int B, n_q, Hq, Hkv, G, D;
+  int bs, S_max, max_blocks, N;
+  int P, max_parts;
+  int cap;               // tokens a sequence may hold
+  float scale_log2;      // scale * log2(e): scores go straight into exp2
+};
+
+struct ReduceParams {
+  const float* ws_o;
+  const float* ws_ml;
+  const int32_t* seq_lens;
+  void* out;
+  int32_t* status;
+  int B, n_q, Hq, D, P, max_parts, cap;
+};
+
+__device__ __forceinline__ void report(int32_t* status, int code) {
+  if (status) atomicMin(status, code);
+}
+
+// bf16 pair held in one 32-bit word: element 2i in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// a.x*b.x + a.y*b.y + c over bf16 pairs with an fp32 accumulator (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutes inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over groups of N consecutive lanes (N = 8, 16 or 32); every lane of a
+// group receives the group's total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Reduce across lanes that differ only in the bits at and above FROM (a power
+// of two <= 32): lanes with the same (lane % FROM) end up with the result.
+template <int FROM>
+__device__ __forceinline__ float cross_max(float x) {
+#pragma unroll
+  for (int m = FROM; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+template <int FROM>
+__device__ __forceinline__ float cross_sum(float x) {
+#pragma unroll
+  for (int m = FROM; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Orders LDS traffic of one wavefront: LDS instructions of a wave execute in
+// issue order, so a compiler-level barrier at wavefront scope is enough for a
+// wave-private LDS region.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace kvc

@@ -1,0 +1,282 @@
+// kvc_api.hip -- the C ABI of libkvc.so: argument checks, work planning and
+// kernel launches on the caller's stream.  Host code only; no allocation, no
+// synchronisation, no global state.
+#include <math.h>
+
+#include "launch.hpp"
+
+namespace {
+
+using namespace kvc;
+
+int check_desc(const kvc_cache_desc* d) {
+  if (!d) return KVC_ERR_ARG;
+  if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVC_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return KVC_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  if (d->dtype != KVC_BF16 && d->dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->block_size < 0) return KVC_ERR_SHAPE;
+  if (d->block_size == 0) {
+    if (d->max_seq_len <= 0) return KVC_ERR_SHAPE;
+  } else {
+    const int bs = d->block_size;
+    if (bs % kTile != 0 || (bs & (bs - 1)) != 0) return KVC_ERR_UNSUPPORTED;
+    if (d->max_blocks_per_seq <= 0 || d->num_blocks <= 0) return KVC_ERR_SHAPE;
+    if ((long)d->max_blocks_per_seq * bs > 0x7fffffffL) return KVC_ERR_SHAPE;
+  }
+  if (d->partition_tokens < 0 || d->partition_tokens % kTile != 0) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+int capacity(const kvc_cache_desc* d) {
+  return d->block_size ? d->max_blocks_per_seq * d->block_size : d->max_seq_len;
+}
+
+size_t elem_bytes(const kvc_cache_desc* d) { return d->dtype == KVC_BF16 ? 2 : 4; }
+
+struct Plan {
+  bool mfma;          // grouped rows on the matrix cores
+  int rows_per_item;  // mfma: 16 or 32 rows per wavefront
+  int P;              // partition length in tokens
+  int max_parts;      // partitions of a full-capacity sequence
+  size_t ml_offset;   // byte offset of the (m, l) array inside the workspace
+  size_t bytes;       // workspace size
+};
+
+// Work is one wavefront per (rows, partition).  The default partition length
+// is 256 keys (two 64 KiB streams of K and V for a 128-wide bf16 head); it is
+// halved while a full-capacity batch would give fewer than 4096 wavefronts.
+Plan make_plan(const kvc_cache_desc* d, int n_q) {
+  Plan pl{};
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int R = G * n_q;
+  pl.mfma = d->dtype == KVC_BF16 && R >= 2;
+  pl.rows_per_item = R > 16 ? 32 : 16;
+  const long units = pl.mfma ? (long)d->batch * d->num_kv_heads *
+                                   ((R + pl.rows_per_item - 1) / pl.rows_per_item)
+                             : (long)d->batch * d->num_q_heads * n_q;
+  const int cap = capacity(d);
+  if (d->partition_tokens > 0) {
+    pl.P = d->partition_tokens;
+  } else {
+    pl.P = 256;
+    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 4096) pl.P >>= 1;
+  }
+  pl.max_parts = (cap + pl.P - 1) / pl.P;
+  const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
+  const size_t o_bytes = rows * pl.max_parts * d->head_dim * sizeof(float);
+  pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
+  pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
+  return pl;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, const void* v,
+               const int32_t* seq_lens, const int32_t* table, float scale, const void* ws,
+               size_t ws_bytes) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!q || !k || !v || !seq_lens || !ws) return KVC_ERR_ARG;
+  if ((d->block_size > 0) != (table != nullptr)) return KVC_ERR_ARG;
+  if (!isfinite(scale)) return KVC_ERR_ARG;
+  if (((uintptr_t)ws & 15) != 0) return KVC_ERR_ARG;
+  if (ws_bytes < make_plan(d, n_q).bytes) return KVC_ERR_WORKSPACE;
+  return KVC_OK;
+}
+
+AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const void* q,
+                       const void* k, const void* v, const int32_t* seq_lens,
+                       const int32_t* table, float scale, void* ws, int32_t* status) {
+  AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.seq_lens = seq_lens;
+  p.table = table;
+  p.ws_o = (float*)ws;
+  p.ws_ml = (float*)((char*)ws + pl.ml_offset);
+  p.status = status;
+  p.B = d->batch;
+  p.n_q = n_q;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.G = d->num_q_heads / d->num_kv_heads;
+  p.D = d->head_dim;
+  p.bs = d->block_size;
+  p.S_max = d->max_seq_len;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.N = d->num_blocks;
+  p.P = pl.P;
+  p.max_parts = pl.max_parts;
+  p.cap = capacity(d);
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_block_table(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_new,
+                    int32_t total_new, int32_t* block_table, const int32_t* free_list,
+                    const int32_t* free_head_in, int32_t* free_head_out, int32_t* slot_mapping,
+                    int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;  // contiguous caches have no table
+  if (total_new < 0) return KVC_ERR_ARG;
+  if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !block_table || !free_list || !free_head_in || !free_head_out)
+    return KVC_ERR_ARG;
+  if (total_new > 0 && !slot_mapping) return KVC_ERR_ARG;
+  BlockTableArgs a{};
+  a.seq_lens = seq_lens;
+  a.cu_new = cu_new;
+  a.table = block_table;
+  a.free_list = free_list;
+  a.head_in = free_head_in;
+  a.head_out = free_head_out;
+  a.slots = slot_mapping;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.bs = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.N = d->num_blocks;
+  a.total_new = total_new;
+  return hip_status(launch_block_table(a, (hipStream_t)stream));
+}
+
+int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+               const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new, int32_t max_new,
+               const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t* seq_lens_out,
+               int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
+  if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !k_cache || !v_cache || !seq_lens_out) return KVC_ERR_ARG;
+  if (seq_lens_out == seq_lens) return KVC_ERR_ARG;
+  if (total_new > 0 && (!k_new || !v_new)) return KVC_ERR_ARG;
+  if (d->block_size > 0 && total_new > 0 && !slot_mapping) return KVC_ERR_ARG;
+  if (d->block_size == 0 && slot_mapping) return KVC_ERR_ARG;
+  AppendArgs a{};
+  a.k_new = (const uint8_t*)k_new;
+  a.v_new = (const uint8_t*)v_new;
+  a.seq_lens = seq_lens;
+  a.cu_new = cu_new;
+  a.slots = d->block_size > 0 ? slot_mapping : nullptr;
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.seq_lens_out = seq_lens_out;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.Hkv = d->num_kv_heads;
+  a.head_bytes = (int)(d->head_dim * elem_bytes(d));
+  a.bs = d->block_size;
+  a.S_max = d->max_seq_len;
+  a.N = d->num_blocks;
+  a.max_new = max_new;
+  a.total_new = total_new;
+  if (d->block_size > 0 && total_new == 0) a.slots = nullptr, a.S_max = 0x7fffffff;
+  return hip_status(launch_append(a, (hipStream_t)stream));
+}
+
+int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
+                       const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                       float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                       void* stream) {
+  int st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
+                      workspace_bytes);
+  if (st != KVC_OK || d->batch == 0) return st;
+  const Plan pl = make_plan(d, n_q);
+  const AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
+                                   workspace, dev_status);
+  hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, (hipStream_t)stream)
+                         : launch_partition_valu(p, d->dtype, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_lens,
+                    const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
+                    int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!seq_lens || !workspace || !out) return KVC_ERR_ARG;
+  if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
+  const Plan pl = make_plan(d, n_q);
+  if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
+  ReduceParams p{};
+  p.ws_o = (const float*)workspace;
+  p.ws_ml = (const float*)((const char*)workspace + pl.ml_offset);
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.status = dev_status;
+  p.B = d->batch;
+  p.n_q = n_q;
+  p.Hq = d->num_q_heads;
+  p.D = d->head_dim;
+  p.P = pl.P;
+  p.max_parts = pl.max_parts;
+  p.cap = capacity(d);
+  return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
+}
+
+int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                    float scale, void* out, int32_t out_dtype, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  int st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
+                      workspace_bytes);
+  if (st != KVC_OK) return st;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!out) return KVC_ERR_ARG;
+  st = kvc_attn_partition(d, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
+                          workspace_bytes, dev_status, stream);
+  if (st != KVC_OK) return st;
+  return kvc_attn_reduce(d, n_q, seq_lens, workspace, workspace_bytes, out, out_dtype, dev_status,
+                         stream);
+}
+
+int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                    float scale, void* out, int32_t out_dtype, void* workspace,
+                    size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  return kvc_verify_attn(d, q, 1, k_cache, v_cache, seq_lens, block_table, scale, out, out_dtype,
+                         workspace, workspace_bytes, dev_status, stream);
+}
+
+size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q) {
+  if (check_desc(d) != KVC_OK || n_q < 1 || n_q > 16) return 0;
+  return make_plan(d, n_q).bytes;
+}
+
+int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q) {
+  const int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  return make_plan(d, n_q).P;
+}
+
+const char* kvc_status_string(int32_t status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_ARG: return "invalid argument";
+    case KVC_ERR_SHAPE: return "inconsistent shape";
+    case KVC_ERR_UNSUPPORTED: return "unsupported size or type";
+    case KVC_ERR_WORKSPACE: return "workspace too small";
+    case KVC_ERR_CAPACITY: return "sequence capacity exceeded";
+    case KVC_ERR_NO_BLOCKS: return "free block list exhausted";
+    case KVC_ERR_HIP: return "HIP launch failed";
+    case KVC_ERR_DATA: return "device data out of range";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// launch.hpp -- host-side launchers of the kvc kernels (internal to libkvc.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace kvc {
+
+struct BlockTableArgs {
+  const int32_t* seq_lens;
+  const int32_t* cu_new;
+  int32_t* table;
+  const int32_t* free_list;
+  const int32_t* head_in;
+  int32_t* head_out;
+  int32_t* slots;
+  int32_t* status;
+  int B, bs, max_blocks, N, total_new;
+};
+
+struct AppendArgs {
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const int32_t* seq_lens;
+  const int32_t* cu_new;
+  const int32_t* slots;  // NULL: contiguous
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int32_t* seq_lens_out;
+  int32_t* status;
+  int B, Hkv, head_bytes, bs, S_max, N, max_new, total_new;
+};
+
+hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+// dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)
+hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,160 @@
+// paging.hip -- block-table allocation and the K/V append (integer and byte work).
+//
+// Block table: "Inference-1" (brunomaga.github.io), "PagedAttention": fixed-size
+// blocks allocated on demand, a per-sequence logical -> physical table; "Inference
+// o quy mo lon" (truongducdung.dev), 05 "Block table": a block is taken only when
+// the last one is full.  Append: "Efficient Inference" (learn.obvix.io), KV-cache
+// passage: rows written in place at the current length of a preallocated cache.
+#include "launch.hpp"
+
+namespace kvc {
+
+constexpr int kBtThreads = 1024;
+
+// One workgroup.  Pass 1 validates and counts the new blocks of every sequence;
+// pass 2 assigns them in batch order with a chunked exclusive scan, consuming
+// the free list front to back; pass 3 maps every new token to its slot.
+__global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs a) {
+  __shared__ int s_scan[kBtThreads];
+  __shared__ int s_err, s_head, s_total;
+  const int tid = threadIdx.x;
+  const int bs = a.bs;
+  if (tid == 0) {
+    s_err = 0;
+    s_head = *a.head_in;
+    s_total = 0;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += kBtThreads) {
+    const int len = a.seq_lens[b];
+    const int n = a.cu_new[b + 1] - a.cu_new[b];
+    if (len < 0 || n < 0) {
+      atomicMin(&s_err, KVC_ERR_DATA);
+      continue;
+    }
+    const long have = ((long)len + bs - 1) / bs;
+    const long want = ((long)len + n + bs - 1) / bs;
+    if (want > a.max_blocks) atomicMin(&s_err, KVC_ERR_CAPACITY);
+    else atomicAdd(&s_total, (int)(want - have));
+  }
+  __syncthreads();
+  if (tid == 0 && s_err == 0 && (s_head < 0 || (long)s_head + s_total > a.N))
+    s_err = KVC_ERR_NO_BLOCKS;
+  __syncthreads();
+  if (s_err != 0) {
+    if (tid == 0) {
+      report(a.status, s_err);
+      *a.head_out = s_head;
+    }
+    return;
+  }
+
+  int carry = 0;
+  for (int base = 0; base < a.B; base += kBtThreads) {
+    const int b = base + tid;
+    int have = 0, need = 0;
+    if (b < a.B) {
+      const int len = a.seq_lens[b];
+      const int n = a.cu_new[b + 1] - a.cu_new[b];
+      have = (len + bs - 1) / bs;
+      need = (int)(((long)len + n + bs - 1) / bs) - have;
+    }
+    s_scan[tid] = need;
+    __syncthreads();
+    for (int off = 1; off < kBtThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int first = s_head + carry + s_scan[tid] - need;
+    for (int i = 0; i < need; ++i)
+      a.table[(long)b * a.max_blocks + have + i] = a.free_list[first + i];
+    carry += s_scan[kBtThreads - 1];
+    __syncthreads();
+  }
+  __syncthreads();  // table entries written above are read below by other threads
+
+  for (int i = tid; i < a.total_new; i += kBtThreads) {
+    int lo = 0, hi = a.B - 1;  // last b with cu_new[b] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_new[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const long pos = (long)a.seq_lens[lo] + (i - a.cu_new[lo]);
+    if (i >= a.cu_new[lo + 1] || pos / bs >= a.max_blocks) {  // cu_new disagrees with total_new
+      a.slots[i] = -1;
+      report(a.status, KVC_ERR_DATA);
+      continue;
+    }
+    const long blk = a.table[(long)lo * a.max_blocks + pos / bs];
+    a.slots[i] = (int32_t)(blk * bs + pos % bs);
+  }
+  if (tid == 0) *a.head_out = s_head + s_total;
+}
+
+constexpr int kAppendThreads = 256;
+constexpr int kAppendTokPerWg = 4;
+
+// grid = (ceil(max_new / kAppendTokPerWg), B).  Every row is a head_bytes-long
+// run copied in 16-byte pieces, no conversion.
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.y;
+  const int len = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n = a.cu_new[b + 1] - c0;
+  const bool bad = len < 0 || n < 0 || (a.slots == nullptr && (long)len + n > a.S_max);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.seq_lens_out[b] = bad ? len : len + n;
+    if (bad) report(a.status, (len < 0 || n < 0) ? KVC_ERR_DATA : KVC_ERR_CAPACITY);
+    // more new tokens than the host's max_new promised: the excess is not written
+    else if (n > (long)gridDim.x * kAppendTokPerWg) report(a.status, KVC_ERR_DATA);
+  }
+  if (bad) return;
+  const int t0 = blockIdx.x * kAppendTokPerWg;
+  const int t1 = min(t0 + kAppendTokPerWg, n);
+  const int vec_per_head = a.head_bytes >> 4;
+  const int vec_per_tok = a.Hkv * vec_per_head;
+  for (int t = t0; t < t1; ++t) {
+    const long src_tok = (long)c0 + t;
+    if (src_tok >= a.total_new) {  // cu_new points past the new-row buffers
+      if (threadIdx.x == 0) report(a.status, KVC_ERR_DATA);
+      break;
+    }
+    long blk = 0, off = 0;
+    if (a.slots) {
+      const long slot = a.slots[src_tok];
+      if (slot < 0 || slot >= (long)a.N * a.bs) {
+        if (threadIdx.x == 0) report(a.status, KVC_ERR_DATA);
+        continue;
+      }
+      blk = slot / a.bs;
+      off = slot % a.bs;
+    }
+    for (int idx = threadIdx.x; idx < vec_per_tok; idx += kAppendThreads) {
+      const int g = idx / vec_per_head;
+      const int w = idx - g * vec_per_head;
+      const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+      long dst;
+      if (a.slots) dst = ((blk * a.Hkv + g) * a.bs + off) * a.head_bytes + w * 16;
+      else dst = (((long)b * a.Hkv + g) * a.S_max + len + t) * a.head_bytes + w * 16;
+      *reinterpret_cast<uint4*>(a.k_cache + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
+      *reinterpret_cast<uint4*>(a.v_cache + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
+    }
+  }
+}
+
+hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(block_table_kernel, dim3(1), dim3(kBtThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const int gx = a.max_new > 0 ? (a.max_new + kAppendTokPerWg - 1) / kAppendTokPerWg : 1;
+  hipLaunchKernelGGL(append_kernel, dim3(gx, a.B), dim3(kAppendThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

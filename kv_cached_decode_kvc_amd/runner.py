@@ -1,0 +1,183 @@
+"""One layer's KV cache in device memory, driven through the C ABI.
+
+``LayerCache`` owns the device buffers of a workload (cache or block pool,
+block table, free list, lengths, workspace) and runs the decode step the way a
+serving loop would: ``kvc_block_table`` (paged caches) -> ``kvc_append`` ->
+``kvc_attn_partition`` -> ``kvc_attn_reduce``.  Every step of the computation
+runs in the library's kernels; this module only allocates tensors with torch
+and passes their addresses.
+
+A prepared step (``prepare_step``) reads lengths and the free-list head from
+buffers it never writes, so it can be replayed any number of times with an
+identical effect: the benchmark times exactly that replay.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import kvc, synth
+
+
+def to_dev(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
+    """Host rows (bf16 bit patterns or float32) -> device tensor of that element type."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def i32(a, dev="cuda") -> torch.Tensor:
+    return torch.as_tensor(np.asarray(a, dtype=np.int32)).to(dev)
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+class LayerCache:
+    def __init__(self, w: synth.Workload, partition_tokens: int = 0, dev="cuda",
+                 block_size: int | None = None, capacity: int | None = None,
+                 pool_blocks: int | None = None, poison_nan: bool = False):
+        self.w, self.dev = w, dev
+        self.bs = w.block_size if block_size is None else block_size
+        cap = capacity or synth.capacity_tokens(w)
+        tdt = torch_dtype(w.dtype)
+        fill = float("nan") if poison_nan else 0.0
+        if self.bs == 0:
+            self.cap = cap
+            shape = (w.B, w.Hkv, cap, w.D)
+            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.dtype, 0, max_seq_len=cap,
+                                       partition_tokens=partition_tokens)
+            self.table = None
+            self.N = 0
+            self.max_blocks = 0
+        else:
+            self.max_blocks = -(-cap // self.bs)
+            self.cap = self.max_blocks * self.bs
+            if pool_blocks is None:
+                pool_blocks = (w.B * self.max_blocks + w.B if block_size is not None
+                               else synth.pool_blocks(w))
+            self.N = pool_blocks
+            shape = (self.N, w.Hkv, self.bs, w.D)
+            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.dtype, self.bs,
+                                       max_blocks_per_seq=self.max_blocks, num_blocks=self.N,
+                                       partition_tokens=partition_tokens)
+            self.table = torch.full((w.B, self.max_blocks), -1, dtype=torch.int32, device=dev)
+            self.free_host = synth.rng(w, synth.S_POOL).permutation(self.N).astype(np.int32)
+            self.free_list = i32(self.free_host, dev)
+            self.head = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.k = torch.full(shape, fill, dtype=tdt, device=dev)
+        self.v = torch.full(shape, fill, dtype=tdt, device=dev)
+        self.seq_lens = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.n_q = w.n_q
+        self.scale = 1.0 / math.sqrt(w.D)
+
+    # -- building the cache ----------------------------------------------
+    def add_tokens(self, k_rows: np.ndarray, v_rows: np.ndarray, counts):
+        """Append counts[b] packed rows per sequence (host arrays); returns the
+        slot mapping of a paged cache."""
+        w = self.w
+        counts = np.asarray(counts, dtype=np.int64)
+        cu = synth.cu_from_counts(counts)
+        total = int(cu[-1])
+        cu_d = i32(cu, self.dev)
+        slots = None
+        if self.bs:
+            slots = torch.empty(max(total, 1), dtype=torch.int32, device=self.dev)
+            kvc.kvc_block_table(self.desc, self.seq_lens, cu_d, total, self.table, self.free_list,
+                                self.head, self.head, slots, self.status)
+        out = torch.empty_like(self.seq_lens)
+        kvc.kvc_append(self.desc, to_dev(k_rows, w.dtype, self.dev),
+                       to_dev(v_rows, w.dtype, self.dev), self.seq_lens, cu_d, total,
+                       int(counts.max()) if len(counts) else 0, slots, self.k, self.v, out,
+                       self.status)
+        self.seq_lens = out
+        return slots
+
+    def prefill(self, lengths):
+        """The cached rows of every sequence (the generator's stream of cached keys/values)."""
+        w = self.w
+        return self.add_tokens(synth.packed_cache_rows(w, "k", lengths),
+                               synth.packed_cache_rows(w, "v", lengths), lengths)
+
+    def step_rows(self, step=0):
+        w = self.w
+        return self.add_tokens(synth.packed_new_rows(w, "k", step),
+                               synth.packed_new_rows(w, "v", step), [w.n_q] * w.B)
+
+    def workspace(self, n_q):
+        nbytes = kvc.kvc_attn_workspace_bytes(self.desc, n_q)
+        return torch.empty(max((nbytes + 3) // 4, 4), dtype=torch.float32, device=self.dev)
+
+    def attend(self, q: torch.Tensor, n_q: int, out_dtype=torch.float32, scale=None,
+               seq_lens=None) -> torch.Tensor:
+        w = self.w
+        scale = self.scale if scale is None else scale
+        out = torch.empty((w.B, n_q, w.Hq, w.D), dtype=out_dtype, device=self.dev)
+        ws = self.workspace(n_q)
+        sl = self.seq_lens if seq_lens is None else seq_lens
+        if n_q == 1:
+            kvc.kvc_decode_attn(self.desc, q, self.k, self.v, sl, self.table, scale, out, ws,
+                                self.status)
+        else:
+            kvc.kvc_verify_attn(self.desc, q, n_q, self.k, self.v, sl, self.table, scale, out, ws,
+                                self.status)
+        return out
+
+    def dev_status(self) -> int:
+        torch.cuda.synchronize()
+        return int(self.status.item())
+
+    # -- a replayable decode step ------------------------------------------
+    def prepare_step(self, step=0):
+        """Stage one decode step's inputs (new rows, queries) on the device.  The
+        cache must already hold the cached rows (``prefill``)."""
+        w = self.w
+        self.s_len0 = self.seq_lens.clone()  # lengths before the step: never written
+        self.s_len1 = torch.empty_like(self.seq_lens)
+        self.s_cu = i32(synth.cu_from_counts([w.n_q] * w.B), self.dev)
+        self.s_total = w.n_q * w.B
+        self.s_k = to_dev(synth.packed_new_rows(w, "k", step), w.dtype, self.dev)
+        self.s_v = to_dev(synth.packed_new_rows(w, "v", step), w.dtype, self.dev)
+        self.s_q = to_dev(synth.packed_queries(w, step), w.dtype, self.dev)
+        self.s_out = torch.empty((w.B, w.n_q, w.Hq, w.D), dtype=torch.float32, device=self.dev)
+        self.s_ws = self.workspace(w.n_q)
+        if self.bs:
+            self.s_head0 = self.head.clone()  # free-list head before the step: never written
+            self.s_head1 = torch.empty_like(self.head)
+            self.s_slots = torch.empty(self.s_total, dtype=torch.int32, device=self.dev)
+        else:
+            self.s_slots = None
+
+    def step_front(self):
+        """Block table (paged) and append of the prepared step."""
+        if self.bs:
+            kvc.kvc_block_table(self.desc, self.s_len0, self.s_cu, self.s_total, self.table,
+                                self.free_list, self.s_head0, self.s_head1, self.s_slots,
+                                self.status)
+        kvc.kvc_append(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu, self.s_total,
+                       self.w.n_q, self.s_slots, self.k, self.v, self.s_len1, self.status)
+
+    def step_partition(self):
+        kvc.kvc_attn_partition(self.desc, self.s_q, self.w.n_q, self.k, self.v, self.s_len1,
+                               self.table, self.scale, self.s_ws, self.status)
+
+    def step_reduce(self):
+        kvc.kvc_attn_reduce(self.desc, self.w.n_q, self.s_len1, self.s_ws, self.s_out, self.status)
+
+    def step(self):
+        self.step_front()
+        self.step_partition()
+        self.step_reduce()
+        return self.s_out
+
+
+def build(w: synth.Workload, step=0, **kw) -> LayerCache:
+    """A full workload on the device: cached rows appended, one step prepared."""
+    lc = LayerCache(w, **kw)
+    lc.prefill(synth.cached_lengths(w))
+    lc.prepare_step(step)
+    return lc

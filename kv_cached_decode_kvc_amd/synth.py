@@ -14,6 +14,8 @@ workload is bf16.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -80,10 +82,18 @@ def rng(w: Workload, stream: int, *ids: int) -> np.random.Generator:
     return np.random.default_rng([w.seed, stream, *ids])
 
 
-def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+def to_bf16_bits(x: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
     """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    u += t
+    u >>= 16
+    if out is None:
+        return u.astype(np.uint16)
+    out[...] = u
+    return out
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -149,10 +159,24 @@ def cu_from_counts(counts) -> np.ndarray:
     return cu
 
 
-def packed_cache_rows(w: Workload, which: str, lengths) -> np.ndarray:
-    """All sequences' cached rows packed in batch order: [sum(lengths), Hkv, D]."""
-    parts = [cache_rows(w, which, b, int(n)) for b, n in enumerate(lengths)]
-    return np.concatenate(parts, axis=0) if parts else np.zeros((0, w.Hkv, w.D))
+def packed_cache_rows(w: Workload, which: str, lengths, threads: int = 16) -> np.ndarray:
+    """All sequences' cached rows packed in batch order: [sum(lengths), Hkv, D].
+    Sequences are drawn in parallel threads (each from its own stream)."""
+    cu = cu_from_counts(lengths)
+    out = np.empty((int(cu[-1]), w.Hkv, w.D), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
+    stream = S_KCACHE if which == "k" else S_VCACHE
+
+    def fill(b):
+        n = int(cu[b + 1] - cu[b])
+        x = rng(w, stream, b).standard_normal((n, w.Hkv, w.D), dtype=np.float32)
+        if w.dtype == "bf16":
+            to_bf16_bits(x, out[cu[b]:cu[b + 1]])
+        else:
+            out[cu[b]:cu[b + 1]] = x
+
+    with ThreadPoolExecutor(max_workers=max(1, min(threads, os.cpu_count() or 1))) as ex:
+        list(ex.map(fill, range(len(lengths))))
+    return out
 
 
 def packed_new_rows(w: Workload, which: str, step: int = 0) -> np.ndarray:

@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: it loads, exports every symbol its header
+declares, and refuses bad arguments before any launch (no GPU needed: each
+call here returns during argument checking)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cached_decode_kvc_amd import kvc, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvc.LIB_PATH):
+        from kv_cached_decode_kvc_amd import build
+        build.build(verbose=False)
+    return kvc.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(kvc_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for n in ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn"):
+        assert n in names
+    assert set(names) == set(kvc.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", kvc.LIB_PATH], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def desc(**kw):
+    base = dict(batch=16, num_q_heads=40, num_kv_heads=40, head_dim=128, dtype=0, block_size=0,
+                max_seq_len=2048, max_blocks_per_seq=0, num_blocks=0, partition_tokens=0)
+    base.update(kw)
+    return kvc.kvc_cache_desc(*[base[f] for f, _ in kvc.kvc_cache_desc._fields_])
+
+
+def decode(lib, d, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, table=None, scale=0.1, out=FAKE, out_dtype=1,
+           ws=FAKE, ws_bytes=1 << 40):
+    return lib.kvc_decode_attn(ctypes.byref(d) if d is not None else None, q, k, v, sl, table,
+                               scale, out, out_dtype, ws, ws_bytes, None, None)
+
+
+def test_attention_argument_errors(lib):
+    assert decode(lib, None) == -1
+    assert decode(lib, desc(head_dim=96)) == -3
+    assert decode(lib, desc(num_kv_heads=7)) == -2
+    assert decode(lib, desc(dtype=7)) == -3
+    assert decode(lib, desc(block_size=24, max_blocks_per_seq=4, num_blocks=8), table=FAKE) == -3
+    assert decode(lib, desc(block_size=48, max_blocks_per_seq=4, num_blocks=8), table=FAKE) == -3
+    assert decode(lib, desc(partition_tokens=24)) == -3
+    assert decode(lib, desc(), q=None) == -1
+    assert decode(lib, desc(), table=FAKE) == -1  # contiguous cache with a table
+    assert decode(lib, desc(block_size=16, max_blocks_per_seq=4, num_blocks=8)) == -1  # no table
+    assert decode(lib, desc(), ws_bytes=100) == -4
+    assert decode(lib, desc(), ws=ctypes.c_void_p(0x1004)) == -1  # misaligned workspace
+    assert decode(lib, desc(), scale=float("nan")) == -1
+    assert decode(lib, desc(), out_dtype=5) == -3
+    assert decode(lib, desc(max_seq_len=0)) == -2
+    d = desc()
+    for n_q in (0, 17):
+        assert lib.kvc_verify_attn(ctypes.byref(d), FAKE, n_q, FAKE, FAKE, FAKE, None, 0.1, FAKE, 1,
+                                   FAKE, 1 << 40, None, None) == -3
+    # an empty batch is a no-op: nothing to check, nothing launched
+    assert decode(lib, desc(batch=0), q=None, k=None, v=None, sl=None, out=None, ws=None) == 0
+
+
+def test_paging_argument_errors(lib):
+    paged = desc(block_size=16, max_blocks_per_seq=8, num_blocks=64)
+    contig = desc()
+    assert lib.kvc_block_table(ctypes.byref(contig), FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None) == -1
+    assert lib.kvc_block_table(ctypes.byref(paged), FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None) == -1
+    assert lib.kvc_block_table(ctypes.byref(paged), FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, None,
+                               None, None) == -1
+    same = FAKE
+    assert lib.kvc_append(ctypes.byref(contig), FAKE, FAKE, same, FAKE, 1, 1, None, FAKE, FAKE,
+                          same, None, None) == -1  # seq_lens_out aliases seq_lens
+    assert lib.kvc_append(ctypes.byref(contig), FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
+                          ctypes.c_void_p(0x2000), None, None) == -1  # slots on a contiguous cache
+    assert lib.kvc_append(ctypes.byref(paged), FAKE, FAKE, FAKE, FAKE, 1, 1, None, FAKE, FAKE,
+                          ctypes.c_void_p(0x2000), None, None) == -1  # paged without slots
+    assert lib.kvc_append(ctypes.byref(contig), None, FAKE, FAKE, FAKE, 1, 1, None, FAKE, FAKE,
+                          ctypes.c_void_p(0x2000), None, None) == -1
+
+
+def test_workspace_and_partition_sizes(lib):
+    d = desc()  # 16 x 40 heads, contiguous, 2048 tokens
+    assert kvc.kvc_attn_partition_tokens(d, 1) == 256
+    rows, parts = 16 * 40, 2048 // 256
+    o = rows * parts * 128 * 4
+    assert kvc.kvc_attn_workspace_bytes(d, 1) == ((o + 255) // 256) * 256 + rows * parts * 2 * 4
+    small = desc(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=64, max_seq_len=288, dtype=1)
+    assert kvc.kvc_attn_partition_tokens(small, 1) == 64  # halved while fewer than 4096 items
+    assert kvc.kvc_attn_partition_tokens(desc(partition_tokens=48), 1) == 48
+    assert kvc.kvc_attn_workspace_bytes(desc(head_dim=80), 1) == 0
+    assert kvc.kvc_attn_partition_tokens(desc(head_dim=80), 1) == -3
+    for name in ("C2", "C3", "C4", "C5"):
+        w = synth.get(name)
+        dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                  block_size=w.block_size, max_seq_len=synth.capacity_tokens(w),
+                  max_blocks_per_seq=synth.max_blocks_per_seq(w) if w.block_size else 0,
+                  num_blocks=synth.pool_blocks(w) if w.block_size else 0)
+        P = kvc.kvc_attn_partition_tokens(dd, w.n_q)
+        assert P > 0 and P % 16 == 0
+        assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) > 0
+
+
+def test_status_strings(lib):
+    for code, name in kvc.STATUS_NAMES.items():
+        s = kvc.kvc_status_string(code)
+        assert s and s != "unknown status", name
+    assert kvc.kvc_status_string(-99) == "unknown status"
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = desc(batch=1, num_q_heads=1, num_kv_heads=1, head_dim=64, max_seq_len=16)
+    t = torch.zeros(16)
+    with pytest.raises(ValueError):
+        kvc.kvc_decode_attn(d, t, t, t, t.int(), None, 0.1, t, t)
