@@ -97,10 +97,10 @@ def test_block_table_exhaustion_changes_nothing():
     gc.prefill([20, 10])  # takes 3 blocks: pool is now empty
     assert gc.dev_status() == 0 and int(gc.head.item()) == 3
     table_before = gc.table.clone()
-    cu = i32([0, 12, 13])  # sequence 0 needs a 3rd block, sequence 1 fits in its block
-    slots = torch.full((13,), -7, dtype=torch.int32, device="cuda")
+    cu = i32([0, 13, 14])  # sequence 0 reaches 33 tokens: a 3rd block; sequence 1 fits
+    slots = torch.full((14,), -7, dtype=torch.int32, device="cuda")
     head_out = torch.full((1,), -9, dtype=torch.int32, device="cuda")
-    kvc.kvc_block_table(gc.desc, gc.seq_lens, cu, 13, gc.table, gc.free_list, gc.head, head_out,
+    kvc.kvc_block_table(gc.desc, gc.seq_lens, cu, 14, gc.table, gc.free_list, gc.head, head_out,
                         slots, gc.status)
     assert gc.dev_status() == -6
     assert torch.equal(gc.table, table_before) and int(head_out.item()) == 3
