@@ -8,7 +8,7 @@
 // out = sum_p w_p O_p / sum_p w_p l_p, then one rounding to the output type.
 //
 // One wavefront per output row (sequence, query head, query row); each lane
-// owns D/64 consecutive columns.
+// owns D/64 consecutive columns and, for the statistics, one partition.
 #include "launch.hpp"
 
 namespace kvc {
@@ -31,18 +31,42 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   float den = 0.f;
   if (L >= p.n_q && L <= p.cap) {
     const int nparts = (L + p.P - 1) / p.P;
-    const float* ml = p.ws_ml + row * p.max_parts * 2;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
     const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
+    // every lane fetches one partition's (m, l): all of them in one round trip
     float mstar = -INFINITY;
-    for (int q = 0; q < nparts; ++q) mstar = fmaxf(mstar, ml[2 * q]);
-    for (int q = 0; q < nparts; ++q) {
-      const float mq = ml[2 * q];
-      if (mq == -INFINITY) continue;  // partition with no visible key
-      const float w = fast_exp2(mq - mstar);
-      den += w * ml[2 * q + 1];
+    for (int q0 = 0; q0 < nparts; q0 += kWave)
+      if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[q0 + lane].x);
+    for (int m = 1; m < kWave; m <<= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, m));
+    for (int q0 = 0; q0 < nparts; q0 += kWave) {
+      float wq = 0.f;
+      if (q0 + lane < nparts) {
+        const float2 mq = ml[q0 + lane];
+        wq = mq.x == -INFINITY ? 0.f : fast_exp2(mq.x - mstar);  // empty partition: 0
+        den += wq * mq.y;
+      }
+      const int cnt = min(kWave, nparts - q0);
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {  // four partitions' loads in flight at once
+        float o[4][CPL];
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) acc[j] += w * po[(long)q * D + j];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) o[u][c] = po[(long)(q0 + j + u) * D + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wj = __shfl(wq, j + u);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] += wj * o[u][c];
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float wj = __shfl(wq, j);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] += wj * po[(long)(q0 + j) * D + c];
+      }
     }
+    for (int m = 1; m < kWave; m <<= 1) den += __shfl_xor(den, m);
   } else if (lane == 0 && h == 0 && r == 0) {
     report(p.status, KVC_ERR_DATA);
   }

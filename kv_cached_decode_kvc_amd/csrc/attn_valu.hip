@@ -2,8 +2,8 @@
 // per wavefront.
 //
 // Computes, for one (sequence b, query head h, query row r, partition p), the
-// running maximum m, running sum l and unnormalised output O over the keys
-// [p*P, min((p+1)*P, visible)) -- the online-softmax recurrence of "Inference-1"
+// running maximum m, running sum l and unnormalised output O over the visible
+// keys of the partition's tiles -- the online-softmax recurrence of "Inference-1"
 // (brunomaga.github.io), section "FlashAttention", and of "Inference o quy mo lon"
 // (truongducdung.dev), 07 "Online softmax"; the partitioning is the split-KV of
 // "Inference-1", section "FlashDecoding".  Row r of n_q sees keys
@@ -11,6 +11,13 @@
 //
 // Used for MHA (one query row per KV row, so there is no dense contraction to
 // give to the matrix cores) and for every fp32 cache.
+//
+// Partition p of a sequence's n = ceil(L / P) partitions owns the 16-key tiles
+// p, p + n, p + 2n, ...: the wavefronts of one sequence run side by side and
+// read neighbouring tiles at the same time.  Any split of the keys gives the
+// same softmax once the partials are combined; this one keeps the memory
+// traffic of concurrent wavefronts inside a narrow window.  Keys are streamed
+// with non-temporal loads: they are read exactly once.
 //
 // Layout of the work: a wavefront streams 16-key tiles.  A key row of D
 // elements is split over LPR lanes holding 16 bytes each, so one 16-byte load
@@ -93,8 +100,9 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
   }
   const int nparts = (L + p.P - 1) / p.P;
   if (part >= nparts) return;
-  const int start = part * p.P;
-  const int end = min(start + p.P, L - p.n_q + r + 1);  // visible keys of row r
+  const int start = part * kTile;              // first tile of this partition
+  const int stride = nparts * kTile;            // distance to its next tile
+  const int end = L - p.n_q + r + 1;            // visible keys of row r
   const long row = ((long)b * p.Hq + h) * p.n_q + r;
   float* wo = p.ws_o + (row * p.max_parts + part) * D;
   float* wml = p.ws_ml + (row * p.max_parts + part) * 2;
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
     const T* vbase = (const T*)p.v;
     const uint4 qv = *reinterpret_cast<const uint4*>(
         (const T*)p.q + (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
-    for (int tile = start; tile < end; tile += kTile) {
+    for (int tile = start; tile < end; tile += stride) {
       long tbase;  // element offset of key `tile` of (b, g)
       if (p.table == nullptr) {
         tbase = (((long)b * p.Hkv + g) * p.S_max + tile) * D;
@@ -131,8 +139,8 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
         int tt = u * RPL + r0;
         tt = tt < nvalid ? tt : nvalid - 1;  // masked lanes re-read a visible row
         const long off = tbase + (long)tt * D + c * VE;
-        kr[u] = *reinterpret_cast<const uint4*>(kbase + off);
-        vr[u] = *reinterpret_cast<const uint4*>(vbase + off);
+        kr[u] = load_stream(kbase + off);
+        vr[u] = load_stream(vbase + off);
       }
       float s[U];
       float mx = -INFINITY;

@@ -12,6 +12,7 @@ using namespace kvc;
 int check_desc(const kvc_cache_desc* d) {
   if (!d) return KVC_ERR_ARG;
   if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVC_ERR_SHAPE;
+  if (d->batch > 65535) return KVC_ERR_UNSUPPORTED;  // one grid row per sequence
   if (d->num_q_heads % d->num_kv_heads != 0) return KVC_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return KVC_ERR_UNSUPPORTED;
   if (d->dtype != KVC_BF16 && d->dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
@@ -44,8 +45,10 @@ struct Plan {
 };
 
 // Work is one wavefront per (rows, partition).  The default partition length
-// is 256 keys (two 64 KiB streams of K and V for a 128-wide bf16 head); it is
-// halved while a full-capacity batch would give fewer than 4096 wavefronts.
+// is the smallest power of two from 256 keys up such that a batch at full
+// capacity gives at most about two rounds of resident wavefronts (5 per SIMD
+// x 4 SIMDs x 256 CUs); short caches halve it, down to 64, while there would
+// be fewer than 4096 wavefronts.
 Plan make_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -59,7 +62,9 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
+    const long two_rounds = 2L * 5 * 4 * 256;
     pl.P = 256;
+    while (pl.P < 4096 && units * ((cap + pl.P - 1) / pl.P) > two_rounds) pl.P <<= 1;
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 4096) pl.P >>= 1;
   }
   pl.max_parts = (cap + pl.P - 1) / pl.P;

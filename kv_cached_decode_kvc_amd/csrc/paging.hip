@@ -97,10 +97,17 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
 constexpr int kAppendThreads = 256;
 constexpr int kAppendTokPerWg = 4;
 
-// grid = (ceil(max_new / kAppendTokPerWg), B).  Every row is a head_bytes-long
-// run copied in 16-byte pieces, no conversion.
+// grid = (vector chunks x token chunks, B): every thread moves one 16-byte
+// piece of one new token's K row and V row (a row of a KV head is head_bytes
+// long), bit for bit.  Decode steps have one token per sequence, so the grid
+// spreads the heads over many workgroups instead of looping inside a few.
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int b = blockIdx.y;
+  const int vec_per_head = a.head_bytes >> 4;
+  const int vec_per_tok = a.Hkv * vec_per_head;
+  const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  const int vchunk = blockIdx.x % n_vchunks;
+  const int tchunk = blockIdx.x / n_vchunks;
   const int len = a.seq_lens[b];
   const int c0 = a.cu_new[b];
   const int n = a.cu_new[b + 1] - c0;
@@ -109,39 +116,37 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     a.seq_lens_out[b] = bad ? len : len + n;
     if (bad) report(a.status, (len < 0 || n < 0) ? KVC_ERR_DATA : KVC_ERR_CAPACITY);
     // more new tokens than the host's max_new promised: the excess is not written
-    else if (n > (long)gridDim.x * kAppendTokPerWg) report(a.status, KVC_ERR_DATA);
+    else if (n > (long)(gridDim.x / n_vchunks) * kAppendTokPerWg) report(a.status, KVC_ERR_DATA);
   }
   if (bad) return;
-  const int t0 = blockIdx.x * kAppendTokPerWg;
+  const int idx = vchunk * kAppendThreads + threadIdx.x;
+  if (idx >= vec_per_tok) return;
+  const int g = idx / vec_per_head;
+  const int w = idx - g * vec_per_head;
+  const int t0 = tchunk * kAppendTokPerWg;
   const int t1 = min(t0 + kAppendTokPerWg, n);
-  const int vec_per_head = a.head_bytes >> 4;
-  const int vec_per_tok = a.Hkv * vec_per_head;
   for (int t = t0; t < t1; ++t) {
     const long src_tok = (long)c0 + t;
     if (src_tok >= a.total_new) {  // cu_new points past the new-row buffers
-      if (threadIdx.x == 0) report(a.status, KVC_ERR_DATA);
+      report(a.status, KVC_ERR_DATA);
       break;
     }
-    long blk = 0, off = 0;
+    long dst;
     if (a.slots) {
       const long slot = a.slots[src_tok];
       if (slot < 0 || slot >= (long)a.N * a.bs) {
-        if (threadIdx.x == 0) report(a.status, KVC_ERR_DATA);
+        if (idx == 0) report(a.status, KVC_ERR_DATA);
         continue;
       }
-      blk = slot / a.bs;
-      off = slot % a.bs;
+      dst = (((slot / a.bs) * a.Hkv + g) * a.bs + slot % a.bs) * a.head_bytes + w * 16;
+    } else {
+      dst = (((long)b * a.Hkv + g) * a.S_max + len + t) * a.head_bytes + w * 16;
     }
-    for (int idx = threadIdx.x; idx < vec_per_tok; idx += kAppendThreads) {
-      const int g = idx / vec_per_head;
-      const int w = idx - g * vec_per_head;
-      const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
-      long dst;
-      if (a.slots) dst = ((blk * a.Hkv + g) * a.bs + off) * a.head_bytes + w * 16;
-      else dst = (((long)b * a.Hkv + g) * a.S_max + len + t) * a.head_bytes + w * 16;
-      *reinterpret_cast<uint4*>(a.k_cache + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
-      *reinterpret_cast<uint4*>(a.v_cache + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
-    }
+    const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+    const uint4 kv = *reinterpret_cast<const uint4*>(a.k_new + src);
+    const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
+    *reinterpret_cast<uint4*>(a.k_cache + dst) = kv;
+    *reinterpret_cast<uint4*>(a.v_cache + dst) = vv;
   }
 }
 
@@ -152,8 +157,12 @@ hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  const int gx = a.max_new > 0 ? (a.max_new + kAppendTokPerWg - 1) / kAppendTokPerWg : 1;
-  hipLaunchKernelGGL(append_kernel, dim3(gx, a.B), dim3(kAppendThreads), 0, s, a);
+  const int vec_per_tok = a.Hkv * (a.head_bytes >> 4);
+  const long n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  const long n_tchunks = a.max_new > 0 ? (a.max_new + kAppendTokPerWg - 1) / kAppendTokPerWg : 1;
+  if (n_vchunks * n_tchunks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)(n_vchunks * n_tchunks), a.B), dim3(kAppendThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 
