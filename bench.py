@@ -77,12 +77,15 @@ def cpu_baseline(w, seconds: float, gpu_out=None):
     lens = synth.final_lengths(w)
     scale = 1.0 / math.sqrt(w.D)
     spent, nbytes, nseq, worst = 0.0, 0, 0, 0.0
+    rows = {}  # generated once per sequence; only the oracle call is timed
     b = 0
-    while spent < seconds and nseq < 4 * w.B:
-        k = np.concatenate([synth.cache_rows(w, "k", b, int(cached[b])),
-                            synth.new_rows(w, "k", b)]).transpose(1, 0, 2).copy()
-        v = np.concatenate([synth.cache_rows(w, "v", b, int(cached[b])),
-                            synth.new_rows(w, "v", b)]).transpose(1, 0, 2).copy()
+    while spent < seconds:
+        if b not in rows:
+            rows[b] = tuple(
+                np.concatenate([synth.cache_rows(w, x, b, int(cached[b])),
+                                synth.new_rows(w, x, b)]).transpose(1, 0, 2).copy()
+                for x in ("k", "v"))
+        k, v = rows[b]
         q = synth.queries(w, b)
         t0 = time.perf_counter()
         want = ref.attention(q, k, v, scale, w.dtype)
