@@ -47,14 +47,14 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
       }
       const int cnt = min(kWave, nparts - q0);
       int j = 0;
-      for (; j + 4 <= cnt; j += 4) {  // four partitions' loads in flight at once
-        float o[4][CPL];
+      for (; j + 8 <= cnt; j += 8) {  // eight partitions' loads in flight at once
+        float o[8][CPL];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
           for (int c = 0; c < CPL; ++c) o[u][c] = po[(long)(q0 + j + u) * D + c];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const float wj = __shfl(wq, j + u);
 #pragma unroll
           for (int c = 0; c < CPL; ++c) acc[c] += wj * o[u][c];

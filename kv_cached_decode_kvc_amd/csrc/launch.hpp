@@ -31,6 +31,7 @@ struct AppendArgs {
   int32_t* seq_lens_out;
   int32_t* status;
   int B, Hkv, head_bytes, bs, S_max, N, max_new, total_new;
+  int tok_per_wg;  // set by the launcher
 };
 
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);

@@ -16,13 +16,19 @@ constexpr int kBtThreads = 1024;
 // the free list front to back; pass 3 maps every new token to its slot.
 __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs a) {
   __shared__ int s_scan[kBtThreads];
+  __shared__ int s_cu[kBtThreads], s_len[kBtThreads];  // batches below kBtThreads
   __shared__ int s_err, s_head, s_total;
   const int tid = threadIdx.x;
   const int bs = a.bs;
+  const bool staged = a.B < kBtThreads;  // B + 1 offsets need B + 1 threads
   if (tid == 0) {
     s_err = 0;
     s_head = *a.head_in;
     s_total = 0;
+  }
+  if (staged) {
+    if (tid < a.B) s_len[tid] = a.seq_lens[tid];
+    if (tid <= a.B) s_cu[tid] = a.cu_new[tid];
   }
   __syncthreads();
   for (int b = tid; b < a.B; b += kBtThreads) {
@@ -75,15 +81,17 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
   }
   __syncthreads();  // table entries written above are read below by other threads
 
+  const int* cu = staged ? s_cu : a.cu_new;  // the search runs in LDS when it fits
+  const int* lens = staged ? s_len : a.seq_lens;
   for (int i = tid; i < a.total_new; i += kBtThreads) {
     int lo = 0, hi = a.B - 1;  // last b with cu_new[b] <= i
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.cu_new[mid] <= i) lo = mid;
+      if (cu[mid] <= i) lo = mid;
       else hi = mid - 1;
     }
-    const long pos = (long)a.seq_lens[lo] + (i - a.cu_new[lo]);
-    if (i >= a.cu_new[lo + 1] || pos / bs >= a.max_blocks) {  // cu_new disagrees with total_new
+    const long pos = (long)lens[lo] + (i - cu[lo]);
+    if (i >= cu[lo + 1] || pos / bs >= a.max_blocks) {  // cu_new disagrees with total_new
       a.slots[i] = -1;
       report(a.status, KVC_ERR_DATA);
       continue;
@@ -95,7 +103,6 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
 }
 
 constexpr int kAppendThreads = 256;
-constexpr int kAppendTokPerWg = 4;
 
 // grid = (vector chunks x token chunks, B): every thread moves one 16-byte
 // piece of one new token's K row and V row (a row of a KV head is head_bytes
@@ -108,6 +115,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
   const int vchunk = blockIdx.x % n_vchunks;
   const int tchunk = blockIdx.x / n_vchunks;
+  const int tok_per_wg = a.tok_per_wg;
   const int len = a.seq_lens[b];
   const int c0 = a.cu_new[b];
   const int n = a.cu_new[b + 1] - c0;
@@ -116,15 +124,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     a.seq_lens_out[b] = bad ? len : len + n;
     if (bad) report(a.status, (len < 0 || n < 0) ? KVC_ERR_DATA : KVC_ERR_CAPACITY);
     // more new tokens than the host's max_new promised: the excess is not written
-    else if (n > (long)(gridDim.x / n_vchunks) * kAppendTokPerWg) report(a.status, KVC_ERR_DATA);
+    else if (n > (long)(gridDim.x / n_vchunks) * tok_per_wg) report(a.status, KVC_ERR_DATA);
   }
   if (bad) return;
   const int idx = vchunk * kAppendThreads + threadIdx.x;
   if (idx >= vec_per_tok) return;
   const int g = idx / vec_per_head;
   const int w = idx - g * vec_per_head;
-  const int t0 = tchunk * kAppendTokPerWg;
-  const int t1 = min(t0 + kAppendTokPerWg, n);
+  const int t0 = tchunk * tok_per_wg;
+  const int t1 = min(t0 + tok_per_wg, n);
   for (int t = t0; t < t1; ++t) {
     const long src_tok = (long)c0 + t;
     if (src_tok >= a.total_new) {  // cu_new points past the new-row buffers
@@ -159,10 +167,13 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const int vec_per_tok = a.Hkv * (a.head_bytes >> 4);
   const long n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
-  const long n_tchunks = a.max_new > 0 ? (a.max_new + kAppendTokPerWg - 1) / kAppendTokPerWg : 1;
+  // decode-sized steps: one token per workgroup; prefills: four per workgroup
+  AppendArgs b = a;
+  b.tok_per_wg = a.max_new <= 64 ? 1 : 4;
+  const long n_tchunks = a.max_new > 0 ? (a.max_new + b.tok_per_wg - 1) / b.tok_per_wg : 1;
   if (n_vchunks * n_tchunks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)(n_vchunks * n_tchunks), a.B), dim3(kAppendThreads),
-                     0, s, a);
+                     0, s, b);
   return hipGetLastError();
 }
 

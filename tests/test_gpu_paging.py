@@ -163,3 +163,21 @@ def test_full_size_tables_bit_exact(ref, name):
     assert st == 0 and st2 == 0
     assert np.array_equal(table.cpu().numpy(), t) and int(head.item()) == h
     assert np.array_equal(slots1.cpu().numpy(), s1) and np.array_equal(slots2.cpu().numpy(), s2)
+
+
+def test_block_table_batch_above_one_workgroup(ref):
+    """More sequences than block-table threads: the scan runs in chunks and the
+    slot search reads global memory; still bit-exact."""
+    w = synth.custom(seed=9, B=1500, Hq=1, Hkv=1, D=64, dtype="bf16", block_size=16, n_q=1,
+                     len_lo=1, len_hi=70)
+    cached = synth.final_lengths(w)
+    gc = GpuCache(w, block_size=16, capacity=int(cached.max()) + 8)
+    gc.prefill(cached)
+    slots = gc.step_rows(0)
+    assert gc.dev_status() == 0
+    st, t, h, s1 = ref.block_table(np.zeros(w.B, np.int32), synth.cu_from_counts(cached),
+                                   np.full((w.B, gc.max_blocks), -1, np.int32), gc.free_host, 0, 16)
+    st2, t, h, s2 = ref.block_table(cached, synth.cu_from_counts([1] * w.B), t, gc.free_host, h, 16)
+    assert st == 0 and st2 == 0
+    assert np.array_equal(gc.table.cpu().numpy(), t) and int(gc.head.item()) == h
+    assert np.array_equal(slots.cpu().numpy(), s2)
