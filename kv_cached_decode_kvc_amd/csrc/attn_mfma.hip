@@ -34,17 +34,15 @@ typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 // MINW: wavefronts per SIMD the register allocation must leave room for.
-template <int D, int NT, int TK, int MINW>
+template <int D, int NT, int MINW>
 __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
-  constexpr int KK = D / 32;         // QK^T steps of 32 along D
-  constexpr int DT = D / 16;         // PV output column tiles
-  constexpr int CH = D / 8;          // 16-byte chunks per key row
-  constexpr int RPL = kWave / CH;    // key rows per wave load
-  constexpr int U = TK / RPL;        // loads per tile, each of K and V
-  constexpr int SB = TK / kTile;     // 16-key sub-tiles per tile
-  constexpr int ROWB = D * 2;        // bytes per key row
-  constexpr int TILEB = TK * ROWB;   // bytes per K (or V) tile
-  static_assert(TK % kTile == 0 && U * RPL == TK, "tile shape");
+  constexpr int KK = D / 32;          // QK^T steps of 32 along D
+  constexpr int DT = D / 16;          // PV output column tiles
+  constexpr int CH = D / 8;           // 16-byte chunks per key row
+  constexpr int RPL = kWave / CH;     // key rows per wave load
+  constexpr int U = kTile / RPL;      // loads per tile, each of K and V
+  constexpr int ROWB = D * 2 + 16;    // LDS row stride: one 16-byte pad per key row
+  constexpr int TILEB = kTile * ROWB;
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][2 * TILEB];
 
   const int lane = threadIdx.x & 63;
@@ -60,24 +58,24 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   const long item = (long)blockIdx.x * 4 + wave;
   const long n_items = (long)p.B * p.Hkv * n_rb * p.max_parts;
   if (item >= n_items) return;
-  // item = ((b * Hkv + g) * n_rb + rb) * max_parts + part
-  const int part = (int)(item % p.max_parts);
+  // item = ((b * Hkv + g) * n_rb + rb) * max_parts + part; all wave-uniform
+  const int part = __builtin_amdgcn_readfirstlane((int)(item % p.max_parts));
   long t = item / p.max_parts;
-  const int rb = (int)(t % n_rb);
+  const int rb = __builtin_amdgcn_readfirstlane((int)(t % n_rb));
   t /= n_rb;
-  const int g = (int)(t % p.Hkv);
-  const int b = (int)(t / p.Hkv);
+  const int g = __builtin_amdgcn_readfirstlane((int)(t % p.Hkv));
+  const int b = __builtin_amdgcn_readfirstlane((int)(t / p.Hkv));
 
-  const int L = p.seq_lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
   if (L < p.n_q || L > p.cap) {
     if (part == 0 && g == 0 && rb == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
     return;
   }
   const int nparts = (L + p.P - 1) / p.P;
   if (part >= nparts) return;
-  const int start = part * TK;       // first tile of this partition
-  const int stride = nparts * TK;    // distance to its next tile
-  const int end = L;                 // the last row sees every key
+  const int start = part * kTile;     // first tile of this partition
+  const int stride = nparts * kTile;  // distance to its next tile
+  const int end = L;                  // the last row sees every key
 
   // this lane's query rows: row i = r * G + hh, query head g * G + hh
   int lvis[NT];
@@ -89,7 +87,7 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
     rvalid[nt] = i < R;
     const int r = rvalid[nt] ? i / p.G : 0;
     const int h = g * p.G + (rvalid[nt] ? i % p.G : 0);
-    lvis[nt] = rvalid[nt] ? L - p.n_q + r + 1 : L;
+    lvis[nt] = rvalid[nt] ? L - p.n_q + r + 1 : L;  // <= end
     qoff[nt] = (((long)b * p.n_q + r) * p.Hq + h) * D;
     wrow[nt] = ((long)b * p.Hq + h) * p.n_q + r;
   }
@@ -107,7 +105,7 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
     }
 
   f32x4_t oacc[NT][DT];
-  float m[NT], l[NT];
+  float m[NT], l[NT];  // m: reference maximum (log2 domain), may trail the true one
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
@@ -116,122 +114,103 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
     for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint16_t* kbase = (const uint16_t*)p.k;
-  const uint16_t* vbase = (const uint16_t*)p.v;
-  const int lr = lane / CH;   // row of a wave load
-  const int pos = lane % CH;  // 16-byte position inside the LDS row
-
-  // Global -> registers for the tile starting at key `tile`; false when the
-  // block table points outside the pool (the tile is then skipped).
+  const int lr = lane / CH;   // key row of a wave load
+  const int pos = lane % CH;  // 16-byte chunk of that row
+  const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  // wave-uniform element offset of key `tile` of (b, g); -1 when the block
+  // table points outside the pool (the tile is then skipped)
+  auto tile_base = [&](int tile) -> long {
+    if (p.table == nullptr) return (((long)b * p.Hkv + g) * p.S_max + tile) * D;
+    const int blk = __builtin_amdgcn_readfirstlane(
+        p.table[(long)b * p.max_blocks + (tile >> bs_shift)]);
+    if (blk < 0 || blk >= p.N) return -1;
+    return (((long)blk * p.Hkv + g) * p.bs + (tile & (p.bs - 1))) * D;
+  };
   uint4 kreg[U], vreg[U];
-  auto load_tile = [&](int tile) -> bool {
-    const int nvalid = min(TK, end - tile);
-    long sbase[SB];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      sbase[sb] = 0;
-      if (sb * kTile >= nvalid) continue;  // never look up blocks past the length
-      const int t0 = tile + sb * kTile;
-      if (p.table == nullptr) {
-        sbase[sb] = (((long)b * p.Hkv + g) * p.S_max + t0) * D;
-      } else {
-        const int blk = p.table[(long)b * p.max_blocks + t0 / p.bs];
-        if (blk < 0 || blk >= p.N) return false;
-        sbase[sb] = (((long)blk * p.Hkv + g) * p.bs + (t0 % p.bs)) * D;
-      }
-    }
+  auto load_tile = [&](int tile, long tb) {
+    const uint16_t* kt = (const uint16_t*)p.k + tb;  // uniform bases, 32-bit lane offsets
+    const uint16_t* vt = (const uint16_t*)p.v + tb;
+    const int last = min(kTile, end - tile) - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = u * RPL + lr;                 // LDS row this lane fills
-      const int src = key < nvalid ? key : nvalid - 1;  // masked keys re-read a visible row
-      const int chunk = pos ^ (key & (CH - 1));     // chunk stored at position pos
-      const long off = sbase[src / kTile] + (long)(src % kTile) * D + chunk * 8;
-      kreg[u] = load_stream(kbase + off);
-      vreg[u] = load_stream(vbase + off);
+      const int key = min(u * RPL + lr, last);  // masked keys re-read a visible row
+      const uint32_t off = (uint32_t)(key * D + pos * 8);
+      kreg[u] = load_stream(kt + off);
+      vreg[u] = load_stream(vt + off);
     }
-    return true;
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = u * RPL + lr;
-      *reinterpret_cast<uint4*>(k_lds + key * ROWB + pos * 16) = kreg[u];
-      *reinterpret_cast<uint4*>(v_lds + key * ROWB + pos * 16) = vreg[u];
+      const int off = (u * RPL + lr) * ROWB + pos * 16;
+      *reinterpret_cast<uint4*>(k_lds + off) = kreg[u];
+      *reinterpret_cast<uint4*>(v_lds + off) = vreg[u];
     }
   };
+  // per-lane LDS operand addresses (loop invariant; the k/dt steps are immediates)
+  const uint8_t* ka_ptr = k_lds + col * ROWB + grp * 16;
+  const uint8_t* va_ptr = v_lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+  constexpr float kLazy = 8.f;  // the reference maximum moves only past m + 8 (p <= 2^8)
 
   if (start < end) {
-    bool ok = load_tile(start);
+    long tb = tile_base(start);
+    if (tb >= 0) load_tile(start, tb);
     store_tile();
     wave_lds_fence();
     for (int tile = start; tile < end; tile += stride) {
       const int next = tile + stride;
-      bool ok_next = true;
-      if (next < end) ok_next = load_tile(next);  // in flight while this tile computes
+      const bool ok = tb >= 0;
+      long tb_next = -1;
+      if (next < end) {
+        tb_next = tile_base(next);
+        if (tb_next >= 0) load_tile(next, tb_next);  // in flight while this tile computes
+      }
       if (ok) {
+        // S^T for 16 keys: lane holds keys tile + grp*4 + v of row col (+16 nt)
+        bf16x8_t ka[KK];
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-          // S^T for keys sb*16 .. +16: lane holds keys grp*4 + v of row col (+16 nt)
-          bf16x8_t ka[KK];
+        for (int kk = 0; kk < KK; ++kk)
+          ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
+        bf16x4_t pb[NT];
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const int key = sb * kTile + col;
-            const int chunk = (kk * 4 + grp) ^ (key & (CH - 1));
-            ka[kk] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + key * ROWB + chunk * 16));
-          }
-          bf16x4_t pb[NT];
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < KK; ++kk)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], s, 0, 0, 0);
+          const int key0 = tile + grp * 4;
+          float sv[4];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-              s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], s, 0, 0, 0);
-            float sv[4];
-            float mx = -INFINITY;
+          for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
+          float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const bool move = mx > m[nt] + kLazy;  // false while the row has no visible key
+          if (__any(move)) {
+            const float m_new = move ? mx : m[nt];
+            const float alpha = m[nt] == -INFINITY ? 0.f : fast_exp2(m[nt] - m_new);
+            l[nt] *= alpha;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int key = tile + sb * kTile + grp * 4 + v;
-              sv[v] = (key < end && key < lvis[nt]) ? s[v] * p.scale_log2 : -INFINITY;
-              mx = fmaxf(mx, sv[v]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m[nt], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no visible key yet
-            const float alpha = fast_exp2(m[nt] - m_use);
-            uint32_t pw[4];
-            float psum = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              pw[v] = f32_to_bf16_bits(fast_exp2(sv[v] - m_use));
-              psum += __uint_as_float(pw[v] << 16);
-            }
-            pb[nt] = __builtin_bit_cast(bf16x4_t,
-                                        make_uint2(pw[0] | (pw[1] << 16), pw[2] | (pw[3] << 16)));
-            l[nt] = l[nt] * alpha + psum;
-            if (alpha != 1.f) {
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha;
-            }
+            for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha;
             m[nt] = m_new;
           }
-          // V^T operand: lane (grp, col = 4s + q) points at V[key sb*16 + 4grp + s][dt*16 + 4q]
+          const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
+          const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+          const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+          const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
+          const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
+          l[nt] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+          pb[nt] = __builtin_bit_cast(bf16x4_t, make_uint2(w01, w23));
+        }
+        // V^T operand: lane (grp, col = 4s + q) points at V[key 4grp + s][dt*16 + 4q]
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int key = sb * kTile + grp * 4 + (col >> 2);
-            const int d0 = dt * 16 + (col & 3) * 4;
-            const int chunk = (d0 >> 3) ^ (key & (CH - 1));
-            lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
-                (__attribute__((address_space(3))) uint8_t*)(v_lds + key * ROWB + chunk * 16 +
-                                                             (d0 & 7) * 2));
-            const bf16x4_t va =
-                __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+        for (int dt = 0; dt < DT; ++dt) {
+          lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+              (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
+          const bf16x4_t va = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              oacc[nt][dt] =
-                  __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[nt], oacc[nt][dt], 0, 0, 0);
-          }
+          for (int nt = 0; nt < NT; ++nt)
+            oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[nt], oacc[nt][dt], 0, 0, 0);
         }
       } else if (lane == 0) {
         report(p.status, KVC_ERR_DATA);
@@ -239,7 +218,7 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
       wave_lds_fence();  // this tile's LDS reads are issued before it is overwritten
       if (next < end) store_tile();
       wave_lds_fence();
-      ok = ok_next;
+      tb = tb_next;
     }
   }
 
@@ -267,14 +246,14 @@ hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, hipStre
   const long n_items = (long)p.B * p.Hkv * n_rb * p.max_parts;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_items + 3) / 4)), block(256);
-  // 16-key tiles; the register budget leaves room for 2 (32-row blocks) or 3
+  // The register budget leaves room for 2 (32-row blocks) or 3
   // (16-row blocks) wavefronts per SIMD, which measured best on MI355X.
   if (rows_per_item == 32) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 2, 16, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_mfma<64, 2, 16, 2>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 2, 2>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_mfma<64, 2, 2>), grid, block, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 1, 16, 3>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_mfma<64, 1, 16, 3>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 1, 3>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_mfma<64, 1, 3>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
