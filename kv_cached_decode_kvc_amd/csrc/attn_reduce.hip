@@ -33,20 +33,36 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     const int nparts = (L + p.P - 1) / p.P;
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
     const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
-    // every lane fetches one partition's (m, l): all of them in one round trip
-    float mstar = -INFINITY;
-    for (int q0 = 0; q0 < nparts; q0 += kWave)
+    // Round trip 1: every lane fetches one partition's (m, l) and, independently,
+    // the first kEarly partitions' outputs for its columns.
+    constexpr int kEarly = 16;
+    float early[kEarly][CPL];
+#pragma unroll
+    for (int j = 0; j < kEarly; ++j)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) early[j][c] = j < nparts ? po[(long)j * D + c] : 0.f;
+    float2 mine = make_float2(-INFINITY, 0.f);
+    if (lane < nparts) mine = ml[lane];
+    float mstar = mine.x;
+    for (int q0 = kWave; q0 < nparts; q0 += kWave)  // more than 64 partitions
       if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[q0 + lane].x);
     for (int m = 1; m < kWave; m <<= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, m));
     for (int q0 = 0; q0 < nparts; q0 += kWave) {
-      float wq = 0.f;
-      if (q0 + lane < nparts) {
-        const float2 mq = ml[q0 + lane];
-        wq = mq.x == -INFINITY ? 0.f : fast_exp2(mq.x - mstar);  // empty partition: 0
-        den += wq * mq.y;
-      }
+      float2 mq = q0 == 0 ? mine : make_float2(-INFINITY, 0.f);
+      if (q0 > 0 && q0 + lane < nparts) mq = ml[q0 + lane];
+      const float wq = mq.x == -INFINITY ? 0.f : fast_exp2(mq.x - mstar);  // empty: 0
+      den += wq * mq.y;
       const int cnt = min(kWave, nparts - q0);
       int j = 0;
+      if (q0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kEarly; ++u) {
+          const float wj = __shfl(wq, u);  // 0 beyond nparts: those lanes hold weight 0
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] += wj * early[u][c];
+        }
+        j = kEarly;
+      }
       for (; j + 8 <= cnt; j += 8) {  // eight partitions' loads in flight at once
         float o[8][CPL];
 #pragma unroll

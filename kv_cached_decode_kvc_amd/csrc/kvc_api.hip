@@ -45,10 +45,11 @@ struct Plan {
 };
 
 // Work is one wavefront per (rows, partition).  The default partition length
-// is the smallest power of two from 256 keys up such that a batch at full
-// capacity gives at most about two rounds of resident wavefronts (5 per SIMD
-// x 4 SIMDs x 256 CUs); short caches halve it, down to 64, while there would
-// be fewer than 4096 wavefronts.
+// is the smallest multiple of 256 keys such that a batch at full capacity
+// gives at most two rounds of resident wavefronts (the kernel's wavefronts
+// per SIMD x 4 SIMDs x 256 CUs; the VALU kernel keeps 5 per SIMD, the MFMA
+// kernel 4 for 16-row blocks and 2 for 32-row blocks); short caches halve it,
+// down to 64, while there would be less than one round.
 Plan make_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -62,10 +63,11 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
-    const long two_rounds = 2L * 5 * 4 * 256;
+    const int waves_per_simd = !pl.mfma ? 5 : (pl.rows_per_item == 16 ? 4 : 2);
+    const long one_round = (long)waves_per_simd * 4 * 256;
     pl.P = 256;
-    while (pl.P < 4096 && units * ((cap + pl.P - 1) / pl.P) > two_rounds) pl.P <<= 1;
-    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 4096) pl.P >>= 1;
+    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 2 * one_round) pl.P += 256;
+    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
   }
   pl.max_parts = (cap + pl.P - 1) / pl.P;
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;

@@ -10,25 +10,49 @@
 namespace kvc {
 
 constexpr int kBtThreads = 1024;
+constexpr int kBtWaves = kBtThreads / kWave;
 
-// One workgroup.  Pass 1 validates and counts the new blocks of every sequence;
-// pass 2 assigns them in batch order with a chunked exclusive scan, consuming
-// the free list front to back; pass 3 maps every new token to its slot.
+// Inclusive prefix sum over a workgroup of kBtThreads (shuffles inside each
+// wave, one LDS exchange across waves); also returns the workgroup total.
+__device__ __forceinline__ int block_inclusive_scan(int x, int* s_wave, int& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kBtWaves; ++w) {
+    const int v = s_wave[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  __syncthreads();  // s_wave may be reused by the next call
+  return x + before;
+}
+
+// One workgroup; thread i owns sequences i, i + kBtThreads, ...  Pass 1
+// validates and counts every sequence's new blocks; pass 2 assigns them in
+// batch order (free list consumed front to back) and maps each new token to
+// its slot, taking the block id straight from the free list or from the
+// sequence's already-held last block, so no pass waits on another's stores.
 __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs a) {
-  __shared__ int s_scan[kBtThreads];
-  __shared__ int s_cu[kBtThreads], s_len[kBtThreads];  // batches below kBtThreads
-  __shared__ int s_err, s_head, s_total;
+  constexpr int kLongSeq = 16;  // sequences with more new tokens go to the token-parallel pass
+  __shared__ int s_wave[kBtWaves];
+  __shared__ int s_err, s_total, s_long;
+  __shared__ int s_cu[kBtThreads], s_first[kBtThreads];  // staged when B < kBtThreads
   const int tid = threadIdx.x;
   const int bs = a.bs;
-  const bool staged = a.B < kBtThreads;  // B + 1 offsets need B + 1 threads
+  const int head = *a.head_in;
   if (tid == 0) {
     s_err = 0;
-    s_head = *a.head_in;
     s_total = 0;
-  }
-  if (staged) {
-    if (tid < a.B) s_len[tid] = a.seq_lens[tid];
-    if (tid <= a.B) s_cu[tid] = a.cu_new[tid];
+    s_long = 0;
   }
   __syncthreads();
   for (int b = tid; b < a.B; b += kBtThreads) {
@@ -44,62 +68,79 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
     else atomicAdd(&s_total, (int)(want - have));
   }
   __syncthreads();
-  if (tid == 0 && s_err == 0 && (s_head < 0 || (long)s_head + s_total > a.N))
-    s_err = KVC_ERR_NO_BLOCKS;
-  __syncthreads();
-  if (s_err != 0) {
+  int err = s_err;
+  if (err == 0 && (head < 0 || (long)head + s_total > a.N)) err = KVC_ERR_NO_BLOCKS;
+  if (err != 0) {
     if (tid == 0) {
-      report(a.status, s_err);
-      *a.head_out = s_head;
+      report(a.status, err);
+      *a.head_out = head;
     }
     return;
   }
 
   int carry = 0;
-  for (int base = 0; base < a.B; base += kBtThreads) {
+  for (int base = 0; base < a.B; base += kBtThreads) {  // uniform trip count
     const int b = base + tid;
-    int have = 0, need = 0;
+    int len = 0, c0 = 0, n = 0, have = 0, need = 0;
     if (b < a.B) {
-      const int len = a.seq_lens[b];
-      const int n = a.cu_new[b + 1] - a.cu_new[b];
+      len = a.seq_lens[b];
+      c0 = a.cu_new[b];
+      n = a.cu_new[b + 1] - c0;
       have = (len + bs - 1) / bs;
       need = (int)(((long)len + n + bs - 1) / bs) - have;
     }
-    s_scan[tid] = need;
-    __syncthreads();
-    for (int off = 1; off < kBtThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int add = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
+    int chunk_total;
+    const int first = head + carry + block_inclusive_scan(need, s_wave, chunk_total) - need;
+    carry += chunk_total;
+    if (b >= a.B) continue;
+    int32_t* row = a.table + (long)b * a.max_blocks;
+    for (int i = 0; i < need; ++i) row[have + i] = a.free_list[first + i];
+    const bool staged = a.B < kBtThreads;
+    if (staged) {
+      s_cu[b] = c0;
+      s_first[b] = first;
+      if (b == a.B - 1) s_cu[a.B] = c0 + n;
     }
-    const int first = s_head + carry + s_scan[tid] - need;
-    for (int i = 0; i < need; ++i)
-      a.table[(long)b * a.max_blocks + have + i] = a.free_list[first + i];
-    carry += s_scan[kBtThreads - 1];
-    __syncthreads();
-  }
-  __syncthreads();  // table entries written above are read below by other threads
-
-  const int* cu = staged ? s_cu : a.cu_new;  // the search runs in LDS when it fits
-  const int* lens = staged ? s_len : a.seq_lens;
-  for (int i = tid; i < a.total_new; i += kBtThreads) {
-    int lo = 0, hi = a.B - 1;  // last b with cu_new[b] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cu[mid] <= i) lo = mid;
-      else hi = mid - 1;
-    }
-    const long pos = (long)lens[lo] + (i - cu[lo]);
-    if (i >= cu[lo + 1] || pos / bs >= a.max_blocks) {  // cu_new disagrees with total_new
-      a.slots[i] = -1;
+    if (n > 0 && c0 + n > a.total_new) {  // cu_new points past the slot buffer
       report(a.status, KVC_ERR_DATA);
       continue;
     }
-    const long blk = a.table[(long)lo * a.max_blocks + pos / bs];
-    a.slots[i] = (int32_t)(blk * bs + pos % bs);
+    if (staged && n > kLongSeq) {  // many new tokens: spread them over the workgroup below
+      s_long = 1;
+      continue;
+    }
+    for (int t = 0; t < n; ++t) {
+      const int pos = len + t;
+      const int lb = pos / bs;
+      const int blk = lb < have ? row[lb] : a.free_list[first + lb - have];
+      a.slots[c0 + t] = blk * bs + pos % bs;
+    }
   }
-  if (tid == 0) *a.head_out = s_head + s_total;
+  __syncthreads();
+  if (a.B < kBtThreads && s_long) {
+    // token-parallel slots of the long sequences (prefill-sized appends); table
+    // entries of this call are not read back: new blocks come from the free list
+    const int total = min(s_cu[a.B], a.total_new);
+    for (int i = tid; i < total; i += kBtThreads) {
+      int lo = 0, hi = a.B - 1;  // last b with cu_new[b] <= i
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cu[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const int c0 = s_cu[lo];
+      const int n = s_cu[lo + 1] - c0;
+      if (n <= kLongSeq || i >= a.total_new) continue;  // short ones are done
+      const int len = a.seq_lens[lo];
+      const int have = (len + bs - 1) / bs;
+      const int pos = len + (i - c0);
+      const int lb = pos / bs;
+      const int blk = lb < have ? a.table[(long)lo * a.max_blocks + lb]
+                                : a.free_list[s_first[lo] + lb - have];
+      a.slots[i] = blk * bs + pos % bs;
+    }
+  }
+  if (tid == 0) *a.head_out = head + s_total;
 }
 
 constexpr int kAppendThreads = 256;
