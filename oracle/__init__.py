@@ -59,7 +59,11 @@ class Oracle:
                                                 ctypes.c_double, P, P]
         lib.kvc_ref_attention_split.argtypes = [I, I, I, I, I, I, P, P, P, ctypes.c_double,
                                                 I, P]
-        for name in ("kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
+        lib.kvc_ref_fork.argtypes = [I, I, I, I, P, P, I, P, P, P]
+        lib.kvc_ref_truncate.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+        lib.kvc_ref_cow.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        for name in ("kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
+                     "kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
                      "kvc_ref_attention", "kvc_ref_cache_attention",
                      "kvc_ref_attention_split"):
             getattr(lib, name).restype = ctypes.c_int
@@ -140,6 +144,54 @@ class Oracle:
         if st != 0:
             raise ValueError("gather failed: %d" % st)
         return out
+
+    # -- block lifecycle (kvc_ref_fork / kvc_ref_truncate / kvc_ref_cow) ------
+    def fork(self, parents, children, seq_lens, table, refs, bs, N):
+        """Returns (status, seq_lens', table', refs'); inputs are not modified."""
+        seq_lens = self._c(seq_lens, np.int32).copy()
+        table = self._c(table, np.int32).copy()
+        refs = self._c(refs, np.int32).copy()
+        parents = np.ascontiguousarray(parents, dtype=np.int32)
+        children = np.ascontiguousarray(children, dtype=np.int32)
+        B, maxb = table.shape
+        st = self.lib.kvc_ref_fork(B, bs, maxb, N, self._p(parents), self._p(children),
+                                   len(parents), self._p(seq_lens), self._p(table), self._p(refs))
+        return st, seq_lens, table, refs
+
+    def truncate(self, seq_lens, new_lens, table, free_list, head, refs, bs):
+        """Returns (status, table', free_list', head', refs', seq_lens_out)."""
+        seq_lens = self._c(seq_lens, np.int32)
+        new_lens = self._c(new_lens, np.int32)
+        table = self._c(table, np.int32).copy()
+        free_list = self._c(free_list, np.int32).copy()
+        refs = None if refs is None else self._c(refs, np.int32).copy()
+        B, maxb = table.shape
+        h = np.array([head], np.int32)
+        out = np.zeros(B, np.int32)
+        st = self.lib.kvc_ref_truncate(B, bs, maxb, len(free_list), self._p(seq_lens),
+                                       self._p(new_lens), self._p(table), self._p(free_list),
+                                       self._p(h), self._p(refs), self._p(out))
+        return st, table, free_list, int(h[0]), refs, out
+
+    def cow(self, seq_lens, cu_new, table, free_list, head, refs, k_pool, v_pool, bs):
+        """In-place on k_pool/v_pool; returns (status, table', free_list', head', refs',
+        cow_src, cow_dst)."""
+        seq_lens = self._c(seq_lens, np.int32)
+        cu_new = self._c(cu_new, np.int32)
+        table = self._c(table, np.int32).copy()
+        free_list = self._c(free_list, np.int32).copy()
+        refs = self._c(refs, np.int32).copy()
+        assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+        B, maxb = table.shape
+        N, Hkv, _, D = k_pool.shape
+        h = np.array([head], np.int32)
+        src = np.full(B, -1, np.int32)
+        dst = np.full(B, -1, np.int32)
+        st = self.lib.kvc_ref_cow(B, bs, maxb, N, Hkv, D, k_pool.dtype.itemsize, self._p(seq_lens),
+                                  self._p(cu_new), self._p(table), self._p(free_list), self._p(h),
+                                  self._p(refs), self._p(k_pool), self._p(v_pool), self._p(src),
+                                  self._p(dst))
+        return st, table, free_list, int(h[0]), refs, src, dst
 
     # -- kvc_ref_attention --------------------------------------------------
     def attention(self, q, k, v, scale, dtype):

@@ -404,3 +404,150 @@ int kvc_ref_attention_split(int n_q, int Hq, int Hkv, int D, int L, int dtype, c
   free(cO);
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Block lifecycle: sharing, copy-on-write, rollback.
+ *
+ * [VN] 05 "Chia se block va copy-on-write": every physical block carries a
+ * reference count; parallel samples share the prompt's blocks and a sample
+ * that must write into a shared block first copies it.  [I1] "PagedAttention":
+ * blocks shared by several sequences are copied only when one of them writes.
+ * [EI] paged-attention passage: a finished request's blocks return to the free
+ * pool.  [I2] "Draft-model speculative decoding": after verification the
+ * target's cache is truncated to the accepted tokens.
+ *
+ * Readings (the pages fix none of these details):
+ *   - refs[blk] counts the owners beyond the first: a block held by one
+ *     sequence, or free, has 0;
+ *   - the free pool is the tail free_list[head .. N) of the allocation list;
+ *     freed blocks are pushed back just below head, in increasing block id;
+ *   - copy-on-write is decided on the state at the start of the call: every
+ *     sequence about to append into a partly filled last block that is
+ *     shared takes a fresh block (batch order, from the free list front),
+ *     gets a copy of the whole block (all heads, K and V) and drops one
+ *     reference; an original left with no owner is freed.
+ */
+
+static int cmp_i32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Push the blocks in `cand` whose refs fell below zero (or every candidate
+ * when refs == NULL) back onto the free list, once each, in increasing id. */
+static int push_freed(int32_t* cand, long nc, int32_t* free_list, int32_t* head, int32_t* refs) {
+  qsort(cand, (size_t)nc, sizeof(int32_t), cmp_i32);
+  long nf = 0;
+  for (long i = 0; i < nc; ++i) {
+    if (i > 0 && cand[i] == cand[i - 1]) continue;
+    if (refs && refs[cand[i]] >= 0) continue;
+    cand[nf++] = cand[i];
+  }
+  if (*head - nf < 0) return REF_ERR_DATA;
+  *head -= (int32_t)nf;
+  for (long i = 0; i < nf; ++i) {
+    free_list[*head + i] = cand[i];
+    if (refs) refs[cand[i]] = 0;
+  }
+  return REF_OK;
+}
+
+/* Fork: child i takes parent i's blocks (table row and length) and each of
+ * those blocks gains one reference.  Children must be empty.  All or nothing. */
+int kvc_ref_fork(int B, int bs, int max_blocks, int N, const int32_t* parents,
+                 const int32_t* children, int n, int32_t* seq_lens, int32_t* table, int32_t* refs) {
+  for (int i = 0; i < n; ++i) {
+    int p = parents[i], c = children[i];
+    if (p < 0 || p >= B || c < 0 || c >= B || p == c) return REF_ERR_DATA;
+    if (seq_lens[c] != 0 || seq_lens[p] < 0 || seq_lens[p] > (long)max_blocks * bs) return REF_ERR_DATA;
+  }
+  for (int i = 0; i < n; ++i) {
+    int p = parents[i], c = children[i];
+    long nb = ((long)seq_lens[p] + bs - 1) / bs;
+    for (long j = 0; j < nb; ++j) {
+      int32_t blk = table[(long)p * max_blocks + j];
+      table[(long)c * max_blocks + j] = blk;
+      if (blk >= 0 && blk < N) refs[blk] += 1;
+    }
+    seq_lens[c] = seq_lens[p];
+  }
+  return REF_OK;
+}
+
+/* Truncate: sequence b keeps new_lens[b] <= seq_lens[b] tokens; its logical
+ * blocks from ceil(new_len/bs) on are released (table entry -1).  A released
+ * block with extra references loses one; otherwise it is freed.  All or
+ * nothing on a bad length. */
+int kvc_ref_truncate(int B, int bs, int max_blocks, int N, const int32_t* seq_lens,
+                     const int32_t* new_lens, int32_t* table, int32_t* free_list, int32_t* head,
+                     int32_t* refs, int32_t* seq_lens_out) {
+  long total = 0;
+  for (int b = 0; b < B; ++b) {
+    if (new_lens[b] < 0 || new_lens[b] > seq_lens[b]) return REF_ERR_DATA;
+    total += ((long)seq_lens[b] + bs - 1) / bs - ((long)new_lens[b] + bs - 1) / bs;
+  }
+  int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));
+  if (!cand) return REF_ERR_ARG;
+  long nc = 0;
+  for (int b = 0; b < B; ++b) {
+    long old_nb = ((long)seq_lens[b] + bs - 1) / bs;
+    long new_nb = ((long)new_lens[b] + bs - 1) / bs;
+    for (long j = old_nb - 1; j >= new_nb; --j) {
+      int32_t blk = table[(long)b * max_blocks + j];
+      table[(long)b * max_blocks + j] = -1;
+      if (blk < 0 || blk >= N) continue;
+      if (refs) refs[blk] -= 1;
+      cand[nc++] = blk;
+    }
+    seq_lens_out[b] = new_lens[b];
+  }
+  int st = push_freed(cand, nc, free_list, head, refs);
+  free(cand);
+  return st;
+}
+
+/* Copy-on-write before an append (see the readings above).  cow_src/cow_dst
+ * receive the copied pair of every sequence (-1 when none).  The block data
+ * (Hkv * bs * D elements of esize bytes, K and V) is copied in the pools.
+ * All or nothing when the free list cannot cover the copies. */
+int kvc_ref_cow(int B, int bs, int max_blocks, int N, int Hkv, int D, int esize,
+                const int32_t* seq_lens, const int32_t* cu_new, int32_t* table,
+                int32_t* free_list, int32_t* head, int32_t* refs, void* k_pool, void* v_pool,
+                int32_t* cow_src, int32_t* cow_dst) {
+  long need = 0;
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b], n = (long)cu_new[b + 1] - cu_new[b];
+    cow_src[b] = cow_dst[b] = -1;
+    if (n <= 0 || len % bs == 0) continue;
+    int32_t blk = table[(long)b * max_blocks + len / bs];
+    if (blk >= 0 && blk < N && refs[blk] > 0) need += 1;
+  }
+  if (*head + need > N) return REF_ERR_NO_BLOCKS;
+  /* decide every copy on the state at the start of the call */
+  int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)(need > 0 ? need : 1));
+  if (!cand) return REF_ERR_ARG;
+  long nc = 0;
+  for (int b = 0; b < B; ++b) {
+    long len = seq_lens[b], n = (long)cu_new[b + 1] - cu_new[b];
+    if (n <= 0 || len % bs == 0) continue;
+    int32_t blk = table[(long)b * max_blocks + len / bs];
+    if (blk >= 0 && blk < N && refs[blk] > 0) {
+      cow_src[b] = blk;
+      cow_dst[b] = free_list[*head];
+      *head += 1;
+      cand[nc++] = blk;
+    }
+  }
+  size_t bytes = (size_t)Hkv * bs * D * esize;
+  for (int b = 0; b < B; ++b) {
+    if (cow_src[b] < 0) continue;
+    long len = seq_lens[b];
+    memcpy((char*)k_pool + (size_t)cow_dst[b] * bytes, (const char*)k_pool + (size_t)cow_src[b] * bytes, bytes);
+    memcpy((char*)v_pool + (size_t)cow_dst[b] * bytes, (const char*)v_pool + (size_t)cow_src[b] * bytes, bytes);
+    table[(long)b * max_blocks + len / bs] = cow_dst[b];
+    refs[cow_src[b]] -= 1;
+  }
+  int st = push_freed(cand, nc, free_list, head, refs);
+  free(cand);
+  return st;
+}

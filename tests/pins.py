@@ -520,6 +520,119 @@ def pin_cached_decode_equals_recompute(o):
 
 
 # ---------------------------------------------------------------------------
+# block lifecycle: sharing, copy-on-write, rollback
+# ---------------------------------------------------------------------------
+def _lifecycle_state_ok(table, seq_lens, free_list, head, refs, bs, N):
+    """Ownership invariants: every block is free xor owned; refs = owners - 1
+    (0 when free); the free region holds distinct blocks."""
+    owners = {}
+    for b in range(table.shape[0]):
+        nb = -(-int(seq_lens[b]) // bs)
+        for j in range(nb):
+            owners.setdefault(int(table[b, j]), []).append(b)
+        assert np.all(table[b, nb:] == -1), "entries past the length must be -1"
+    free = [int(x) for x in free_list[head:]]
+    assert len(set(free)) == len(free)
+    assert not (set(free) & set(owners)), "a block is both free and owned"
+    assert set(free) | set(owners) == set(range(N)), "a block was lost"
+    for blk in range(N):
+        want = len(owners[blk]) - 1 if blk in owners else 0
+        assert refs[blk] == want, (blk, refs[blk], want)
+
+
+def pin_lifecycle_random_ops(o):
+    """Random appends, forks (parallel sampling), copy-on-write and truncations
+    (speculative rollback) on a tiny pool, against a brute-force model: each
+    sequence's logical rows are tracked as plain Python lists, and block
+    ownership is recomputed from the tables after every operation."""
+    rng = np.random.default_rng(25)
+    bs, N, B, maxb, D = 4, 48, 5, 8, 2
+    for trial in range(40):
+        table = np.full((B, maxb), -1, np.int32)
+        free_list = rng.permutation(N).astype(np.int32)
+        head = 0
+        refs = np.zeros(N, np.int32)
+        lens = np.zeros(B, np.int32)
+        pool = np.zeros((N, 1, bs, D), np.float32)
+        vpool = np.zeros_like(pool)
+        model = [[] for _ in range(B)]  # logical rows of every sequence
+        stamp = [0]
+
+        def rows(n):
+            out = []
+            for _ in range(n):
+                stamp[0] += 1
+                out.append(float(stamp[0]))
+            return out
+
+        for step in range(25):
+            op = rng.integers(0, 4)
+            if op == 0 or step < 2:  # copy-on-write, then allocate, then append
+                counts = [int(rng.integers(0, 4)) if len(model[b]) + 4 <= maxb * bs else 0
+                          for b in range(B)]
+                cu = synth.cu_from_counts(counts)
+                st, table, free_list, head, refs, src, dst = o.cow(lens, cu, table, free_list,
+                                                                    head, refs, pool, vpool, bs)
+                if st != 0:
+                    continue
+                st, table, head, slots = o.block_table(lens, cu, table, free_list, head, bs)
+                if st != 0:
+                    continue
+                new = [rows(c) for c in counts]
+                kr = np.array([[[x, -x]] for seq in new for x in seq], np.float32).reshape(-1, 1, D)
+                st, lens = o.append(kr, kr, lens, cu, pool, vpool, bs=bs, slots=slots)
+                assert st == 0
+                for b in range(B):
+                    model[b] += new[b]
+            elif op == 1:  # fork an occupied sequence into an empty one
+                empty = [b for b in range(B) if lens[b] == 0]
+                full = [b for b in range(B) if lens[b] > 0]
+                if not empty or not full:
+                    continue
+                p_, c_ = int(rng.choice(full)), int(rng.choice(empty))
+                st, lens, table, refs = o.fork([p_], [c_], lens, table, refs, bs, N)
+                assert st == 0
+                model[c_] = list(model[p_])
+            else:  # truncate some sequences (accepted drafts), sometimes to zero
+                new_lens = np.array([int(rng.integers(0, lens[b] + 1)) if rng.random() < 0.6
+                                     else int(lens[b]) for b in range(B)], np.int32)
+                st, table, free_list, head, refs, lens = o.truncate(lens, new_lens, table,
+                                                                    free_list, head, refs, bs)
+                assert st == 0
+                for b in range(B):
+                    model[b] = model[b][:new_lens[b]]
+            _lifecycle_state_ok(table, lens, free_list, head, refs, bs, N)
+            for b in range(B):
+                assert lens[b] == len(model[b])
+                if lens[b]:
+                    got = o.gather(pool, b, int(lens[b]), bs=bs, table=table)[0, :, 0]
+                    assert list(got) == model[b], (trial, step, b)
+
+
+def pin_lifecycle_errors(o):
+    """Bad lengths are refused with nothing changed; a fork into a non-empty
+    sequence is refused; copy-on-write needs free blocks for every copy."""
+    bs, N = 4, 6
+    table = np.full((2, 4), -1, np.int32)
+    table[0, :2] = [3, 1]
+    lens = np.array([6, 0], np.int32)
+    free_list = np.array([3, 1, 0, 2, 4, 5], np.int32)
+    refs = np.zeros(N, np.int32)
+    st, t, f, h, r, out = o.truncate(lens, np.array([7, 0], np.int32), table, free_list, 2, refs, bs)
+    assert st == -8 and np.array_equal(t, table) and h == 2
+    st, l2, t2, r2 = o.fork([0], [0], lens, table, refs, bs, N)
+    assert st == -8
+    st, l2, t2, r2 = o.fork([0, 1], [1, 0], lens, table, refs, bs, N)  # child 0 is not empty
+    assert st == -8 and np.array_equal(t2, table)
+    st, l2, t2, r2 = o.fork([0], [1], lens, table, refs, bs, N)
+    assert st == 0 and list(t2[1, :2]) == [3, 1] and r2[3] == 1 and r2[1] == 1
+    pool = np.zeros((N, 1, bs, 1), np.float32)
+    st, t3, f3, h3, r3, src, dst = o.cow(l2, np.array([0, 1, 2], np.int32), t2, free_list, 6, r2,
+                                         pool, pool.copy(), bs)
+    assert st == -6 and h3 == 6  # both need a copy of block 1, the pool is empty
+
+
+# ---------------------------------------------------------------------------
 # byte accounting and output rounding
 # ---------------------------------------------------------------------------
 def _rows(name):

@@ -24,6 +24,14 @@ MUTANTS = {
     "slot_offset_shifted": ("(int32_t)(blk * bs + pos % bs);", "(int32_t)(blk * bs + (pos + 1) % bs);"),
     "bf16_ties_away": ("nearbyint(ax / ulp)", "round(ax / ulp)"),
     "combine_unweighted_sum": ("den += exp(cm[c] - M) * cl[c];", "den += cl[c];"),
+    "fork_without_reference": ("if (blk >= 0 && blk < N) refs[blk] += 1;",
+                               "if (blk >= 0 && blk < N) refs[blk] += 0;"),
+    "truncate_keeps_entries": ("      table[(long)b * max_blocks + j] = -1;\n      if (blk < 0 || blk >= N) continue;",
+                               "      if (blk < 0 || blk >= N) continue;"),
+    "cow_keeps_reference": ("refs[cow_src[b]] -= 1;", "refs[cow_src[b]] -= 0;"),
+    "cow_writes_shared_block": ("table[(long)b * max_blocks + len / bs] = cow_dst[b];",
+                                "table[(long)b * max_blocks + len / bs] = cow_src[b];"),
+    "freed_twice": ("if (i > 0 && cand[i] == cand[i - 1]) continue;", "if (0) continue;"),
     "paged_row_shifted": ("return ((blk * Hkv + g) * bs + j % bs) * D;",
                           "return ((blk * Hkv + g) * bs + (j + 1) % bs) * D;"),
 }
