@@ -453,7 +453,9 @@ static int push_freed(int32_t* cand, long nc, int32_t* free_list, int32_t* head,
 }
 
 /* Fork: child i takes parent i's blocks (table row and length) and each of
- * those blocks gains one reference.  Children must be empty.  All or nothing. */
+ * those blocks gains one reference.  Children must be empty and distinct, and
+ * no sequence may be both a parent and a child in one call (the forks of a
+ * call are independent of each other).  All or nothing. */
 int kvc_ref_fork(int B, int bs, int max_blocks, int N, const int32_t* parents,
                  const int32_t* children, int n, int32_t* seq_lens, int32_t* table, int32_t* refs) {
   for (int i = 0; i < n; ++i) {
@@ -461,6 +463,11 @@ int kvc_ref_fork(int B, int bs, int max_blocks, int N, const int32_t* parents,
     if (p < 0 || p >= B || c < 0 || c >= B || p == c) return REF_ERR_DATA;
     if (seq_lens[c] != 0 || seq_lens[p] < 0 || seq_lens[p] > (long)max_blocks * bs) return REF_ERR_DATA;
   }
+  for (int i = 0; i < n; ++i)
+    for (int k = 0; k < n; ++k) {
+      if (k != i && children[k] == children[i]) return REF_ERR_DATA;
+      if (parents[k] == children[i]) return REF_ERR_DATA;
+    }
   for (int i = 0; i < n; ++i) {
     int p = parents[i], c = children[i];
     long nb = ((long)seq_lens[p] + bs - 1) / bs;

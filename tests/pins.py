@@ -624,6 +624,12 @@ def pin_lifecycle_errors(o):
     assert st == -8
     st, l2, t2, r2 = o.fork([0, 1], [1, 0], lens, table, refs, bs, N)  # child 0 is not empty
     assert st == -8 and np.array_equal(t2, table)
+    lens3 = np.array([6, 0, 0], np.int32)
+    table3 = np.vstack([table, np.full((1, 4), -1, np.int32)])
+    st, *_ = o.fork([0, 0], [1, 1], lens3, table3, refs, bs, N)  # the same child twice
+    assert st == -8
+    st, *_ = o.fork([0, 1], [1, 2], lens3, table3, refs, bs, N)  # 1 is parent and child
+    assert st == -8
     st, l2, t2, r2 = o.fork([0], [1], lens, table, refs, bs, N)
     assert st == 0 and list(t2[1, :2]) == [3, 1] and r2[3] == 1 and r2[1] == 1
     pool = np.zeros((N, 1, bs, 1), np.float32)
