@@ -11,9 +11,8 @@
 // Per tile of TK keys:
 //   1. K and V rows arrive with coalesced non-temporal 16-byte loads (one
 //      instruction = RPL whole rows, contiguous) one tile ahead, and are
-//      written to a wave-private LDS tile whose 16-byte chunks are XOR-
-//      swizzled by key so that both the writes and the operand reads below
-//      hit distinct banks;
+//      written to a wave-private LDS tile whose rows are padded by 16 bytes so
+//      that both the writes and the operand reads below spread over the banks;
 //   2. S^T[key][row] = K . Q^T on v_mfma_f32_16x16x32_bf16 (K operands read
 //      with ds_read_b128, Q^T held in registers for the whole partition);
 //   3. online softmax per row -- running max m and sum l ("Inference-1",
@@ -21,11 +20,15 @@
 //      with verify row r limited to keys 0 .. L - n_q + r ("Inference-1",
 //      "KV cache"); the MFMA result layout puts one row in each lane's
 //      registers, so only the maximum over the four key groups needs shuffles;
-//   4. O^T[d][row] += V^T . P^T on v_mfma_f32_16x16x16_bf16; the V^T operand
+//   4. O^T[d][row] += V^T . P^T on v_mfma_f32_16x16x32_bf16; the V^T operand
 //      comes straight from the row-major LDS tile through ds_read_b64_tr_b16,
 //      whose 16-lane transpose delivers four consecutive keys of one column.
-// P is rounded to bf16 for the second product and l sums the same rounded
-// weights, so each partition's result is a convex combination of value rows.
+// The weights enter the second product as two bf16 halves, hi = bf16(p) and
+// lo = bf16(p - hi), side by side along the reduction index against two
+// copies of the V^T fragment: p keeps about 16 significant bits (a plain bf16
+// p would perturb each weight by up to 2^-9, which on a few dominant keys with
+// large values exceeds the output tolerance), at the same instruction count
+// as a single 16x16x16 product.  l sums the fp32 weights.
 #include "launch.hpp"
 
 namespace kvc {
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
-        bf16x4_t pb[NT];
+        bf16x8_t pb[NT];  // keys grp*4 + 0..3: hi halves, then lo halves
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -197,10 +200,16 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
           const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
           const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
           const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
-          const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
-          const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
-          l[nt] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
-          pb[nt] = __builtin_bit_cast(bf16x4_t, make_uint2(w01, w23));
+          const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+          const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+          const f32x2_t r01 = p01 - __builtin_convertvector(h01, f32x2_t);  // exact
+          const f32x2_t r23 = p23 - __builtin_convertvector(h23, f32x2_t);
+          const bf16x2_t lo01 = __builtin_convertvector(r01, bf16x2_t);
+          const bf16x2_t lo23 = __builtin_convertvector(r23, bf16x2_t);
+          l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+          pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                           __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
         }
         // V^T operand: lane (grp, col = 4s + q) points at V[key 4grp + s][dt*16 + 4q]
 #pragma unroll
@@ -208,9 +217,10 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
           lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
               (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
           const bf16x4_t va = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+          const bf16x8_t va2 = __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[nt], oacc[nt][dt], 0, 0, 0);
+            oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[nt], oacc[nt][dt], 0, 0, 0);
         }
       } else if (lane == 0) {
         report(p.status, KVC_ERR_DATA);

@@ -235,3 +235,32 @@ def test_workspace_too_small_is_refused():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_decode_attn(gc.desc, q, gc.k, gc.v, gc.seq_lens, None, 0.1, out, small)
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("n_q", [1, 5])
+def test_peaked_weights_large_values(ref, n_q):
+    """Matrix-core path on short contexts where a few keys take nearly all the
+    weight and value rows are large (|v| up to ~16): the error the weights
+    carry into the value product shows up undamped here, so this case bounds
+    the precision of the probabilities in that product."""
+    D, Hq, Hkv, B = 128, 8, 2, 24
+    w = synth.custom(name="peaked", seed=31 + n_q, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                     block_size=0, n_q=n_q, len_lo=n_q, len_hi=40)
+    lengths = synth.final_lengths(w)
+    rng = np.random.default_rng(4242 + n_q)
+    total = int(lengths.sum())
+    k = synth.to_bf16_bits(rng.standard_normal((total, Hkv, D), dtype=np.float32))
+    v = synth.to_bf16_bits(4.0 * rng.standard_normal((total, Hkv, D), dtype=np.float32))
+    q = synth.to_bf16_bits(rng.standard_normal((B, n_q, Hq, D), dtype=np.float32))
+    scale = 3.0 / math.sqrt(D)  # scores spread ~3x wider than 1/sqrt(D) gives
+    gc = GpuCache(w, capacity=48)
+    gc.add_tokens(k, v, lengths)
+    got = gc.attend(to_dev(q, "bf16"), n_q, scale=scale).cpu().numpy()
+    assert gc.dev_status() == 0
+    kc = np.zeros((B, Hkv, 48, D), np.uint16)
+    vc = np.zeros_like(kc)
+    st, lens = ref.append(k, v, np.zeros(B, np.int32), synth.cu_from_counts(lengths), kc, vc)
+    assert st == 0
+    st, want = ref.cache_attention(q, kc, vc, lens, scale, "bf16")
+    assert st == 0
+    assert_close(got, want, "peaked n_q=%d" % n_q)
