@@ -202,6 +202,90 @@ size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
 
 /* Static text for a kvc_status value. */
+/*
+ * Block lifecycle (paged caches only): sharing, copy-on-write and rollback.
+ *
+ * [VN] 05 "Chia se block va copy-on-write": physical blocks carry reference
+ * counts; parallel samples share the prompt's blocks and a sample copies a
+ * shared block before writing into it.  [I1] "PagedAttention": shared blocks
+ * are copied only when written.  [EI] paged-attention passage: a finished
+ * request's blocks go back to the free pool.  [I2] "Draft-model speculative
+ * decoding": after verification the cache is cut back to the accepted tokens.
+ *
+ *   ref_counts (device) [num_blocks] owners beyond the first: 0 for a block
+ *              held by one sequence or free.  The caller zeroes it once.
+ *   free pool  free_list[*free_head .. num_blocks): blocks are taken from the
+ *              front (kvc_block_table, kvc_cow) and freed blocks are pushed
+ *              back just below the head, in increasing block id, so results do
+ *              not depend on thread order.
+ * Each call runs one workgroup (microseconds) and is all or nothing on bad
+ * device data (dev_status receives KVC_ERR_DATA or KVC_ERR_NO_BLOCKS and only
+ * free_head_out = free_head_in is written).  num_blocks <= 262144 for
+ * kvc_truncate and kvc_cow (KVC_ERR_UNSUPPORTED otherwise).
+ */
+
+/*
+ * kvc_fork -- child i starts as a copy of parent i: it takes the parent's
+ * length and table row (its first ceil(len/block_size) entries) and every
+ * block gained gets one more reference.  No block data moves.
+ *
+ *   parents, children (device) [n_forks] sequence indices; children distinct,
+ *                     empty (seq_lens 0), and no sequence is both a parent and
+ *                     a child in one call
+ *   seq_lens          (device) [B] in/out: children's entries are set
+ *   block_table       (device) in/out: children's rows are set
+ *   ref_counts        (device) in/out
+ */
+int kvc_fork(const kvc_cache_desc* d, const int32_t* parents, const int32_t* children,
+             int32_t n_forks, int32_t* seq_lens, int32_t* block_table, int32_t* ref_counts,
+             int32_t* dev_status, void* stream);
+
+/*
+ * kvc_truncate -- sequence b keeps its first new_lens[b] tokens (0 releases the
+ * whole sequence).  Its logical blocks from ceil(new_len/block_size) on become
+ * -1; each such block loses one reference, or, having none beyond its owner,
+ * is freed.  The kept tokens are not touched.
+ *
+ *   seq_lens       (device) [B] lengths now; new_lens (device) [B], 0 <= new <= len
+ *   block_table    (device) in/out
+ *   free_list      (device) in/out; free_head_in / free_head_out as for
+ *                  kvc_block_table (free_head_out = free_head_in - blocks freed)
+ *   ref_counts     (device) in/out, or NULL when no block is shared (every
+ *                  released block is then freed)
+ *   seq_lens_out   (device) [B] receives new_lens; may alias seq_lens
+ */
+int kvc_truncate(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* new_lens,
+                 int32_t* block_table, int32_t* free_list, const int32_t* free_head_in,
+                 int32_t* free_head_out, int32_t* ref_counts, int32_t* seq_lens_out,
+                 int32_t* dev_status, void* stream);
+
+/*
+ * kvc_cow -- copy-on-write before an append; call it before kvc_block_table
+ * with the same seq_lens and cu_new.  Decided on the state at the start of
+ * the call: every sequence with new tokens whose last block is partly filled
+ * and has extra references takes a fresh block from the free-list front
+ * (batch order), gets a copy of the whole block (all KV heads, K and V), points
+ * its table entry at it and drops one reference on the original; an original
+ * left with no owner is freed.
+ *
+ *   cow_src, cow_dst (device) [B] out: the copied pair of sequence b, -1 when none
+ *   free_head_out    = free_head_in + copies - originals freed
+ * The copies run as a second kernel (kvc_copy_blocks) on the same stream.
+ */
+int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_new,
+            int32_t* block_table, int32_t* free_list, const int32_t* free_head_in,
+            int32_t* free_head_out, int32_t* ref_counts, void* k_cache, void* v_cache,
+            int32_t* cow_src, int32_t* cow_dst, int32_t* dev_status, void* stream);
+
+/*
+ * kvc_copy_blocks -- for i < n with src[i] >= 0, copy pool block src[i] onto
+ * dst[i] (all KV heads, K and V, bit for bit).  Pairs must not overlap (no
+ * block both a source and a destination).  A block id >= num_blocks is
+ * KVC_ERR_DATA and that pair is skipped.
+ */
+int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* dst, int32_t n,
+                    void* k_cache, void* v_cache, int32_t* dev_status, void* stream);
+
 const char* kvc_status_string(int32_t status);
 
 #ifdef __cplusplus

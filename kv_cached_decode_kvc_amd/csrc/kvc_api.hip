@@ -12,7 +12,7 @@ using namespace kvc;
 int check_desc(const kvc_cache_desc* d) {
   if (!d) return KVC_ERR_ARG;
   if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVC_ERR_SHAPE;
-  if (d->batch > 65535) return KVC_ERR_UNSUPPORTED;  // one grid row per sequence
+  if (d->batch >= kMaxBatch) return KVC_ERR_UNSUPPORTED;  // one grid row per sequence
   if (d->num_q_heads % d->num_kv_heads != 0) return KVC_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return KVC_ERR_UNSUPPORTED;
   if (d->dtype != KVC_BF16 && d->dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
@@ -257,6 +257,111 @@ int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
   return kvc_verify_attn(d, q, 1, k_cache, v_cache, seq_lens, block_table, scale, out, out_dtype,
                          workspace, workspace_bytes, dev_status, stream);
+}
+
+int kvc_fork(const kvc_cache_desc* d, const int32_t* parents, const int32_t* children,
+             int32_t n_forks, int32_t* seq_lens, int32_t* block_table, int32_t* ref_counts,
+             int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;
+  if (n_forks < 0) return KVC_ERR_ARG;
+  if (n_forks == 0 || d->batch == 0) return KVC_OK;
+  if (!parents || !children || !seq_lens || !block_table || !ref_counts) return KVC_ERR_ARG;
+  LifecycleArgs a{};
+  a.seq_lens = seq_lens;
+  a.seq_lens_out = seq_lens;
+  a.parents = parents;
+  a.children = children;
+  a.table = block_table;
+  a.refs = ref_counts;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.bs = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.N = d->num_blocks;
+  a.n = n_forks;
+  return hip_status(launch_fork(a, (hipStream_t)stream));
+}
+
+int kvc_truncate(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* new_lens,
+                 int32_t* block_table, int32_t* free_list, const int32_t* free_head_in,
+                 int32_t* free_head_out, int32_t* ref_counts, int32_t* seq_lens_out,
+                 int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;
+  if (d->num_blocks > kMaxPoolBlocks) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!seq_lens || !new_lens || !block_table || !free_list || !free_head_in || !free_head_out ||
+      !seq_lens_out)
+    return KVC_ERR_ARG;
+  LifecycleArgs a{};
+  a.seq_lens = seq_lens;
+  a.new_lens = new_lens;
+  a.table = block_table;
+  a.free_list = free_list;
+  a.head_in = free_head_in;
+  a.head_out = free_head_out;
+  a.refs = ref_counts;
+  a.seq_lens_out = seq_lens_out;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.bs = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.N = d->num_blocks;
+  return hip_status(launch_truncate(a, (hipStream_t)stream));
+}
+
+int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* dst, int32_t n,
+                    void* k_cache, void* v_cache, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;
+  if (n < 0 || n >= kMaxBatch) return KVC_ERR_ARG;
+  if (n == 0) return KVC_OK;
+  if (!src || !dst || !k_cache || !v_cache) return KVC_ERR_ARG;
+  CopyArgs c{};
+  c.src = src;
+  c.dst = dst;
+  c.k = (uint8_t*)k_cache;
+  c.v = (uint8_t*)v_cache;
+  c.block_bytes = (long)d->num_kv_heads * d->block_size * d->head_dim * (long)elem_bytes(d);
+  c.N = d->num_blocks;
+  c.status = dev_status;
+  return hip_status(launch_copy_blocks(c, n, (hipStream_t)stream));
+}
+
+int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_new,
+            int32_t* block_table, int32_t* free_list, const int32_t* free_head_in,
+            int32_t* free_head_out, int32_t* ref_counts, void* k_cache, void* v_cache,
+            int32_t* cow_src, int32_t* cow_dst, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;
+  if (d->num_blocks > kMaxPoolBlocks) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!seq_lens || !cu_new || !block_table || !free_list || !free_head_in || !free_head_out ||
+      !ref_counts || !k_cache || !v_cache || !cow_src || !cow_dst)
+    return KVC_ERR_ARG;
+  LifecycleArgs a{};
+  a.seq_lens = seq_lens;
+  a.cu_new = cu_new;
+  a.table = block_table;
+  a.free_list = free_list;
+  a.head_in = free_head_in;
+  a.head_out = free_head_out;
+  a.refs = ref_counts;
+  a.cow_src = cow_src;
+  a.cow_dst = cow_dst;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.bs = d->block_size;
+  a.max_blocks = d->max_blocks_per_seq;
+  a.N = d->num_blocks;
+  hipError_t e = launch_cow(a, (hipStream_t)stream);
+  if (e != hipSuccess) return KVC_ERR_HIP;
+  return kvc_copy_blocks(d, cow_src, cow_dst, d->batch, k_cache, v_cache, dev_status, stream);
 }
 
 size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q) {

@@ -34,6 +34,41 @@ struct AppendArgs {
   int tok_per_wg;  // set by the launcher
 };
 
+constexpr int kMaxBatch = 65536;        // sequences per call (one grid row each)
+constexpr int kMaxPoolBlocks = 262144;  // pool size the lifecycle kernels can track in LDS
+
+struct LifecycleArgs {
+  const int32_t* seq_lens;
+  const int32_t* new_lens;  // truncate
+  const int32_t* cu_new;    // copy-on-write
+  const int32_t* parents;   // fork
+  const int32_t* children;
+  int32_t* table;
+  int32_t* free_list;
+  const int32_t* head_in;
+  int32_t* head_out;
+  int32_t* refs;            // may be NULL for truncate
+  int32_t* seq_lens_out;
+  int32_t* cow_src;
+  int32_t* cow_dst;
+  int32_t* status;
+  int B, bs, max_blocks, N, n;
+};
+
+struct CopyArgs {
+  const int32_t* src;
+  const int32_t* dst;
+  uint8_t* k;
+  uint8_t* v;
+  long block_bytes;
+  int N;
+  int32_t* status;
+};
+
+hipError_t launch_fork(const LifecycleArgs& a, hipStream_t s);
+hipError_t launch_truncate(const LifecycleArgs& a, hipStream_t s);
+hipError_t launch_cow(const LifecycleArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s);
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)

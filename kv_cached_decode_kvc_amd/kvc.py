@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "KVC_OK", -1: "KVC_ERR_ARG", -2: "KVC_ERR_SHAPE", -3: "KVC_ER
                 -7: "KVC_ERR_HIP", -8: "KVC_ERR_DATA"}
 EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn",
            "kvc_attn_partition", "kvc_attn_reduce", "kvc_attn_workspace_bytes",
+           "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
            "kvc_attn_partition_tokens", "kvc_status_string")
 
 
@@ -67,7 +68,11 @@ def lib() -> ctypes.CDLL:
         L.kvc_attn_partition.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t,
                                          P, P]
         L.kvc_attn_reduce.argtypes = [D, I, P, P, ctypes.c_size_t, P, I, P, P]
-        for n in EXPORTS[:6]:
+        L.kvc_fork.argtypes = [D, P, P, I, P, P, P, P, P]
+        L.kvc_truncate.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+        L.kvc_cow.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.kvc_copy_blocks.argtypes = [D, P, P, I, P, P, P, P]
+        for n in EXPORTS[:6] + ("kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks"):
             getattr(L, n).restype = ctypes.c_int
         L.kvc_attn_workspace_bytes.argtypes = [D, I]
         L.kvc_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -173,6 +178,43 @@ def kvc_attn_reduce(desc, n_q, seq_lens, workspace, out, dev_status=None, stream
         ctypes.byref(desc), int(n_q), _ptr(seq_lens, "seq_lens", I32), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(out, "out"), _out_dtype(out, out_dtype),
         _ptr(dev_status, "dev_status", I32), _stream(stream)))
+
+
+def kvc_fork(desc, parents, children, n_forks, seq_lens, block_table, ref_counts,
+             dev_status=None, stream=None):
+    _check("kvc_fork", lib().kvc_fork(
+        ctypes.byref(desc), _ptr(parents, "parents", I32), _ptr(children, "children", I32),
+        int(n_forks), _ptr(seq_lens, "seq_lens", I32), _ptr(block_table, "block_table", I32),
+        _ptr(ref_counts, "ref_counts", I32), _ptr(dev_status, "dev_status", I32),
+        _stream(stream)))
+
+
+def kvc_truncate(desc, seq_lens, new_lens, block_table, free_list, free_head_in, free_head_out,
+                 ref_counts, seq_lens_out, dev_status=None, stream=None):
+    _check("kvc_truncate", lib().kvc_truncate(
+        ctypes.byref(desc), _ptr(seq_lens, "seq_lens", I32), _ptr(new_lens, "new_lens", I32),
+        _ptr(block_table, "block_table", I32), _ptr(free_list, "free_list", I32),
+        _ptr(free_head_in, "free_head_in", I32), _ptr(free_head_out, "free_head_out", I32),
+        _ptr(ref_counts, "ref_counts", I32), _ptr(seq_lens_out, "seq_lens_out", I32),
+        _ptr(dev_status, "dev_status", I32), _stream(stream)))
+
+
+def kvc_cow(desc, seq_lens, cu_new, block_table, free_list, free_head_in, free_head_out,
+            ref_counts, k_cache, v_cache, cow_src, cow_dst, dev_status=None, stream=None):
+    _check("kvc_cow", lib().kvc_cow(
+        ctypes.byref(desc), _ptr(seq_lens, "seq_lens", I32), _ptr(cu_new, "cu_new", I32),
+        _ptr(block_table, "block_table", I32), _ptr(free_list, "free_list", I32),
+        _ptr(free_head_in, "free_head_in", I32), _ptr(free_head_out, "free_head_out", I32),
+        _ptr(ref_counts, "ref_counts", I32), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(cow_src, "cow_src", I32), _ptr(cow_dst, "cow_dst", I32),
+        _ptr(dev_status, "dev_status", I32), _stream(stream)))
+
+
+def kvc_copy_blocks(desc, src, dst, n, k_cache, v_cache, dev_status=None, stream=None):
+    _check("kvc_copy_blocks", lib().kvc_copy_blocks(
+        ctypes.byref(desc), _ptr(src, "src", I32), _ptr(dst, "dst", I32), int(n),
+        _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"), _ptr(dev_status, "dev_status", I32),
+        _stream(stream)))
 
 
 def kvc_attn_workspace_bytes(desc, n_q) -> int:

@@ -489,8 +489,10 @@ int kvc_ref_truncate(int B, int bs, int max_blocks, int N, const int32_t* seq_le
                      const int32_t* new_lens, int32_t* table, int32_t* free_list, int32_t* head,
                      int32_t* refs, int32_t* seq_lens_out) {
   long total = 0;
+  if (*head < 0 || *head > N) return REF_ERR_DATA;
   for (int b = 0; b < B; ++b) {
     if (new_lens[b] < 0 || new_lens[b] > seq_lens[b]) return REF_ERR_DATA;
+    if (seq_lens[b] > (long)max_blocks * bs) return REF_ERR_DATA;
     total += ((long)seq_lens[b] + bs - 1) / bs - ((long)new_lens[b] + bs - 1) / bs;
   }
   int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));

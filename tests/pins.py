@@ -620,6 +620,8 @@ def pin_lifecycle_errors(o):
     refs = np.zeros(N, np.int32)
     st, t, f, h, r, out = o.truncate(lens, np.array([7, 0], np.int32), table, free_list, 2, refs, bs)
     assert st == -8 and np.array_equal(t, table) and h == 2
+    st, t, f, h, r, out = o.truncate(lens, np.array([2, 0], np.int32), table, free_list, 7, refs, bs)
+    assert st == -8 and np.array_equal(t, table) and h == 7  # head beyond the pool
     st, l2, t2, r2 = o.fork([0], [0], lens, table, refs, bs, N)
     assert st == -8
     st, l2, t2, r2 = o.fork([0, 1], [1, 0], lens, table, refs, bs, N)  # child 0 is not empty
