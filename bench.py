@@ -106,6 +106,243 @@ def cpu_baseline(w, seconds: float, gpu_out=None):
     }
 
 
+def pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs, dtype=np.float64), q)), 3)
+
+
+def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
+    """Steps timed one at a time with a >= 1 GiB write between them, so that no
+    KV row is served from the last-level caches; HIP events on the library's
+    stream.  Returns (step us list, partition us list)."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    step_us, part_us = [], []
+    for i in range(iters):
+        buf.fill_(float(i))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        lc.step_front()
+        e[1].record()
+        lc.step_partition()
+        e[2].record()
+        lc.step_reduce()
+        e[3].record()
+        torch.cuda.synchronize()
+        step_us.append(e[0].elapsed_time(e[3]) * 1e3)
+        part_us.append(e[1].elapsed_time(e[2]) * 1e3)
+    del buf
+    return step_us, part_us
+
+
+class CallTimer:
+    """HIP events between consecutive library calls on torch's current stream
+    (the stream the binding launches on); per-call medians in microseconds.
+    Each round starts behind a 1 GiB fill, which flushes the caches and keeps
+    the device busy while the host enqueues the round, so that the events time
+    the device and not the host's launch rate."""
+
+    def __init__(self):
+        import torch
+        self.samples = {}
+        self.pending = []
+        self.lead = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+
+    def start(self):
+        import torch
+        self.lead.fill_(1.0)
+        self.pending = [(None, torch.cuda.Event(enable_timing=True))]
+        self.pending[0][1].record()
+
+    def mark(self, name):
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pending.append((name, e))
+
+    def collect(self):
+        import torch
+        torch.cuda.synchronize()
+        for (_, a), (name, b) in zip(self.pending, self.pending[1:]):
+            if name is not None:
+                self.samples.setdefault(name, []).append(a.elapsed_time(b) * 1e3)
+        self.pending = []
+
+    def medians(self):
+        return {k: pct(v, 50) for k, v in self.samples.items()}
+
+
+def lifecycle_bench(iters: int, warmup: int):
+    """Per-call device time of the block-lifecycle entry points in two
+    replayable round trips, plus the block-copy bandwidth.
+
+    speculative: the 5-row verify workload; each round runs copy-on-write,
+      allocation and append of the 5 rows, attention, then truncation to the
+      base length plus a seeded accepted count (0..5); an untimed truncation
+      back to the base length restores the state.
+    parallel sampling: 32 prompts (GQA 32/8, lengths 1024..4096) each forked
+      into 4 samples (B = 128); each round forks, copies the shared partly
+      filled last blocks, appends one token to every sample, attends, and
+      releases the 96 forked samples (the timed truncation); an untimed
+      truncation returns the prompts to their length.
+    """
+    import numpy as np
+    import torch
+
+    from kv_cached_decode_kvc_amd import kvc, metrics, runner, synth
+
+    dev = "cuda"
+    out = {"metric": "block-lifecycle call latency (us, median of HIP-event times)",
+           "iters": iters, "warmup": warmup}
+
+    # -- speculative rollback on the verify workload ----------------------
+    w = synth.get("C5")
+    lc = runner.build(w)
+    refs = torch.zeros(lc.N, dtype=torch.int32, device=dev)
+    src = torch.empty(w.B, dtype=torch.int32, device=dev)
+    dst = torch.empty(w.B, dtype=torch.int32, device=dev)
+    h = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(4)]
+    l_t = torch.empty_like(lc.seq_lens)
+    l_r = torch.empty_like(lc.seq_lens)
+    rng = np.random.default_rng(55)
+    accepted = [runner.i32(lc.s_len0.cpu().numpy() + rng.integers(0, w.n_q + 1, size=w.B), dev)
+                for _ in range(8)]
+    t = CallTimer()
+    for it in range(warmup + iters):
+        t.start()
+        kvc.kvc_cow(lc.desc, lc.s_len0, lc.s_cu, lc.table, lc.free_list, lc.s_head0, h[0], refs,
+                    lc.k, lc.v, src, dst, lc.status)
+        t.mark("cow")
+        kvc.kvc_block_table(lc.desc, lc.s_len0, lc.s_cu, lc.s_total, lc.table, lc.free_list,
+                            h[0], h[1], lc.s_slots, lc.status)
+        t.mark("block_table")
+        kvc.kvc_append(lc.desc, lc.s_k, lc.s_v, lc.s_len0, lc.s_cu, lc.s_total, w.n_q,
+                       lc.s_slots, lc.k, lc.v, lc.s_len1, lc.status)
+        t.mark("append")
+        lc.step_partition()
+        t.mark("partition")
+        lc.step_reduce()
+        t.mark("reduce")
+        kvc.kvc_truncate(lc.desc, lc.s_len1, accepted[it % 8], lc.table, lc.free_list, h[1],
+                         h[2], refs, l_t, lc.status)
+        t.mark("truncate")
+        kvc.kvc_truncate(lc.desc, l_t, lc.s_len0, lc.table, lc.free_list, h[2], h[3], refs, l_r,
+                         lc.status)
+        if it >= warmup:
+            t.collect()
+        else:
+            t.pending = []
+    torch.cuda.synchronize()
+    assert lc.dev_status() == 0, lc.dev_status()
+    assert int(h[3].item()) == int(lc.s_head0.item())
+    med = t.medians()
+    step = sum(med.values())
+    out["speculative"] = {
+        "workload": w.name, "draft_rows": w.n_q, "calls_us": med, "round_us": round(step, 3),
+        "lifecycle_share": round((med["cow"] + med["truncate"]) / step, 4),
+        "verify_rows_per_s": round(w.B * w.n_q / (step * 1e-6), 1),
+    }
+    del lc
+
+    # -- parallel sampling: fork + copy-on-write ---------------------------
+    ws = synth.custom(name="parallel-sampling-32x4-gqa32x8-paged-ctx1024to4096", seed=6, B=128,
+                      Hq=32, Hkv=8, D=128, dtype="bf16", block_size=16, n_q=1, len_lo=1024,
+                      len_hi=4096)
+    n_prompt = 32
+    plen = synth.final_lengths(ws)[:n_prompt]
+    pool = int(sum(-(-int(x) // 16) + 1 for x in plen) * 4 + ws.B)
+    lc = runner.LayerCache(ws, block_size=16, capacity=4112, pool_blocks=pool)
+    lengths = np.zeros(ws.B, np.int64)
+    lengths[:n_prompt] = plen
+    lc.prefill(lengths)
+    lc.prepare_step(0)
+    torch.cuda.synchronize()
+    head0 = lc.head.clone()
+    base = lc.seq_lens.clone()
+    parents = runner.i32(np.repeat(np.arange(n_prompt), 3), dev)
+    children = runner.i32(np.arange(n_prompt, ws.B), dev)
+    zero_children = base.clone()  # prompts keep their length, samples go to 0
+    refs = torch.zeros(lc.N, dtype=torch.int32, device=dev)
+    src = torch.empty(ws.B, dtype=torch.int32, device=dev)
+    dst = torch.empty(ws.B, dtype=torch.int32, device=dev)
+    l_a = torch.empty_like(lc.seq_lens)
+    l_b = torch.empty_like(lc.seq_lens)
+    prompt_only = runner.i32(np.where(np.arange(ws.B) < n_prompt, lengths + 1, 0), dev)
+    t = CallTimer()
+    for it in range(warmup + iters):
+        lens = base.clone()
+        t.start()
+        kvc.kvc_fork(lc.desc, parents, children, ws.B - n_prompt, lens, lc.table, refs, lc.status)
+        t.mark("fork")
+        kvc.kvc_cow(lc.desc, lens, lc.s_cu, lc.table, lc.free_list, lc.head, lc.head, refs, lc.k,
+                    lc.v, src, dst, lc.status)
+        t.mark("cow")
+        kvc.kvc_block_table(lc.desc, lens, lc.s_cu, lc.s_total, lc.table, lc.free_list, lc.head,
+                            lc.head, lc.s_slots, lc.status)
+        t.mark("block_table")
+        kvc.kvc_append(lc.desc, lc.s_k, lc.s_v, lens, lc.s_cu, lc.s_total, 1, lc.s_slots, lc.k,
+                       lc.v, l_a, lc.status)
+        t.mark("append")
+        kvc.kvc_attn_partition(lc.desc, lc.s_q, 1, lc.k, lc.v, l_a, lc.table, lc.scale, lc.s_ws,
+                               lc.status)
+        t.mark("partition")
+        kvc.kvc_attn_reduce(lc.desc, 1, l_a, lc.s_ws, lc.s_out, lc.status)
+        t.mark("reduce")
+        kvc.kvc_truncate(lc.desc, l_a, prompt_only, lc.table, lc.free_list, lc.head, lc.head,
+                         refs, l_b, lc.status)
+        t.mark("truncate")
+        kvc.kvc_truncate(lc.desc, l_b, zero_children, lc.table, lc.free_list, lc.head, lc.head,
+                         refs, lens, lc.status)
+        if it >= warmup:
+            t.collect()
+        else:
+            t.pending = []
+    torch.cuda.synchronize()
+    assert lc.dev_status() == 0, lc.dev_status()
+    assert int(lc.head.item()) == int(head0.item())
+    assert int(refs.abs().sum().item()) == 0
+    med = t.medians()
+    step = sum(med.values())
+    att_bytes = metrics.attended_kv_bytes(np.repeat(plen + 1, 4), ws.Hkv, ws.D, ws.esize)
+    out["parallel_sampling"] = {
+        "workload": ws.name, "prompts": n_prompt, "samples_per_prompt": 4,
+        "calls_us": med, "round_us": round(step, 3),
+        "lifecycle_share": round((med["fork"] + med["cow"] + med["truncate"]) / step, 4),
+        "attention_gbs": round(att_bytes / ((med["partition"] + med["reduce"]) * 1e-6) / 1e9, 2),
+    }
+    blk_bytes = ws.Hkv * 16 * ws.D * ws.esize
+    del lc
+
+    # -- block copies: bandwidth -------------------------------------------
+    n = 4096
+    desc = kvc.cache_desc(1, ws.Hq, ws.Hkv, ws.D, "bf16", 16, max_blocks_per_seq=1,
+                          num_blocks=2 * n)
+    kp = torch.zeros((2 * n, ws.Hkv, 16, ws.D), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    perm = np.random.default_rng(7).permutation(2 * n).astype(np.int32)
+    s_d, d_d = runner.i32(perm[:n], dev), runner.i32(perm[n:], dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    t = CallTimer()
+    for it in range(warmup + iters):
+        t.start()
+        kvc.kvc_copy_blocks(desc, s_d, d_d, n, kp, vp, status)
+        t.mark("copy_blocks")
+        if it >= warmup:
+            t.collect()
+        else:
+            t.pending = []
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    us = t.medians()["copy_blocks"]
+    moved = 2 * 2 * n * blk_bytes  # K and V, read and write
+    out["copy_blocks"] = {
+        "pairs": n, "block_bytes_k": blk_bytes, "us": us,
+        "gbs": round(moved / (us * 1e-6) / 1e9, 2),
+        "hbm_frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    return out
+
+
 def calibrate_copy(nbytes: int, reps: int):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -127,6 +364,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--flush-iters", type=int, default=30,
+                    help="extra steps timed singly after a 1 GiB cache flush (0: skip)")
+    ap.add_argument("--lifecycle", action="store_true",
+                    help="time the block-lifecycle calls instead (speculative rollback, "
+                         "parallel sampling, block copies)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +384,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    if args.lifecycle:
+        print(json.dumps(lifecycle_bench(max(args.steps, 10), args.warmup)), flush=True)
         return
 
     w = synth.get(args.workload)
@@ -181,6 +427,19 @@ def main():
     shash = source_hash(ksrc)
     traffic = stored_traffic(w.name, kname, shash)
 
+    flushed = None
+    if args.flush_iters > 0:
+        st_us, pt_us = flushed_steps(lc, args.flush_iters)
+        assert lc.dev_status() == 0
+        flushed = {
+            "iters": args.flush_iters, "flush_bytes": 1 << 30,
+            "step_us": {"p10": pct(st_us, 10), "median": pct(st_us, 50), "p90": pct(st_us, 90)},
+            "partition_us": {"p10": pct(pt_us, 10), "median": pct(pt_us, 50),
+                             "p90": pct(pt_us, 90)},
+            "gbs_step_median": round(kv_bytes / (pct(st_us, 50) * 1e-6) / 1e9, 2),
+            "gbs_partition_median": round(kv_bytes / (pct(pt_us, 50) * 1e-6) / 1e9, 2),
+        }
+
     gpu_out = lc.s_out.cpu().numpy()
     line = {
         "metric": METRIC,
@@ -203,6 +462,7 @@ def main():
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.B / (ms_per_step / 1e3), 1),
+        "query_rows_per_s": round(w.B * w.n_q / (ms_per_step / 1e3), 1),
         "kv_bytes_per_step": kv_bytes,
         "roofline": {
             "bound": "hbm",
@@ -216,6 +476,7 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
             "source_sha256": shash,
         },
+        "cache_flushed": flushed,
     }
     if args.no_cpu_baseline:
         line["cpu_baseline"] = None

@@ -105,18 +105,20 @@ __global__ __launch_bounds__(kLcThreads) void fork_kernel(LifecycleArgs a) {
     if (tid == 0) report(a.status, s_err);
     return;
   }
-  for (int i = tid; i < a.n; i += kLcThreads) {
+  // one wavefront per fork, its lanes over the table row
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  for (int i = wave; i < a.n; i += kLcWaves) {
     const int p = a.parents[i], c = a.children[i];
     const int lp = a.seq_lens[p];
     const int nb = (lp + a.bs - 1) / a.bs;
     const int32_t* src = a.table + (long)p * a.max_blocks;
     int32_t* dst = a.table + (long)c * a.max_blocks;
-    for (int j = 0; j < nb; ++j) {
+    for (int j = lane; j < nb; j += kWave) {
       const int blk = src[j];
       dst[j] = blk;
       if (blk >= 0 && blk < a.N) atomicAdd(&a.refs[blk], 1);
     }
-    a.seq_lens_out[c] = lp;  // seq_lens_out == seq_lens: the children's entries only
+    if (lane == 0) a.seq_lens_out[c] = lp;  // seq_lens_out == seq_lens: children only
   }
 }
 
@@ -145,18 +147,21 @@ __global__ __launch_bounds__(kLcThreads) void truncate_kernel(LifecycleArgs a) {
     }
     return;
   }
-  for (int b = tid; b < a.B; b += kLcThreads) {
+  // one wavefront per sequence, its lanes over the released blocks
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  for (int b = wave; b < a.B; b += kLcWaves) {
     const int len = a.seq_lens[b], nl = a.new_lens[b];
-    const int old_nb = (len + a.bs - 1) / a.bs, new_nb = (nl + a.bs - 1) / a.bs;
+    const int old_nb = min((len + a.bs - 1) / a.bs, a.max_blocks);
+    const int new_nb = (nl + a.bs - 1) / a.bs;
     int32_t* row = a.table + (long)b * a.max_blocks;
-    for (int j = new_nb; j < old_nb && j < a.max_blocks; ++j) {
+    for (int j = new_nb + lane; j < old_nb; j += kWave) {
       const int blk = row[j];
       row[j] = -1;
       if (blk < 0 || blk >= a.N) continue;
       const bool freed = a.refs ? atomicSub(&a.refs[blk], 1) == 0 : true;
       if (freed) atomicOr(&s_bits[blk >> 5], 1u << (blk & 31));
     }
-    a.seq_lens_out[b] = nl;
+    if (lane == 0) a.seq_lens_out[b] = nl;
   }
   __syncthreads();
   const int new_head = push_marked(s_bits, nwords, a.free_list, head, a.refs, s_wave, a.status);
