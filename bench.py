@@ -343,6 +343,45 @@ def lifecycle_bench(iters: int, warmup: int):
     return out
 
 
+def graph_replay(w, lc, replays: int = 50):
+    """The workload's whole multi-step loop (block table, append, attention per
+    step) captured once as a HIP graph and replayed; also the same loop issued
+    eagerly from Python, for comparison."""
+    import time
+
+    import torch
+
+    from kv_cached_decode_kvc_amd import metrics, runner, synth
+
+    loop = runner.DecodeLoop(lc)
+    g = loop.capture()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    t_graph = (time.perf_counter() - t0) / replays
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        loop.run()
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / replays
+    assert lc.dev_status() == 0
+    final = synth.final_lengths(w)
+    loop_bytes = sum(metrics.attended_kv_bytes(final + s * w.n_q, w.Hkv, w.D, w.esize)
+                     for s in range(w.steps))
+    return {
+        "steps_per_replay": w.steps, "replays": replays,
+        "us_per_step": round(t_graph / w.steps * 1e6, 3),
+        "eager_us_per_step": round(t_eager / w.steps * 1e6, 3),
+        "kv_bytes_per_loop": loop_bytes,
+        "gbs": round(loop_bytes / t_graph / 1e9, 3),
+        "seq_steps_per_s": round(w.B * w.steps / t_graph, 1),
+    }
+
+
 def calibrate_copy(nbytes: int, reps: int):
     """A plain device-to-device copy of known size, for scaling HBM counters."""
     import torch
@@ -440,6 +479,10 @@ def main():
             "gbs_partition_median": round(kv_bytes / (pct(pt_us, 50) * 1e-6) / 1e9, 2),
         }
 
+    graph = None
+    if w.steps > 1:
+        graph = graph_replay(w, lc)
+
     gpu_out = lc.s_out.cpu().numpy()
     line = {
         "metric": METRIC,
@@ -478,6 +521,8 @@ def main():
         },
         "cache_flushed": flushed,
     }
+    if graph is not None:
+        line["graph_replay"] = graph
     if args.no_cpu_baseline:
         line["cpu_baseline"] = None
     else:

@@ -175,6 +175,59 @@ class LayerCache:
         return self.s_out
 
 
+class DecodeLoop:
+    """``w.steps`` dependent decode steps (block table, append, attention) with
+    every input staged on the device.  Step s reads lengths[s] and writes
+    lengths[s + 1] (and, paged, heads[s] -> heads[s + 1]), so running the loop
+    again repeats exactly the same work: it can be captured once in a HIP graph
+    and replayed.  The cache must already hold the cached rows."""
+
+    def __init__(self, lc: LayerCache):
+        w, dev = lc.w, lc.dev
+        self.lc, self.w, self.S = lc, w, w.steps
+        self.lens = [lc.seq_lens.clone()] + [torch.empty_like(lc.seq_lens) for _ in range(w.steps)]
+        self.k = [to_dev(synth.packed_new_rows(w, "k", s), w.dtype, dev) for s in range(w.steps)]
+        self.v = [to_dev(synth.packed_new_rows(w, "v", s), w.dtype, dev) for s in range(w.steps)]
+        self.q = [to_dev(synth.packed_queries(w, s), w.dtype, dev) for s in range(w.steps)]
+        self.out = torch.empty((w.steps, w.B, w.n_q, w.Hq, w.D), dtype=torch.float32, device=dev)
+        self.cu = i32(synth.cu_from_counts([w.n_q] * w.B), dev)
+        self.total = w.n_q * w.B
+        self.ws = lc.workspace(w.n_q)
+        if lc.bs:
+            self.heads = [lc.head.clone()] + [torch.empty_like(lc.head) for _ in range(w.steps)]
+            self.slots = [torch.empty(self.total, dtype=torch.int32, device=dev)
+                          for _ in range(w.steps)]
+
+    def run(self):
+        lc, w = self.lc, self.w
+        for s in range(self.S):
+            slots = None
+            if lc.bs:
+                slots = self.slots[s]
+                kvc.kvc_block_table(lc.desc, self.lens[s], self.cu, self.total, lc.table,
+                                    lc.free_list, self.heads[s], self.heads[s + 1], slots,
+                                    lc.status)
+            kvc.kvc_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total, w.n_q,
+                           slots, lc.k, lc.v, self.lens[s + 1], lc.status)
+            kvc.kvc_attn_partition(lc.desc, self.q[s], w.n_q, lc.k, lc.v, self.lens[s + 1],
+                                   lc.table, lc.scale, self.ws, lc.status)
+            kvc.kvc_attn_reduce(lc.desc, w.n_q, self.lens[s + 1], self.ws, self.out[s], lc.status)
+        return self.out
+
+    def capture(self):
+        """The whole loop as one HIP graph (through torch's graph capture)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()  # warm the lazy initialisation outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        return g
+
+
 def build(w: synth.Workload, step=0, **kw) -> LayerCache:
     """A full workload on the device: cached rows appended, one step prepared."""
     lc = LayerCache(w, **kw)
