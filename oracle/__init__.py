@@ -24,8 +24,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
 _LIB = os.path.join(_HERE, "libkvc_oracle.so")
 
-DTYPES = {"bf16": 0, "f32": 1}
-NP_DTYPES = {"bf16": np.uint16, "f32": np.float32}
+DTYPES = {"bf16": 0, "f32": 1, "f64": 2}
+NP_DTYPES = {"bf16": np.uint16, "f32": np.float32, "f64": np.float64}
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -62,6 +63,16 @@ class Oracle:
         lib.kvc_ref_fork.argtypes = [I, I, I, I, P, P, I, P, P, P]
         lib.kvc_ref_truncate.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
         lib.kvc_ref_cow.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        lib.kvc_ref_fp8_decode.argtypes = [I, I]
+        lib.kvc_ref_fp8_decode.restype = ctypes.c_double
+        lib.kvc_ref_fp8_encode.argtypes = [ctypes.c_double, I]
+        lib.kvc_ref_fp8_encode.restype = ctypes.c_int
+        lib.kvc_ref_fp8_max.argtypes = [I]
+        lib.kvc_ref_fp8_max.restype = ctypes.c_double
+        lib.kvc_ref_quantize_rows.argtypes = [P, ctypes.c_long, I, I, P, P]
+        lib.kvc_ref_quantize_rows.restype = None
+        lib.kvc_ref_dequantize_rows.argtypes = [P, P, ctypes.c_long, I, I, P]
+        lib.kvc_ref_dequantize_rows.restype = None
         for name in ("kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
                      "kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
                      "kvc_ref_attention", "kvc_ref_cache_attention",
@@ -192,6 +203,46 @@ class Oracle:
                                   self._p(refs), self._p(k_pool), self._p(v_pool), self._p(src),
                                   self._p(dst))
         return st, table, free_list, int(h[0]), refs, src, dst
+
+    # -- FP8 cache: kvc_ref_fp8_decode / _encode / quantize / dequantize ------
+    def fp8_decode(self, codes, fmt) -> np.ndarray:
+        """Values of FP8 codes (float64); fmt "e4m3" or "e5m2"."""
+        f = FP8_FORMATS[fmt]
+        c = np.asarray(codes, dtype=np.int64)
+        return np.array([self.lib.kvc_ref_fp8_decode(int(x), f) for x in c.ravel()],
+                        dtype=np.float64).reshape(c.shape)
+
+    def fp8_encode(self, values, fmt) -> np.ndarray:
+        """Nearest FP8 codes (ties to even, saturating) of finite values."""
+        f = FP8_FORMATS[fmt]
+        v = np.asarray(values, dtype=np.float64)
+        return np.array([self.lib.kvc_ref_fp8_encode(float(x), f) for x in v.ravel()],
+                        dtype=np.uint8).reshape(v.shape)
+
+    def fp8_max(self, fmt) -> float:
+        return float(self.lib.kvc_ref_fp8_max(FP8_FORMATS[fmt]))
+
+    def quantize_rows(self, x_bits, fmt):
+        """bf16 bit patterns [..., D] -> (codes uint8 [..., D], scales float32 [...])."""
+        x = self._c(x_bits, np.uint16)
+        D = x.shape[-1]
+        n = x.size // D if D else 0
+        codes = np.zeros(x.shape, np.uint8)
+        scales = np.zeros(x.shape[:-1], np.float32)
+        self.lib.kvc_ref_quantize_rows(self._p(x), n, D, FP8_FORMATS[fmt], self._p(codes),
+                                       self._p(scales))
+        return codes, scales
+
+    def dequantize_rows(self, codes, scales, fmt) -> np.ndarray:
+        """(codes [..., D], scales [...]) -> float64 values [..., D]."""
+        c = self._c(codes, np.uint8)
+        sc = self._c(scales, np.float32)
+        assert sc.shape == c.shape[:-1]
+        D = c.shape[-1]
+        out = np.zeros(c.shape, np.float64)
+        self.lib.kvc_ref_dequantize_rows(self._p(c), self._p(sc), c.size // D if D else 0, D,
+                                         FP8_FORMATS[fmt], self._p(out))
+        return out
 
     # -- kvc_ref_attention --------------------------------------------------
     def attention(self, q, k, v, scale, dtype):

@@ -39,14 +39,17 @@
 #define REF_ERR_NO_BLOCKS (-6)
 #define REF_ERR_DATA (-8)
 
-/* element types: 0 = bfloat16 (1 sign, 8 exponent, 7 mantissa bits), 1 = IEEE float32 */
+/* element types: 0 = bfloat16 (1 sign, 8 exponent, 7 mantissa bits), 1 = IEEE
+ * float32, 2 = IEEE float64 (dequantized FP8 caches are handed over widened) */
 #define REF_BF16 0
 #define REF_F32 1
+#define REF_F64 2
 
 /* Exact widening of one stored element to double.  A bf16 value is the upper
  * half of the float32 with the same bits ([I2] "Quantization", number-format
  * table: bf16 keeps float32's 8-bit exponent and 7 of its mantissa bits). */
 static double load_elem(const void* base, size_t idx, int dtype) {
+  if (dtype == REF_F64) return ((const double*)base)[idx];
   if (dtype == REF_F32) return (double)((const float*)base)[idx];
   uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
@@ -559,4 +562,93 @@ int kvc_ref_cow(int B, int bs, int max_blocks, int N, int Hkv, int D, int esize,
   int st = push_freed(cand, nc, free_list, head, refs);
   free(cand);
   return st;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 KV cache.
+ *
+ * [I2] "Quantization" number-format table: FP8 E4M3 (1 sign, 4 exponent, 3
+ * mantissa bits, largest value 448) and FP8 E5M2 (1/5/2, largest 57,344), both
+ * used for the KV cache.  [VN] 03 "KV cache quantization": storing K and V in
+ * FP8 halves the cache and the bytes read per decode step; [I2] "KV cache
+ * quantization": FP8 with per-token or per-channel scales is nearly lossless.
+ *
+ * Readings (the pages fix the formats, not the encoding details):
+ *   - E4M3 is the variant with no infinities whose only NaN pattern is
+ *     S.1111.111 (so 448 = 1.1100 x 2^8 is the largest value); E5M2 follows the
+ *     IEEE layout (exponent 11111 holds infinities and NaNs);
+ *   - exponent bias 2^(e-1) - 1 (7 and 15), subnormals when the exponent field
+ *     is zero;
+ *   - one fp32 scale per (token, KV head) for K and for V: s = amax / FMAX with
+ *     amax the largest |x| of that row (float32 division), and the code of x
+ *     is the FP8 value nearest to x / s (float32 division), ties to the even
+ *     code, saturated to +-FMAX; a row of zeros has s = 0 and codes 0;
+ *   - the dequantized element is decode(code) * s, exactly (in double).
+ */
+#define REF_E4M3 0
+#define REF_E5M2 1
+
+static int fp8_mant_bits(int fmt) { return fmt == REF_E4M3 ? 3 : 2; }
+static int fp8_bias(int fmt) { return fmt == REF_E4M3 ? 7 : 15; }
+
+/* Value of an FP8 code, straight from the bit fields. */
+double kvc_ref_fp8_decode(int code, int fmt) {
+  int mb = fp8_mant_bits(fmt), eb = 7 - mb;
+  int sign = (code >> 7) & 1, e = (code >> mb) & ((1 << eb) - 1), m = code & ((1 << mb) - 1);
+  int emax = (1 << eb) - 1;
+  double v;
+  if (fmt == REF_E4M3 && e == emax && m == (1 << mb) - 1) return NAN;
+  if (fmt == REF_E5M2 && e == emax) return m ? NAN : (sign ? -INFINITY : INFINITY);
+  if (e == 0)
+    v = ldexp((double)m, 1 - fp8_bias(fmt) - mb); /* subnormal: m * 2^(1 - bias - mb) */
+  else
+    v = ldexp(1.0 + (double)m / (1 << mb), e - fp8_bias(fmt));
+  return sign ? -v : v;
+}
+
+double kvc_ref_fp8_max(int fmt) { return fmt == REF_E4M3 ? 448.0 : 57344.0; }
+
+/* Nearest FP8 code to the finite value y: the non-negative codes from 0 up
+ * to the largest finite one hold increasing values, so the nearest is found
+ * among them (ties to the code with an even mantissa), with the sign bit set
+ * for negative y.  Values beyond the largest finite one saturate to it. */
+int kvc_ref_fp8_encode(double y, int fmt) {
+  int sign = y < 0 ? 0x80 : 0;
+  double a = fabs(y);
+  int top = fmt == REF_E4M3 ? 0x7E : 0x7B; /* largest finite code */
+  if (a >= kvc_ref_fp8_decode(top, fmt)) return sign | top;
+  int lo = 0, hi = top; /* invariant: value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (kvc_ref_fp8_decode(mid, fmt) <= a) lo = mid; else hi = mid;
+  }
+  double dlo = a - kvc_ref_fp8_decode(lo, fmt), dhi = kvc_ref_fp8_decode(hi, fmt) - a;
+  int c = dlo < dhi ? lo : dhi < dlo ? hi : ((lo & 1) == 0 ? lo : hi);
+  return sign | c;
+}
+
+/* Quantize n rows of D bf16 elements (bit patterns): one scale per row. */
+void kvc_ref_quantize_rows(const uint16_t* x, long n, int D, int fmt, uint8_t* codes,
+                           float* scales) {
+  for (long r = 0; r < n; ++r) {
+    float amax = 0.f;
+    for (int d = 0; d < D; ++d) {
+      float v = (float)fabs(load_elem(x, (size_t)r * D + d, REF_BF16));
+      if (v > amax) amax = v;
+    }
+    float s = amax / (float)kvc_ref_fp8_max(fmt);
+    scales[r] = s;
+    for (int d = 0; d < D; ++d) {
+      float v = (float)load_elem(x, (size_t)r * D + d, REF_BF16);
+      codes[(size_t)r * D + d] = s == 0.f ? 0 : (uint8_t)kvc_ref_fp8_encode((double)(v / s), fmt);
+    }
+  }
+}
+
+/* The values an FP8 cache holds: decode(code) * scale, in double (exact). */
+void kvc_ref_dequantize_rows(const uint8_t* codes, const float* scales, long n, int D, int fmt,
+                             double* out) {
+  for (long r = 0; r < n; ++r)
+    for (int d = 0; d < D; ++d)
+      out[(size_t)r * D + d] = kvc_ref_fp8_decode(codes[(size_t)r * D + d], fmt) * (double)scales[r];
 }

@@ -693,5 +693,128 @@ def pin_round_bf16_exhaustive_neighbours(o):
         assert int(g) == best[1] or (x == 0.0), (x, hex(int(g)), hex(best[1]))
 
 
+# ---------------------------------------------------------------------------
+# FP8 KV cache: formats, encoding, per-row scales
+# ---------------------------------------------------------------------------
+_TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def pin_fp8_decode_matches_torch(o):
+    """All 256 codes of both formats decode to what torch's float8 types hold
+    (an independent implementation of the same two formats), and the largest
+    finite values are the ones the pages' number-format table prints."""
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in _TORCH_FP8.items():
+        mine = o.fp8_decode(codes, fmt)
+        ref = torch.from_numpy(codes).view(tdt).to(torch.float64).numpy()
+        same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+        assert same.all(), (fmt, np.nonzero(~same)[0][:5])
+        assert np.nanmax(mine[np.isfinite(mine)]) == {"e4m3": 448.0, "e5m2": 57344.0}[fmt]
+        assert o.fp8_max(fmt) == {"e4m3": 448.0, "e5m2": 57344.0}[fmt]
+
+
+def pin_fp8_encode_nearest_ties_even(o):
+    """Encoding = torch's float8 rounding on values spread over every binade
+    (subnormals included); exact midpoints between neighbouring codes go to
+    the even code; values past the largest finite one saturate to it."""
+    rng = np.random.default_rng(81)
+    for fmt, tdt in _TORCH_FP8.items():
+        top = o.fp8_max(fmt)
+        x = rng.standard_normal(4000) * np.exp2(rng.uniform(-20, np.log2(top), 4000))
+        x = np.clip(x, -top, top)
+        got = o.fp8_encode(x, fmt)
+        ref = torch.from_numpy(x).to(tdt).view(torch.uint8).numpy()
+        assert np.array_equal(got, ref), fmt
+        vals = o.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+        finite = [c for c in range(0x80) if np.isfinite(vals[c])]
+        for c in finite[:-1]:  # midpoint of c and c + 1: the even one of the two wins
+            mid = (vals[c] + vals[c + 1]) / 2
+            want = c if c % 2 == 0 else c + 1
+            assert o.fp8_encode([mid], fmt)[0] == want, (fmt, c)
+            assert o.fp8_encode([-mid], fmt)[0] == want | 0x80, (fmt, c)
+        assert o.fp8_encode([top * 3, -top * 3], fmt).tolist() == [finite[-1], finite[-1] | 0x80]
+
+
+def _representable_rows(o, fmt, rng, n, D):
+    """Rows whose quantization is lossless: random codes times a power-of-two
+    scale, with one element at +-FMAX so that amax / FMAX is that scale."""
+    top = o.fp8_max(fmt)
+    vals = o.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+    ok = np.nonzero(np.isfinite(vals))[0].astype(np.uint8)
+    codes = rng.choice(ok, size=(n, D)).astype(np.uint8)
+    top_code = int(o.fp8_encode([top], fmt)[0])
+    codes[np.arange(n), rng.integers(0, D, n)] = top_code | (0x80 * rng.integers(0, 2, n))
+    scales = np.exp2(rng.integers(-12, -4, n)).astype(np.float32)
+    x = o.fp8_decode(codes, fmt) * scales[:, None]
+    bits = o.round_bf16(x)
+    assert np.array_equal(widen(bits), x), "the rows must be exactly bf16"
+    return bits, codes, scales
+
+
+def widen(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_fp8_quantize_lossless_on_representable_rows(o):
+    """Rows made of FP8 values times a power-of-two scale, with one element at
+    the format's largest value, quantize back to exactly those codes and that
+    scale, and dequantize to exactly the rows."""
+    rng = np.random.default_rng(82)
+    for fmt in _TORCH_FP8:
+        bits, codes, scales = _representable_rows(o, fmt, rng, 40, 64)
+        c2, s2 = o.quantize_rows(bits, fmt)
+        assert np.array_equal(s2, scales), fmt
+        # a zero may be encoded with either sign: compare values
+        assert np.array_equal(o.fp8_decode(c2, fmt), o.fp8_decode(codes, fmt)), fmt
+        assert np.array_equal(o.dequantize_rows(c2, s2, fmt), widen(bits)), fmt
+    z, zs = o.quantize_rows(np.zeros((2, 8), np.uint16), "e4m3")
+    assert not z.any() and not zs.any()
+
+
+def pin_fp8_quantize_error_and_nearest(o):
+    """On random bf16 rows: the scale is the row's largest magnitude over the
+    format's largest value; every code is at least as near to x / s as both
+    neighbouring codes; the dequantization error is within half a spacing."""
+    rng = np.random.default_rng(83)
+    for fmt, mb in (("e4m3", 3), ("e5m2", 2)):
+        x = rng.standard_normal((30, 3, 128)).astype(np.float32) * \
+            np.exp2(rng.uniform(-6, 6, (30, 3, 1))).astype(np.float32)
+        bits = synth.to_bf16_bits(x)
+        codes, scales = o.quantize_rows(bits, fmt)
+        xv = widen(bits)
+        amax = np.abs(xv).max(axis=-1)
+        assert np.array_equal(scales, (amax.astype(np.float32) / np.float32(o.fp8_max(fmt))))
+        y = (xv.astype(np.float32) / scales[..., None]).astype(np.float64)
+        vals = o.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+        got = vals[codes]
+        for step in (-1, 1):
+            nb = np.clip((codes & 0x7F).astype(int) + step, 0, 0x7E if fmt == "e4m3" else 0x7B)
+            nv = vals[nb | (codes & 0x80)]
+            assert np.all(np.abs(y - got) <= np.abs(y - nv) + 0.0)
+        deq = o.dequantize_rows(codes, scales, fmt)
+        rel = np.abs(deq - xv) / np.maximum(np.abs(xv), 2.0 ** (1 - (7 if mb == 3 else 15)) *
+                                           scales[..., None])
+        assert rel.max() <= 2.0 ** -(mb + 1) * (1 + 1e-6), (fmt, rel.max())
+
+
+def pin_fp8_cache_attention_equals_bf16_on_representable_rows(o):
+    """Attention over an FP8 cache (dequantized K and V) equals attention over
+    the bf16 cache of the same rows when the quantization is lossless: the
+    scales belong to the right tensor and the right row."""
+    rng = np.random.default_rng(84)
+    Hq, Hkv, D, L, n_q = 4, 2, 64, 37, 3
+    for fmt in _TORCH_FP8:
+        kb, _, _ = _representable_rows(o, fmt, rng, Hkv * L, D)
+        vb, _, _ = _representable_rows(o, fmt, rng, Hkv * L, D)
+        kc, ks = o.quantize_rows(kb, fmt)
+        vc, vs = o.quantize_rows(vb, fmt)
+        kd = o.dequantize_rows(kc, ks, fmt).reshape(Hkv, L, D)
+        vd = o.dequantize_rows(vc, vs, fmt).reshape(Hkv, L, D)
+        q = synth.to_bf16_bits(rng.standard_normal((n_q, Hq, D)).astype(np.float32))
+        want = o.attention(q, kb.reshape(Hkv, L, D), vb.reshape(Hkv, L, D), 0.125, "bf16")
+        got = o.attention(widen(q), kd, vd, 0.125, "f64")
+        assert np.array_equal(got, want), fmt
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 FAST_PINS = [p for p in ALL_PINS if p.__name__ not in ("pin_page_code3a_magnitude",)]

@@ -32,6 +32,10 @@ MUTANTS = {
     "cow_writes_shared_block": ("table[(long)b * max_blocks + len / bs] = cow_dst[b];",
                                 "table[(long)b * max_blocks + len / bs] = cow_src[b];"),
     "freed_twice": ("if (i > 0 && cand[i] == cand[i - 1]) continue;", "if (0) continue;"),
+    "fp8_bias_off_by_one": ("return fmt == REF_E4M3 ? 7 : 15;", "return fmt == REF_E4M3 ? 8 : 16;"),
+    "fp8_ties_up": ("((lo & 1) == 0 ? lo : hi)", "hi"),
+    "fp8_scale_not_applied": ("* (double)scales[r];", "* 1.0;"),
+    "fp8_amax_of_first_element": ("if (v > amax) amax = v;", "if (d == 0) amax = v;"),
     "paged_row_shifted": ("return ((blk * Hkv + g) * bs + j % bs) * D;",
                           "return ((blk * Hkv + g) * bs + (j + 1) % bs) * D;"),
 }
