@@ -88,9 +88,14 @@ def cpu_baseline(w, seconds: float, gpu_out=None):
         k, v = rows[b]
         q = synth.queries(w, b)
         t0 = time.perf_counter()
-        want = ref.attention(q, k, v, scale, w.dtype)
+        if w.kv:  # the oracle's own quantization of the rows, dequantized exactly
+            kd = ref.dequantize_rows(*ref.quantize_rows(k, w.kv), w.kv)
+            vd = ref.dequantize_rows(*ref.quantize_rows(v, w.kv), w.kv)
+            want = ref.attention(oracle.widen(q, "bf16"), kd, vd, scale, "f64")
+        else:
+            want = ref.attention(q, k, v, scale, w.dtype)
         spent += time.perf_counter() - t0
-        nbytes += metrics.attended_kv_bytes([lens[b]], w.Hkv, w.D, w.esize)
+        nbytes += metrics.attended_cache_bytes([lens[b]], w.Hkv, w.kv_row_bytes)
         nseq += 1
         if gpu_out is not None and nseq <= w.B:
             worst = max(worst, float(np.abs(gpu_out[b] - want).max()))
@@ -370,7 +375,7 @@ def graph_replay(w, lc, replays: int = 50):
     t_eager = (time.perf_counter() - t0) / replays
     assert lc.dev_status() == 0
     final = synth.final_lengths(w)
-    loop_bytes = sum(metrics.attended_kv_bytes(final + s * w.n_q, w.Hkv, w.D, w.esize)
+    loop_bytes = sum(metrics.attended_cache_bytes(final + s * w.n_q, w.Hkv, w.kv_row_bytes)
                      for s in range(w.steps))
     return {
         "steps_per_replay": w.steps, "replays": replays,
@@ -434,7 +439,7 @@ def main():
     lc = runner.build(w, partition_tokens=args.partition_tokens)
     torch.cuda.synchronize()
     P = kvc.kvc_attn_partition_tokens(lc.desc, w.n_q)
-    mfma = w.dtype == "bf16" and w.G * w.n_q >= 2
+    mfma = w.dtype == "bf16" and w.G * w.n_q >= 2  # bf16 and FP8 caches
 
     for _ in range(args.warmup):
         lc.step()
@@ -458,7 +463,7 @@ def main():
     assert lc.dev_status() == 0
 
     lens = synth.final_lengths(w)
-    kv_bytes = metrics.attended_kv_bytes(lens, w.Hkv, w.D, w.esize)
+    kv_bytes = metrics.attended_cache_bytes(lens, w.Hkv, w.kv_row_bytes)
     ms_per_step = wall / K * 1e3
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / (part_ms / 1e3) / 1e9
@@ -495,13 +500,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": w.cache_dtype,
         "data": "synthetic (seeded N(0,1) rows; lengths and block permutation from the seed)",
         "config": {
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "context": [int(lens.min()), int(lens.max())],
             "block_size": w.block_size, "query_rows": w.n_q, "partition_tokens": P,
-            "accumulate": "f32",
+            "accumulate": "f32", "cache": w.cache_dtype, "cache_row_bytes": w.kv_row_bytes,
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.B / (ms_per_step / 1e3), 1),

@@ -30,9 +30,15 @@
  *     zeroes it beforehand and reads it after synchronising).
  *   - A failed launch returns KVC_ERR_HIP.
  *
- * Layouts (element = 2 bytes for KVC_BF16, 4 for KVC_F32; row-major)
+ * Layouts (element = 2 bytes for KVC_BF16, 4 for KVC_F32, 1 for FP8; row-major)
  *   contiguous cache (block_size == 0): k_cache, v_cache [batch][num_kv_heads][max_seq_len][head_dim]
  *   paged pool       (block_size  > 0): k_cache, v_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *   FP8 caches: each buffer holds those codes (rows x head_dim bytes) and then,
+ *                at the next multiple of 256 bytes, one float32 scale per row
+ *                in the same row order; kvc_cache_bytes() gives the size.  A
+ *                row's scale s is its largest |x| over the format's largest
+ *                value and each code is the nearest FP8 value to x / s (ties
+ *                to even, saturating); the cached value is code * s.
  *   block_table  [batch][max_blocks_per_seq] int32, -1 = unassigned
  *   new rows     k_new, v_new [total_new][num_kv_heads][head_dim], sequence b
  *                owns rows cu_new[b] .. cu_new[b+1]-1 (projection order)
@@ -49,7 +55,14 @@
 extern "C" {
 #endif
 
-typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
+/* Cache element types.  For the two FP8 types the queries, the new key and
+ * value rows and the outputs are bf16, and the cache stores one FP8 code per
+ * element plus one float32 scale per row (token, KV head) ([I2] "Quantization"
+ * number-format table: E4M3 = 1/4/3 bits, largest 448; E5M2 = 1/5/2 bits,
+ * largest 57,344; [VN] 03 "KV cache quantization": FP8 halves the cache and
+ * the bytes each decode step reads; [I2] "KV cache quantization": per-token
+ * scales).  E4M3 has no infinities (S.1111.111 is NaN); E5M2 is IEEE-like. */
+typedef enum { KVC_BF16 = 0, KVC_F32 = 1, KVC_FP8_E4M3 = 2, KVC_FP8_E5M2 = 3 } kvc_dtype;
 
 typedef enum {
   KVC_OK = 0,
@@ -63,7 +76,9 @@ typedef enum {
   KVC_ERR_DATA = -8          /* device data out of range (length, slot, block id)      */
 } kvc_status;
 
-/* Shape of one layer's cache (host struct, passed by pointer). */
+/* Shape of one layer's cache (host struct, passed by pointer).  `dtype` is
+ * the kvc_dtype of the cache (and of q and new rows, which are bf16 for the
+ * FP8 types). */
 typedef struct {
   int32_t batch;              /* B sequences                                            */
   int32_t num_q_heads;        /* Hq                                                     */
@@ -285,6 +300,10 @@ int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_
  */
 int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* dst, int32_t n,
                     void* k_cache, void* v_cache, int32_t* dev_status, void* stream);
+
+/* Bytes of one cache buffer (k_cache or v_cache) for this description: FP8
+ * codes and scales, or the plain elements.  0 on an invalid description. */
+size_t kvc_cache_bytes(const kvc_cache_desc* d);
 
 const char* kvc_status_string(int32_t status);
 

@@ -37,11 +37,15 @@ typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 // MINW: wavefronts per SIMD the register allocation must leave room for.
-template <int D, int NT, int MINW>
+// F: 0 for a bf16 cache, else the FP8 format of the codes (the LDS tile and
+// everything after it stay bf16: codes are widened exactly on the way in, the
+// key scales multiply the scores and the value scales join the weights).
+template <int D, int NT, int MINW, int F>
 __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   constexpr int KK = D / 32;          // QK^T steps of 32 along D
   constexpr int DT = D / 16;          // PV output column tiles
-  constexpr int CH = D / 8;           // 16-byte chunks per key row
+  constexpr int EB = F ? 1 : 2;       // bytes per cache element in HBM
+  constexpr int CH = D * EB / 16;     // 16-byte chunks per key row
   constexpr int RPL = kWave / CH;     // key rows per wave load
   constexpr int U = kTile / RPL;      // loads per tile, each of K and V
   constexpr int ROWB = D * 2 + 16;    // LDS row stride: one 16-byte pad per key row
@@ -130,26 +134,49 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
     return (((long)blk * p.Hkv + g) * p.bs + (tile & (p.bs - 1))) * D;
   };
   uint4 kreg[U], vreg[U];
+  float ks_next[4], vs_next[4];  // FP8: scales of keys grp*4 .. +3 of the tile in flight
   auto load_tile = [&](int tile, long tb) {
-    const uint16_t* kt = (const uint16_t*)p.k + tb;  // uniform bases, 32-bit lane offsets
-    const uint16_t* vt = (const uint16_t*)p.v + tb;
+    const uint8_t* kt = (const uint8_t*)p.k + tb * EB;  // uniform bases, 32-bit lane offsets
+    const uint8_t* vt = (const uint8_t*)p.v + tb * EB;
     const int last = min(kTile, end - tile) - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = min(u * RPL + lr, last);  // masked keys re-read a visible row
-      const uint32_t off = (uint32_t)(key * D + pos * 8);
+      const uint32_t off = (uint32_t)(key * D * EB + pos * 16);
       kreg[u] = load_stream(kt + off);
       vreg[u] = load_stream(vt + off);
+    }
+    if constexpr (F != 0) {
+      const long row0 = tb / D;  // cache row of the tile's first key
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = min(grp * 4 + v, last);
+        ks_next[v] = p.k_scale[row0 + key];
+        vs_next[v] = p.v_scale[row0 + key];
+      }
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int off = (u * RPL + lr) * ROWB + pos * 16;
-      *reinterpret_cast<uint4*>(k_lds + off) = kreg[u];
-      *reinterpret_cast<uint4*>(v_lds + off) = vreg[u];
+      if constexpr (F == 0) {
+        const int off = (u * RPL + lr) * ROWB + pos * 16;
+        *reinterpret_cast<uint4*>(k_lds + off) = kreg[u];
+        *reinterpret_cast<uint4*>(v_lds + off) = vreg[u];
+      } else {  // 16 codes -> 16 bf16 (32 bytes)
+        const int off = (u * RPL + lr) * ROWB + pos * 32;
+        const uint2 k0 = fp8x4_to_bf16x4<F>(kreg[u].x), k1 = fp8x4_to_bf16x4<F>(kreg[u].y);
+        const uint2 k2 = fp8x4_to_bf16x4<F>(kreg[u].z), k3 = fp8x4_to_bf16x4<F>(kreg[u].w);
+        const uint2 v0 = fp8x4_to_bf16x4<F>(vreg[u].x), v1 = fp8x4_to_bf16x4<F>(vreg[u].y);
+        const uint2 v2 = fp8x4_to_bf16x4<F>(vreg[u].z), v3 = fp8x4_to_bf16x4<F>(vreg[u].w);
+        *reinterpret_cast<uint4*>(k_lds + off) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(k_lds + off + 16) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+        *reinterpret_cast<uint4*>(v_lds + off) = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        *reinterpret_cast<uint4*>(v_lds + off + 16) = make_uint4(v2.x, v2.y, v3.x, v3.y);
+      }
     }
   };
+  float ks_cur[4] = {1.f, 1.f, 1.f, 1.f}, vs_cur[4] = {1.f, 1.f, 1.f, 1.f};
   // per-lane LDS operand addresses (loop invariant; the k/dt steps are immediates)
   const uint8_t* ka_ptr = k_lds + col * ROWB + grp * 16;
   const uint8_t* va_ptr = v_lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
@@ -159,6 +186,10 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
     long tb = tile_base(start);
     if (tb >= 0) load_tile(start, tb);
     store_tile();
+    if constexpr (F != 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ks_cur[v] = ks_next[v], vs_cur[v] = vs_next[v];
+    }
     wave_lds_fence();
     for (int tile = start; tile < end; tile += stride) {
       const int next = tile + stride;
@@ -175,6 +206,9 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
         for (int kk = 0; kk < KK; ++kk)
           ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
         bf16x8_t pb[NT];  // keys grp*4 + 0..3: hi halves, then lo halves
+        float sl[4];       // score factor of each of this lane's four keys
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sl[v] = F ? ks_cur[v] * p.scale_log2 : p.scale_log2;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -184,7 +218,7 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
           const int key0 = tile + grp * 4;
           float sv[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
+          for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * sl[v] : -INFINITY;
           float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
           mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -198,15 +232,19 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
             m[nt] = m_new;
           }
           const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
-          const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
-          const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+          f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+          f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+          l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+          if constexpr (F != 0) {  // the value rows' scales join the weights
+            p01 *= f32x2_t{vs_cur[0], vs_cur[1]};
+            p23 *= f32x2_t{vs_cur[2], vs_cur[3]};
+          }
           const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
           const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
           const f32x2_t r01 = p01 - __builtin_convertvector(h01, f32x2_t);  // exact
           const f32x2_t r23 = p23 - __builtin_convertvector(h23, f32x2_t);
           const bf16x2_t lo01 = __builtin_convertvector(r01, bf16x2_t);
           const bf16x2_t lo23 = __builtin_convertvector(r23, bf16x2_t);
-          l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
           pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
                                            __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
                                            0, 1, 2, 3, 4, 5, 6, 7);
@@ -227,6 +265,10 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
       }
       wave_lds_fence();  // this tile's LDS reads are issued before it is overwritten
       if (next < end) store_tile();
+      if constexpr (F != 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ks_cur[v] = ks_next[v], vs_cur[v] = vs_next[v];
+      }
       wave_lds_fence();
       tb = tb_next;
     }
@@ -250,21 +292,29 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   }
 }
 
-hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, hipStream_t s) {
+template <int F>
+void launch_mfma_fmt(const AttnParams& p, int rows_per_item, dim3 grid, dim3 block,
+                     hipStream_t s) {
+  // The register budget leaves room for 2 (32-row blocks) or 3 (16-row
+  // blocks) wavefronts per SIMD, which measured best on MI355X.
+  if (rows_per_item == 32) {
+    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 2, 2, F>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_mfma<64, 2, 2, F>), grid, block, 0, s, p);
+  } else {
+    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 1, 3, F>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_mfma<64, 1, 3, F>), grid, block, 0, s, p);
+  }
+}
+
+hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, int fp8, hipStream_t s) {
   const int R = p.G * p.n_q;
   const int n_rb = (R + rows_per_item - 1) / rows_per_item;
   const long n_items = (long)p.B * p.Hkv * n_rb * p.max_parts;
   if (n_items == 0) return hipSuccess;
   const dim3 grid((unsigned)((n_items + 3) / 4)), block(256);
-  // The register budget leaves room for 2 (32-row blocks) or 3
-  // (16-row blocks) wavefronts per SIMD, which measured best on MI355X.
-  if (rows_per_item == 32) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 2, 2>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_mfma<64, 2, 2>), grid, block, 0, s, p);
-  } else {
-    if (p.D == 128) hipLaunchKernelGGL((partition_mfma<128, 1, 3>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_mfma<64, 1, 3>), grid, block, 0, s, p);
-  }
+  if (fp8 == kFp8E4M3) launch_mfma_fmt<kFp8E4M3>(p, rows_per_item, grid, block, s);
+  else if (fp8 == kFp8E5M2) launch_mfma_fmt<kFp8E5M2>(p, rows_per_item, grid, block, s);
+  else launch_mfma_fmt<0>(p, rows_per_item, grid, block, s);
   return hipGetLastError();
 }
 

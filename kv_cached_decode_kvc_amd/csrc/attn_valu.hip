@@ -10,7 +10,11 @@
 // 0 .. L - n_q + r ("Inference-1", "KV cache": shifted causal mask).
 //
 // Used for MHA (one query row per KV row, so there is no dense contraction to
-// give to the matrix cores) and for every fp32 cache.
+// give to the matrix cores) and for every fp32 cache.  FP8 caches ("Inference
+// o quy mo lon", 03 "KV cache quantization"; "Inference-2", "KV cache
+// quantization") hold one code per element and one scale per row: the row's
+// key scale multiplies the reduced dot product and its value scale joins the
+// softmax weight, so the codes are only widened, never rescaled per element.
 //
 // Partition p of a sequence's n = ceil(L / P) partitions owns the 16-key tiles
 // p, p + n, p + 2n, ...: the wavefronts of one sequence run side by side and
@@ -29,13 +33,28 @@
 
 namespace kvc {
 
+// FP8 cache element of format F (codes; queries stay bf16).
+template <int F>
+struct Fp8 {
+  uint8_t code;
+};
+
+template <typename T>
+struct IsFp8 {
+  static constexpr int kFormat = 0;
+};
+template <int F>
+struct IsFp8<Fp8<F>> {
+  static constexpr int kFormat = F;
+};
+
 template <typename T, int D>
 struct ValuShape {
   static constexpr int VE = 16 / (int)sizeof(T);  // elements per lane per load
   static constexpr int LPR = D / VE;                // lanes per key row
   static constexpr int RPL = kWave / LPR;           // key rows per wave load
   static constexpr int U = kTile / RPL;             // loads per tile (each of K, V)
-  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row split");
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "unsupported row split");
 };
 
 template <typename T>
@@ -43,6 +62,10 @@ struct Elem;
 
 template <>
 struct Elem<uint16_t> {  // bf16: a 16-byte load holds 8 elements in 4 words
+  using Q = uint4;
+  static __device__ __forceinline__ Q load_q(const void* q, long off) {
+    return *reinterpret_cast<const uint4*>((const uint16_t*)q + off);
+  }
   static __device__ __forceinline__ float dot(const uint4& q, const uint4& k) {
     float a = dot2_bf16(k.x, q.x, 0.f);
     a = dot2_bf16(k.y, q.y, a);
@@ -63,6 +86,10 @@ struct Elem<uint16_t> {  // bf16: a 16-byte load holds 8 elements in 4 words
 
 template <>
 struct Elem<float> {  // fp32: 4 elements per 16-byte load
+  using Q = uint4;
+  static __device__ __forceinline__ Q load_q(const void* q, long off) {
+    return *reinterpret_cast<const uint4*>((const float*)q + off);
+  }
   static __device__ __forceinline__ float dot(const uint4& q, const uint4& k) {
     float a = __uint_as_float(q.x) * __uint_as_float(k.x);
     a = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), a);
@@ -77,10 +104,49 @@ struct Elem<float> {  // fp32: 4 elements per 16-byte load
   }
 };
 
+template <int F>
+struct Elem<Fp8<F>> {  // FP8 codes: a 16-byte load holds 16 elements; q is 16 bf16
+  struct Q {
+    uint4 a, b;
+  };
+  static __device__ __forceinline__ Q load_q(const void* q, long off) {
+    const uint4* p = reinterpret_cast<const uint4*>((const uint16_t*)q + off);
+    return Q{p[0], p[1]};
+  }
+  // q . codes (the row's scale is applied by the caller): codes widen to bf16
+  // pairs exactly and meet the bf16 query in v_dot2_f32_bf16
+  static __device__ __forceinline__ float dot(const Q& q, const uint4& k) {
+    const uint2 k0 = fp8x4_to_bf16x4<F>(k.x), k1 = fp8x4_to_bf16x4<F>(k.y);
+    const uint2 k2 = fp8x4_to_bf16x4<F>(k.z), k3 = fp8x4_to_bf16x4<F>(k.w);
+    float a = dot2_bf16(k0.x, q.a.x, 0.f);
+    a = dot2_bf16(k0.y, q.a.y, a);
+    a = dot2_bf16(k1.x, q.a.z, a);
+    a = dot2_bf16(k1.y, q.a.w, a);
+    a = dot2_bf16(k2.x, q.b.x, a);
+    a = dot2_bf16(k2.y, q.b.y, a);
+    a = dot2_bf16(k3.x, q.b.z, a);
+    return dot2_bf16(k3.y, q.b.w, a);
+  }
+  // o += p * codes (p carries the row's value scale)
+  static __device__ __forceinline__ void axpy(float p, const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t lo = fp8x2_to_f32<F, false>(w[i]);
+      const f32x2_t hi = fp8x2_to_f32<F, true>(w[i]);
+      o[4 * i + 0] += p * lo[0];
+      o[4 * i + 1] += p * lo[1];
+      o[4 * i + 2] += p * hi[0];
+      o[4 * i + 3] += p * hi[1];
+    }
+  }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
+  constexpr bool kF8 = IsFp8<T>::kFormat != 0;
   const int lane = threadIdx.x & 63;
   const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
@@ -118,8 +184,8 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
     const int g = h / p.G;
     const T* kbase = (const T*)p.k;
     const T* vbase = (const T*)p.v;
-    const uint4 qv = *reinterpret_cast<const uint4*>(
-        (const T*)p.q + (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
+    const typename Elem<T>::Q qv =
+        Elem<T>::load_q(p.q, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
     for (int tile = start; tile < end; tile += stride) {
       long tbase;  // element offset of key `tile` of (b, g)
       if (p.table == nullptr) {
@@ -134,6 +200,7 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
       }
       const int nvalid = min(kTile, end - tile);  // >= 1
       uint4 kr[U], vr[U];
+      float ksc[U], vsc[U];  // FP8: scales of this lane's rows
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         int tt = u * RPL + r0;
@@ -141,12 +208,17 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
         const long off = tbase + (long)tt * D + c * VE;
         kr[u] = load_stream(kbase + off);
         vr[u] = load_stream(vbase + off);
+        if constexpr (kF8) {
+          ksc[u] = p.k_scale[tbase / D + tt];
+          vsc[u] = p.v_scale[tbase / D + tt];
+        }
       }
       float s[U];
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[u]));
+        float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[u]));
+        if constexpr (kF8) dotp *= ksc[u];
         s[u] = (u * RPL + r0 < nvalid) ? dotp * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[u]);
       }
@@ -160,7 +232,8 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
       for (int u = 0; u < U; ++u) {
         const float pu = fast_exp2(s[u] - m_new);
         l += pu;
-        Elem<T>::axpy(pu, vr[u], o);
+        if constexpr (kF8) Elem<T>::axpy(pu * vsc[u], vr[u], o);
+        else Elem<T>::axpy(pu, vr[u], o);
       }
       m = m_new;
     }
@@ -187,6 +260,12 @@ hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) 
   if (dtype == KVC_BF16) {
     if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((partition_valu<uint16_t, 64>), grid, block, 0, s, p);
+  } else if (dtype == KVC_FP8_E4M3) {
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 64>), grid, block, 0, s, p);
+  } else if (dtype == KVC_FP8_E5M2) {
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 128>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 64>), grid, block, 0, s, p);
   } else {
     if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((partition_valu<float, 64>), grid, block, 0, s, p);

@@ -32,6 +32,8 @@ struct AttnParams {
   int P, max_parts;
   int cap;               // tokens a sequence may hold
   float scale_log2;      // scale * log2(e): scores go straight into exp2
+  const float* k_scale;  // FP8 caches: one scale per cache row (token, KV head)
+  const float* v_scale;
 };
 
 struct ReduceParams {
@@ -84,14 +86,14 @@ constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
-// Sum over groups of N consecutive lanes (N = 8, 16 or 32); every lane of a
-// group receives the group's total.
+// Sum over groups of N consecutive lanes (N = 4, 8, 16 or 32); every lane of
+// a group receives the group's total.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
   x += dpp<kDppQuadXor1>(x);
   x += dpp<kDppQuadXor2>(x);
-  x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
   if constexpr (N == 32) x += __shfl_xor(x, 16);
   return x;
@@ -119,6 +121,69 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// FP8 cache elements ("Inference-2", brunomaga.github.io, "Quantization"
+// number-format table: E4M3 = 1 sign, 4 exponent, 3 mantissa bits, largest
+// 448; E5M2 = 1/5/2, largest 57,344).  E4M3 has no infinities (S.1111.111 is
+// its NaN), so its largest finite code is 0x7E; E5M2's is 0x7B.
+constexpr int kFp8E4M3 = 1;
+constexpr int kFp8E5M2 = 2;
+
+template <int F>
+struct Fp8Format;
+template <>
+struct Fp8Format<kFp8E4M3> {
+  static constexpr int kMant = 3, kBias = 7;
+  static constexpr float kMax = 448.f;
+  static constexpr uint32_t kTop = 0x7E;
+};
+template <>
+struct Fp8Format<kFp8E5M2> {
+  static constexpr int kMant = 2, kBias = 15;
+  static constexpr float kMax = 57344.f;
+  static constexpr uint32_t kTop = 0x7B;
+};
+
+// Code of the FP8 value nearest to the finite y, ties to the even code,
+// saturated to the largest finite value.  Scaling by powers of two is exact,
+// so rounding the scaled magnitude to an integer (ties to even) rounds the
+// mantissa; a mantissa that rounds up to the next power of two carries into
+// the exponent field by itself.
+template <int F>
+__device__ __forceinline__ uint32_t fp8_encode(float y) {
+  using Fm = Fp8Format<F>;
+  const uint32_t sign = y < 0.f ? 0x80u : 0u;
+  const float a = fabsf(y);
+  if (!(a < Fm::kMax)) return sign | Fm::kTop;
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;  // floor(log2 a) for normal a
+  if (e < 1 - Fm::kBias)  // below the smallest normal: multiples of 2^(1 - bias - mant)
+    return sign | (uint32_t)__builtin_rintf(__builtin_ldexpf(a, Fm::kBias - 1 + Fm::kMant));
+  const int r = (int)__builtin_rintf(__builtin_ldexpf(a, Fm::kMant - e));  // 2^mant .. 2^(mant+1)
+  return sign | (uint32_t)(((e + Fm::kBias) << Fm::kMant) + r - (1 << Fm::kMant));
+}
+
+// Four codes (one 32-bit word) -> four bf16 values, exactly (every E4M3 and
+// E5M2 value is a bf16 value); the hardware conversion decodes these formats.
+template <int F>
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2_t lo, hi;
+  if constexpr (F == kFp8E4M3) {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+  } else {
+    lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, true);
+  }
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// Two codes (the low or high half of a word) -> two floats.
+template <int F, bool HI>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
+  if constexpr (F == kFp8E4M3) return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  else return __builtin_amdgcn_cvt_pk_f32_bf8(w, HI);
 }
 
 }  // namespace kvc

@@ -15,7 +15,7 @@ int check_desc(const kvc_cache_desc* d) {
   if (d->batch >= kMaxBatch) return KVC_ERR_UNSUPPORTED;  // one grid row per sequence
   if (d->num_q_heads % d->num_kv_heads != 0) return KVC_ERR_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return KVC_ERR_UNSUPPORTED;
-  if (d->dtype != KVC_BF16 && d->dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->dtype < KVC_BF16 || d->dtype > KVC_FP8_E5M2) return KVC_ERR_UNSUPPORTED;
   if (d->block_size < 0) return KVC_ERR_SHAPE;
   if (d->block_size == 0) {
     if (d->max_seq_len <= 0) return KVC_ERR_SHAPE;
@@ -33,7 +33,25 @@ int capacity(const kvc_cache_desc* d) {
   return d->block_size ? d->max_blocks_per_seq * d->block_size : d->max_seq_len;
 }
 
-size_t elem_bytes(const kvc_cache_desc* d) { return d->dtype == KVC_BF16 ? 2 : 4; }
+int fp8_format(const kvc_cache_desc* d) {
+  return d->dtype == KVC_FP8_E4M3 ? kFp8E4M3 : d->dtype == KVC_FP8_E5M2 ? kFp8E5M2 : 0;
+}
+
+// bytes of one cache element, and of one element of q / new rows / outputs
+size_t elem_bytes(const kvc_cache_desc* d) {
+  return fp8_format(d) ? 1 : d->dtype == KVC_BF16 ? 2 : 4;
+}
+size_t input_bytes(const kvc_cache_desc* d) { return d->dtype == KVC_F32 ? 4 : 2; }
+
+size_t cache_rows(const kvc_cache_desc* d) {
+  return d->block_size ? (size_t)d->num_blocks * d->num_kv_heads * d->block_size
+                       : (size_t)d->batch * d->num_kv_heads * d->max_seq_len;
+}
+
+// FP8: byte offset of the scales inside a cache buffer (after the codes)
+size_t scale_offset(const kvc_cache_desc* d) {
+  return (cache_rows(d) * d->head_dim + 255) & ~(size_t)255;
+}
 
 struct Plan {
   bool mfma;          // grouped rows on the matrix cores
@@ -54,7 +72,7 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int G = d->num_q_heads / d->num_kv_heads;
   const int R = G * n_q;
-  pl.mfma = d->dtype == KVC_BF16 && R >= 2;
+  pl.mfma = d->dtype != KVC_F32 && R >= 2;
   pl.rows_per_item = R > 16 ? 32 : 16;
   const long units = pl.mfma ? (long)d->batch * d->num_kv_heads *
                                    ((R + pl.rows_per_item - 1) / pl.rows_per_item)
@@ -120,6 +138,10 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  if (fp8_format(d)) {
+    p.k_scale = (const float*)((const char*)k + scale_offset(d));
+    p.v_scale = (const float*)((const char*)v + scale_offset(d));
+  }
   return p;
 }
 
@@ -181,7 +203,10 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
   a.status = dev_status;
   a.B = d->batch;
   a.Hkv = d->num_kv_heads;
-  a.head_bytes = (int)(d->head_dim * elem_bytes(d));
+  a.head_bytes = (int)(d->head_dim * input_bytes(d));  // bytes of one new row of one head
+  a.fp8 = fp8_format(d);
+  a.D = d->head_dim;
+  a.scale_off = fp8_format(d) ? (long)scale_offset(d) : 0;
   a.bs = d->block_size;
   a.S_max = d->max_seq_len;
   a.N = d->num_blocks;
@@ -201,7 +226,8 @@ int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, cons
   const Plan pl = make_plan(d, n_q);
   const AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
                                    workspace, dev_status);
-  hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, (hipStream_t)stream)
+  hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, fp8_format(d),
+                                                 (hipStream_t)stream)
                          : launch_partition_valu(p, d->dtype, (hipStream_t)stream);
   return hip_status(e);
 }
@@ -327,6 +353,10 @@ int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* 
   c.k = (uint8_t*)k_cache;
   c.v = (uint8_t*)v_cache;
   c.block_bytes = (long)d->num_kv_heads * d->block_size * d->head_dim * (long)elem_bytes(d);
+  if (fp8_format(d)) {
+    c.scale_off = (long)scale_offset(d);
+    c.scale_bytes = d->num_kv_heads * d->block_size * (int)sizeof(float);
+  }
   c.N = d->num_blocks;
   c.status = dev_status;
   return hip_status(launch_copy_blocks(c, n, (hipStream_t)stream));
@@ -362,6 +392,12 @@ int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_
   hipError_t e = launch_cow(a, (hipStream_t)stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
   return kvc_copy_blocks(d, cow_src, cow_dst, d->batch, k_cache, v_cache, dev_status, stream);
+}
+
+size_t kvc_cache_bytes(const kvc_cache_desc* d) {
+  if (check_desc(d) != KVC_OK) return 0;
+  if (fp8_format(d)) return scale_offset(d) + cache_rows(d) * sizeof(float);
+  return cache_rows(d) * d->head_dim * elem_bytes(d);
 }
 
 size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q) {

@@ -32,6 +32,9 @@ struct AppendArgs {
   int32_t* status;
   int B, Hkv, head_bytes, bs, S_max, N, max_new, total_new;
   int tok_per_wg;  // set by the launcher
+  int fp8;         // 0: rows copied bit for bit; kFp8E4M3 / kFp8E5M2: bf16 rows quantized
+  int D;           // FP8: codes per row
+  long scale_off;  // FP8: byte offset of the per-row scales inside each cache buffer
 };
 
 constexpr int kMaxBatch = 65536;        // sequences per call (one grid row each)
@@ -60,7 +63,9 @@ struct CopyArgs {
   const int32_t* dst;
   uint8_t* k;
   uint8_t* v;
-  long block_bytes;
+  long block_bytes;  // element bytes of one pool block (all KV heads)
+  long scale_off;    // FP8: byte offset of the per-row scales (0: none)
+  int scale_bytes;   // FP8: scale bytes of one pool block
   int N;
   int32_t* status;
 };
@@ -73,7 +78,7 @@ hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s);
-hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, hipStream_t s);
+hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, int fp8, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s);
 
 }  // namespace kvc

@@ -199,6 +199,97 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
 }
 
+// FP8 cache: the same grid over bf16 input rows.  The D/8 lanes holding one
+// row (aligned groups of 8 or 16 lanes, all active together) reduce the row's
+// largest magnitude with shuffles; the row's scale is that maximum over the
+// format's largest value and every element is stored as the code of x / s.
+template <int F>
+__device__ __forceinline__ uint2 quantize8(const uint4& x, float s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t c[2] = {0u, 0u};
+  if (s != 0.f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = fp8_encode<F>(__fdiv_rn(bf16_lo(w[i]), s));
+      const uint32_t hi = fp8_encode<F>(__fdiv_rn(bf16_hi(w[i]), s));
+      c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+    }
+  }
+  return make_uint2(c[0], c[1]);
+}
+
+__device__ __forceinline__ float amax8(const uint4& x) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  return m;
+}
+
+template <int F>
+__global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a) {
+  using Fm = Fp8Format<F>;
+  const int b = blockIdx.y;
+  const int vec_per_head = a.head_bytes >> 4;  // lanes per row: D / 8
+  const int vec_per_tok = a.Hkv * vec_per_head;
+  const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  const int vchunk = blockIdx.x % n_vchunks;
+  const int tchunk = blockIdx.x / n_vchunks;
+  const int tok_per_wg = a.tok_per_wg;
+  const int len = a.seq_lens[b];
+  const int c0 = a.cu_new[b];
+  const int n = a.cu_new[b + 1] - c0;
+  const bool bad = len < 0 || n < 0 || (a.slots == nullptr && (long)len + n > a.S_max);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.seq_lens_out[b] = bad ? len : len + n;
+    if (bad) report(a.status, (len < 0 || n < 0) ? KVC_ERR_DATA : KVC_ERR_CAPACITY);
+    else if (n > (long)(gridDim.x / n_vchunks) * tok_per_wg) report(a.status, KVC_ERR_DATA);
+  }
+  if (bad) return;
+  const int idx = vchunk * kAppendThreads + threadIdx.x;
+  if (idx >= vec_per_tok) return;  // whole rows: vec_per_tok is a multiple of the row's lanes
+  const int g = idx / vec_per_head;
+  const int w = idx - g * vec_per_head;
+  float* k_scale = reinterpret_cast<float*>(a.k_cache + a.scale_off);
+  float* v_scale = reinterpret_cast<float*>(a.v_cache + a.scale_off);
+  const int t0 = tchunk * tok_per_wg;
+  const int t1 = min(t0 + tok_per_wg, n);
+  for (int t = t0; t < t1; ++t) {  // every lane of a row takes the same branches
+    const long src_tok = (long)c0 + t;
+    if (src_tok >= a.total_new) {
+      report(a.status, KVC_ERR_DATA);
+      break;
+    }
+    long row;  // cache row of (token, head)
+    if (a.slots) {
+      const long slot = a.slots[src_tok];
+      if (slot < 0 || slot >= (long)a.N * a.bs) {
+        if (idx == 0) report(a.status, KVC_ERR_DATA);
+        continue;
+      }
+      row = ((slot / a.bs) * a.Hkv + g) * a.bs + slot % a.bs;
+    } else {
+      row = ((long)b * a.Hkv + g) * a.S_max + len + t;
+    }
+    const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+    const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
+    const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
+    float km = amax8(kx), vm = amax8(vx);
+    for (int off = 1; off < vec_per_head; off <<= 1) {
+      km = fmaxf(km, __shfl_xor(km, off));
+      vm = fmaxf(vm, __shfl_xor(vm, off));
+    }
+    const float ks = __fdiv_rn(km, Fm::kMax), vs = __fdiv_rn(vm, Fm::kMax);
+    const long dst = row * a.D + w * 8;
+    *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8<F>(kx, ks);
+    *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8<F>(vx, vs);
+    if (w == 0) {
+      k_scale[row] = ks;
+      v_scale[row] = vs;
+    }
+  }
+}
+
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(block_table_kernel, dim3(1), dim3(kBtThreads), 0, s, a);
   return hipGetLastError();
@@ -213,8 +304,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   b.tok_per_wg = a.max_new <= 64 ? 1 : 4;
   const long n_tchunks = a.max_new > 0 ? (a.max_new + b.tok_per_wg - 1) / b.tok_per_wg : 1;
   if (n_vchunks * n_tchunks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)(n_vchunks * n_tchunks), a.B), dim3(kAppendThreads),
-                     0, s, b);
+  const dim3 grid((unsigned)(n_vchunks * n_tchunks), a.B);
+  if (a.fp8 == kFp8E4M3) hipLaunchKernelGGL(append_fp8_kernel<kFp8E4M3>, grid, dim3(kAppendThreads), 0, s, b);
+  else if (a.fp8 == kFp8E5M2) hipLaunchKernelGGL(append_fp8_kernel<kFp8E5M2>, grid, dim3(kAppendThreads), 0, s, b);
+  else hipLaunchKernelGGL(append_kernel, grid, dim3(kAppendThreads), 0, s, b);
   return hipGetLastError();
 }
 

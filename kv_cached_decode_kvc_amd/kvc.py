@@ -16,7 +16,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
-KVC_BF16, KVC_F32 = 0, 1
+KVC_BF16, KVC_F32, KVC_FP8_E4M3, KVC_FP8_E5M2 = 0, 1, 2, 3
+DTYPE_CODES = {"bf16": KVC_BF16, "f32": KVC_F32, "fp8_e4m3": KVC_FP8_E4M3,
+               "fp8_e5m2": KVC_FP8_E5M2}
 KVC_OK = 0
 STATUS_NAMES = {0: "KVC_OK", -1: "KVC_ERR_ARG", -2: "KVC_ERR_SHAPE", -3: "KVC_ERR_UNSUPPORTED",
                 -4: "KVC_ERR_WORKSPACE", -5: "KVC_ERR_CAPACITY", -6: "KVC_ERR_NO_BLOCKS",
@@ -24,7 +26,7 @@ STATUS_NAMES = {0: "KVC_OK", -1: "KVC_ERR_ARG", -2: "KVC_ERR_SHAPE", -3: "KVC_ER
 EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn",
            "kvc_attn_partition", "kvc_attn_reduce", "kvc_attn_workspace_bytes",
            "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
-           "kvc_attn_partition_tokens", "kvc_status_string")
+           "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -42,7 +44,7 @@ class kvc_cache_desc(ctypes.Structure):
 def cache_desc(batch, num_q_heads, num_kv_heads, head_dim, dtype, block_size=0, max_seq_len=0,
                max_blocks_per_seq=0, num_blocks=0, partition_tokens=0) -> kvc_cache_desc:
     if isinstance(dtype, str):
-        dtype = {"bf16": KVC_BF16, "f32": KVC_F32}[dtype]
+        dtype = DTYPE_CODES[dtype]
     return kvc_cache_desc(batch, num_q_heads, num_kv_heads, head_dim, dtype, block_size,
                           max_seq_len, max_blocks_per_seq, num_blocks, partition_tokens)
 
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).restype = ctypes.c_int
         L.kvc_attn_workspace_bytes.argtypes = [D, I]
         L.kvc_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.kvc_cache_bytes.argtypes = [D]
+        L.kvc_cache_bytes.restype = ctypes.c_size_t
         L.kvc_attn_partition_tokens.argtypes = [D, I]
         L.kvc_attn_partition_tokens.restype = ctypes.c_int32
         L.kvc_status_string.argtypes = [I]
@@ -223,6 +227,10 @@ def kvc_attn_workspace_bytes(desc, n_q) -> int:
 
 def kvc_attn_partition_tokens(desc, n_q) -> int:
     return int(lib().kvc_attn_partition_tokens(ctypes.byref(desc), int(n_q)))
+
+
+def kvc_cache_bytes(desc) -> int:
+    return int(lib().kvc_cache_bytes(ctypes.byref(desc)))
 
 
 def kvc_status_string(status) -> str:

@@ -48,7 +48,7 @@ class LayerCache:
         if self.bs == 0:
             self.cap = cap
             shape = (w.B, w.Hkv, cap, w.D)
-            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.dtype, 0, max_seq_len=cap,
+            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.cache_dtype, 0, max_seq_len=cap,
                                        partition_tokens=partition_tokens)
             self.table = None
             self.N = 0
@@ -61,19 +61,37 @@ class LayerCache:
                                else synth.pool_blocks(w))
             self.N = pool_blocks
             shape = (self.N, w.Hkv, self.bs, w.D)
-            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.dtype, self.bs,
+            self.desc = kvc.cache_desc(w.B, w.Hq, w.Hkv, w.D, w.cache_dtype, self.bs,
                                        max_blocks_per_seq=self.max_blocks, num_blocks=self.N,
                                        partition_tokens=partition_tokens)
             self.table = torch.full((w.B, self.max_blocks), -1, dtype=torch.int32, device=dev)
             self.free_host = synth.rng(w, synth.S_POOL).permutation(self.N).astype(np.int32)
             self.free_list = i32(self.free_host, dev)
             self.head = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.k = torch.full(shape, fill, dtype=tdt, device=dev)
-        self.v = torch.full(shape, fill, dtype=tdt, device=dev)
+        self.shape = shape
+        if w.kv:  # FP8: codes, then (at a 256-byte boundary) one float32 scale per row
+            nbytes = kvc.kvc_cache_bytes(self.desc)
+            self.k = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.v = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            if poison_nan:  # 0x7F is NaN in both FP8 formats
+                self.k.fill_(0x7F)
+                self.v.fill_(0x7F)
+        else:
+            self.k = torch.full(shape, fill, dtype=tdt, device=dev)
+            self.v = torch.full(shape, fill, dtype=tdt, device=dev)
         self.seq_lens = torch.zeros(w.B, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.n_q = w.n_q
         self.scale = 1.0 / math.sqrt(w.D)
+
+    def fp8_parts(self, which: str):
+        """FP8 cache: (codes uint8 [*shape], scales float32 [*shape[:-1]]) views."""
+        buf = self.k if which == "k" else self.v
+        rows = int(np.prod(self.shape[:-1]))
+        off = (rows * self.w.D + 255) // 256 * 256
+        codes = buf[:rows * self.w.D].view(self.shape)
+        scales = buf[off:off + 4 * rows].view(torch.float32).view(self.shape[:-1])
+        return codes, scales
 
     # -- building the cache ----------------------------------------------
     def add_tokens(self, k_rows: np.ndarray, v_rows: np.ndarray, counts):

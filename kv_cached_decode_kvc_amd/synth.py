@@ -38,10 +38,21 @@ class Workload:
     len_hi: int
     steps: int = 1  # successive decode steps (the cache grows by n_q each step)
     description: str = ""
+    kv: str = ""  # "": the cache holds dtype; "e4m3" / "e5m2": FP8 codes + a scale per row
 
     @property
     def esize(self) -> int:
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def cache_dtype(self) -> str:
+        return "fp8_" + self.kv if self.kv else self.dtype
+
+    @property
+    def kv_row_bytes(self) -> int:
+        """Cache bytes of one row (token, KV head) of K (the same for V): FP8
+        codes plus the row's float32 scale, or the plain elements."""
+        return self.D + 4 if self.kv else self.D * self.esize
 
     @property
     def G(self) -> int:
@@ -72,6 +83,16 @@ WORKLOADS = {w.name: w for w in [
 
 # short aliases, in the order the workloads are listed above
 ALIASES = {"C%d" % (i + 1): n for i, n in enumerate(WORKLOADS)}
+
+# The same four full-size workloads over an FP8 (E4M3) cache: same seeds, so the
+# same lengths and rows, quantized on append.
+for _i in range(2, 6):
+    _w = WORKLOADS[ALIASES["C%d" % _i]]
+    _f = Workload(_w.name + "-fp8e4m3", _w.seed, _w.B, _w.Hq, _w.Hkv, _w.D, _w.dtype,
+                  _w.block_size, _w.n_q, _w.len_lo, _w.len_hi, _w.steps,
+                  _w.description + "; FP8 E4M3 cache, one scale per row", kv="e4m3")
+    WORKLOADS[_f.name] = _f
+    ALIASES["C%dF8" % _i] = _f.name
 
 
 def get(name: str) -> Workload:
@@ -189,6 +210,7 @@ def packed_queries(w: Workload, step: int = 0) -> np.ndarray:
 
 
 def custom(name="custom", seed=0, B=2, Hq=4, Hkv=4, D=64, dtype="bf16", block_size=0, n_q=1,
-           len_lo=16, len_hi=16, steps=1) -> Workload:
+           len_lo=16, len_hi=16, steps=1, kv="") -> Workload:
     """A small workload for tests (same generators, other sizes)."""
-    return Workload(name, seed, B, Hq, Hkv, D, dtype, block_size, n_q, len_lo, len_hi, steps)
+    return Workload(name, seed, B, Hq, Hkv, D, dtype, block_size, n_q, len_lo, len_hi, steps,
+                    kv=kv)

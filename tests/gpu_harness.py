@@ -10,6 +10,8 @@ import math
 import numpy as np
 import torch
 
+import oracle
+
 from kv_cached_decode_kvc_amd import kvc, synth
 
 ATOL, RTOL = 2e-3, 1e-2  # tolerance fixed for attention outputs (bf16 in, fp32 accumulate)
@@ -36,6 +38,16 @@ def logical_rows(w, b, which, cached_len, steps=1):
     return np.ascontiguousarray(np.concatenate(parts, axis=0).transpose(1, 0, 2))
 
 
+def oracle_attention(ref, w, q, k, v, scale):
+    """The oracle's attention over generator rows; an FP8 cache holds the
+    oracle's own quantization of those rows (dequantized exactly)."""
+    if not w.kv:
+        return ref.attention(q, k, v, scale, w.dtype)
+    kd = ref.dequantize_rows(*ref.quantize_rows(k, w.kv), w.kv)
+    vd = ref.dequantize_rows(*ref.quantize_rows(v, w.kv), w.kv)
+    return ref.attention(oracle.widen(q, "bf16"), kd, vd, scale, "f64")
+
+
 def oracle_outputs(ref, w, b_list, cached, steps=1, step_q=None):
     """Oracle attention (float64) of the given sequences at the last step, from
     generator rows only: {b: [n_q, Hq, D]}."""
@@ -45,7 +57,7 @@ def oracle_outputs(ref, w, b_list, cached, steps=1, step_q=None):
     for b in b_list:
         k = logical_rows(w, b, "k", int(cached[b]), steps)
         v = logical_rows(w, b, "v", int(cached[b]), steps)
-        out[b] = ref.attention(synth.queries(w, b, s), k, v, scale, w.dtype)
+        out[b] = oracle_attention(ref, w, synth.queries(w, b, s), k, v, scale)
     return out
 
 

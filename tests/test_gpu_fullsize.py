@@ -11,7 +11,7 @@ from gpu_harness import assert_close, oracle_outputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5", "C2F8", "C3F8", "C4F8", "C5F8"])
 def test_full_size_sampled(ref, name):
     w = synth.get(name)
     print("full-size workload", w.name, flush=True)
