@@ -147,6 +147,7 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
   constexpr bool kF8 = IsFp8<T>::kFormat != 0;
+  constexpr int TPI = kF8 ? 2 : 1;  // tiles per loop iteration
   const int lane = threadIdx.x & 63;
   const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
@@ -186,54 +187,74 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
     const T* vbase = (const T*)p.v;
     const typename Elem<T>::Q qv =
         Elem<T>::load_q(p.q, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
-    for (int tile = start; tile < end; tile += stride) {
-      long tbase;  // element offset of key `tile` of (b, g)
-      if (p.table == nullptr) {
-        tbase = (((long)b * p.Hkv + g) * p.S_max + tile) * D;
-      } else {
-        const int blk = p.table[(long)b * p.max_blocks + tile / p.bs];
-        if (blk < 0 || blk >= p.N) {
-          if (lane == 0) report(p.status, KVC_ERR_DATA);
-          continue;
-        }
-        tbase = (((long)blk * p.Hkv + g) * p.bs + (tile % p.bs)) * D;
-      }
-      const int nvalid = min(kTile, end - tile);  // >= 1
-      uint4 kr[U], vr[U];
-      float ksc[U], vsc[U];  // FP8: scales of this lane's rows
+    // TPI tiles of the partition per iteration: their loads are all issued
+    // before any of them is used (FP8 tiles carry half the bytes, so two keep
+    // as many bytes in flight per wavefront as one bf16 tile)
+    for (int tile = start; tile < end; tile += TPI * stride) {
+      uint4 kr[TPI][U], vr[TPI][U];
+      float ksc[TPI][U], vsc[TPI][U];  // FP8: scales of this lane's rows
+      int nvalid[TPI];                 // visible keys of each tile (0: none)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int tt = u * RPL + r0;
-        tt = tt < nvalid ? tt : nvalid - 1;  // masked lanes re-read a visible row
-        const long off = tbase + (long)tt * D + c * VE;
-        kr[u] = load_stream(kbase + off);
-        vr[u] = load_stream(vbase + off);
-        if constexpr (kF8) {
-          ksc[u] = p.k_scale[tbase / D + tt];
-          vsc[u] = p.v_scale[tbase / D + tt];
+      for (int i = 0; i < TPI; ++i) {
+        const int ti = tile + i * stride;
+        nvalid[i] = 0;
+        if (ti >= end) continue;
+        long tbase;  // element offset of key `ti` of (b, g)
+        if (p.table == nullptr) {
+          tbase = (((long)b * p.Hkv + g) * p.S_max + ti) * D;
+        } else {
+          const int blk = p.table[(long)b * p.max_blocks + ti / p.bs];
+          if (blk < 0 || blk >= p.N) {
+            if (lane == 0) report(p.status, KVC_ERR_DATA);
+            continue;
+          }
+          tbase = (((long)blk * p.Hkv + g) * p.bs + (ti % p.bs)) * D;
+        }
+        nvalid[i] = min(kTile, end - ti);  // >= 1
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          int tt = u * RPL + r0;
+          tt = tt < nvalid[i] ? tt : nvalid[i] - 1;  // masked lanes re-read a visible row
+          const long off = tbase + (long)tt * D + c * VE;
+          kr[i][u] = load_stream(kbase + off);
+          vr[i][u] = load_stream(vbase + off);
+          if constexpr (kF8) {
+            ksc[i][u] = p.k_scale[tbase / D + tt];
+            vsc[i][u] = p.v_scale[tbase / D + tt];
+          }
         }
       }
-      float s[U];
+      float s[TPI][U];
       float mx = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[u]));
-        if constexpr (kF8) dotp *= ksc[u];
-        s[u] = (u * RPL + r0 < nvalid) ? dotp * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[u]);
-      }
-      mx = cross_max<LPR>(mx);  // finite: the tile has a visible key
+      for (int i = 0; i < TPI; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          s[i][u] = -INFINITY;
+          if (nvalid[i] > 0) {
+            float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[i][u]));
+            if constexpr (kF8) dotp *= ksc[i][u];
+            if (u * RPL + r0 < nvalid[i]) s[i][u] = dotp * p.scale_log2;
+          }
+          mx = fmaxf(mx, s[i][u]);
+        }
+      mx = cross_max<LPR>(mx);
+      if (mx == -INFINITY) continue;  // no visible key in these tiles (bad blocks)
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
       l *= alpha;
 #pragma unroll
       for (int j = 0; j < VE; ++j) o[j] *= alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pu = fast_exp2(s[u] - m_new);
-        l += pu;
-        if constexpr (kF8) Elem<T>::axpy(pu * vsc[u], vr[u], o);
-        else Elem<T>::axpy(pu, vr[u], o);
+      for (int i = 0; i < TPI; ++i) {
+        if (nvalid[i] == 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pu = fast_exp2(s[i][u] - m_new);
+          l += pu;
+          if constexpr (kF8) Elem<T>::axpy(pu * vsc[i][u], vr[i][u], o);
+          else Elem<T>::axpy(pu, vr[i][u], o);
+        }
       }
       m = m_new;
     }
