@@ -73,7 +73,8 @@ class Oracle:
         lib.kvc_ref_quantize_rows.restype = None
         lib.kvc_ref_dequantize_rows.argtypes = [P, P, ctypes.c_long, I, I, P]
         lib.kvc_ref_dequantize_rows.restype = None
-        for name in ("kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
+        lib.kvc_ref_mla_attention.argtypes = [I, I, I, I, I, P, P, ctypes.c_double, P]
+        for name in ("kvc_ref_mla_attention", "kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
                      "kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
                      "kvc_ref_attention", "kvc_ref_cache_attention",
                      "kvc_ref_attention_split"):
@@ -242,6 +243,20 @@ class Oracle:
         out = np.zeros(c.shape, np.float64)
         self.lib.kvc_ref_dequantize_rows(self._p(c), self._p(sc), c.size // D if D else 0, D,
                                          FP8_FORMATS[fmt], self._p(out))
+        return out
+
+    # -- kvc_ref_mla_attention ----------------------------------------------
+    def mla_attention(self, q, c, scale, dv):
+        """q [n_q, Hq, Dk], c [L, Dk] (bf16 bits) -> out [n_q, Hq, dv] float64:
+        attention over latent rows (keys = whole rows, values = first dv dims)."""
+        q, c = self._c(q, np.uint16), self._c(c, np.uint16)
+        n_q, Hq, Dk = q.shape
+        L = c.shape[0]
+        out = np.zeros((n_q, Hq, dv), dtype=np.float64)
+        st = self.lib.kvc_ref_mla_attention(n_q, Hq, Dk, dv, L, self._p(q), self._p(c),
+                                            float(scale), self._p(out))
+        if st != 0:
+            raise ValueError("mla_attention failed: %d" % st)
         return out
 
     # -- kvc_ref_attention --------------------------------------------------

@@ -652,3 +652,57 @@ void kvc_ref_dequantize_rows(const uint8_t* codes, const float* scales, long n, 
     for (int d = 0; d < D; ++d)
       out[(size_t)r * D + d] = kvc_ref_fp8_decode(codes[(size_t)r * D + d], fmt) * (double)scales[r];
 }
+
+/* ------------------------------------------------------------------------ */
+/* MLA latent decode.
+ *
+ * [I1] "Smaller KV caches: MQA, GQA and MLA": MLA caches one latent vector per
+ * token; with the key and value up-projections absorbed into the query and
+ * output projections, attention runs directly over the cached latents, which
+ * act as both keys and values -- one large key-value head shared by every
+ * query head.  [VN] 03 "MLA: compress K/V into a latent": a small decoupled
+ * key carrying RoPE is cached beside the latent; per token d_c + d_h^R values
+ * are cached (512 + 64).  [EI] GQA passage: MLA stores a low-rank latent of
+ * dimension C = 512.
+ *
+ * Readings: a cache row is [latent (Dv) | rope key (Dk - Dv)]; the absorbed
+ * query of each head has the same Dk dims (absorbed latent query, then rope
+ * query); the score is scale * (q . row) over all Dk dims; the value is the
+ * row's first Dv dims (the latent); the output is the weighted latent [Dv],
+ * which the absorbed value up-projection then maps per head (outside this
+ * step).  Verify rows see keys 0 .. L - n_q + r as for ordinary attention.
+ *
+ *   q [n_q][Hq][Dk], c [L][Dk] (bf16 bit patterns), out [n_q][Hq][Dv] (double)
+ */
+int kvc_ref_mla_attention(int n_q, int Hq, int Dk, int Dv, int L, const uint16_t* q,
+                          const uint16_t* c, double scale, double* out) {
+  if (n_q <= 0 || Hq <= 0 || Dk <= 0 || Dv <= 0 || Dv > Dk) return REF_ERR_ARG;
+  if (L < n_q) return REF_ERR_DATA;
+  double* p = (double*)malloc(sizeof(double) * (size_t)L);
+  if (!p) return REF_ERR_ARG;
+  for (int r = 0; r < n_q; ++r)
+    for (int h = 0; h < Hq; ++h) {
+      long last = (long)L - n_q + r;
+      double m = -INFINITY;
+      for (long t = 0; t <= last; ++t) {
+        double s = 0.0;
+        for (int d = 0; d < Dk; ++d)
+          s += load_elem(q, ((size_t)r * Hq + h) * Dk + d, REF_BF16) *
+               load_elem(c, (size_t)t * Dk + d, REF_BF16);
+        p[t] = s * scale;
+        if (p[t] > m) m = p[t];
+      }
+      double l = 0.0;
+      for (long t = 0; t <= last; ++t) {
+        p[t] = exp(p[t] - m);
+        l += p[t];
+      }
+      for (int d = 0; d < Dv; ++d) {
+        double acc = 0.0;
+        for (long t = 0; t <= last; ++t) acc += p[t] * load_elem(c, (size_t)t * Dk + d, REF_BF16);
+        out[((size_t)r * Hq + h) * Dv + d] = acc / l;
+      }
+    }
+  free(p);
+  return REF_OK;
+}

@@ -816,5 +816,46 @@ def pin_fp8_cache_attention_equals_bf16_on_representable_rows(o):
         assert np.array_equal(got, want), fmt
 
 
+# ---------------------------------------------------------------------------
+# MLA: attention over absorbed latent rows
+# ---------------------------------------------------------------------------
+def pin_mla_absorbed_equals_recompute(o):
+    """The pages' check of MLA: attention run directly over the cached latents
+    (key up-projection absorbed into the query, value up-projection applied
+    to the weighted latent) equals attention over keys and values recomputed
+    per head from the latents, with the decoupled RoPE key concatenated to
+    every head's key.  Recompute side: torch's scaled_dot_product_attention in
+    float64 with an explicit mask (verify rows see keys 0 .. L - n_q + r).
+    Small-integer entries keep the absorbed query exact in bf16."""
+    rng = np.random.default_rng(61)
+    H, Dh, dc, dr, L, n_q = 4, 8, 16, 8, 21, 3
+    for trial in range(3):
+        Wuk = rng.integers(-1, 2, (H, Dh, dc)).astype(np.float64)
+        Wuv = rng.integers(-1, 2, (H, Dh, dc)).astype(np.float64)
+        c = rng.integers(-2, 3, (L, dc)).astype(np.float64)
+        kr = rng.integers(-2, 3, (L, dr)).astype(np.float64)
+        qn = rng.integers(-1, 2, (n_q, H, Dh)).astype(np.float64)
+        qr = rng.integers(-1, 2, (n_q, H, dr)).astype(np.float64)
+        scale = 1.0 / math.sqrt(Dh + dr)
+        # recompute: per-head keys [W_uk c ; k_rope], values W_uv c
+        k = np.concatenate([np.einsum("hdc,tc->htd", Wuk, c),
+                            np.broadcast_to(kr, (H, L, dr))], axis=-1)      # [H, L, Dh+dr]
+        v = np.einsum("hdc,tc->htd", Wuv, c)                               # [H, L, Dh]
+        qq = np.concatenate([qn, qr], axis=-1).transpose(1, 0, 2)          # [H, n_q, Dh+dr]
+        mask = np.arange(L)[None, :] <= (L - n_q + np.arange(n_q))[:, None]
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qq)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            attn_mask=torch.from_numpy(mask), scale=scale)[0].numpy().transpose(1, 0, 2)
+        # absorbed: q_lat = W_uk^T q_nope, rows [c | k_rope], values = latent
+        qlat = np.einsum("hdc,rhd->rhc", Wuk, qn)
+        qabs = np.concatenate([qlat, qr], axis=-1)
+        rows = np.concatenate([c, kr], axis=-1)
+        qb, rb = o.round_bf16(qabs), o.round_bf16(rows)
+        assert np.array_equal(widen(qb), qabs) and np.array_equal(widen(rb), rows)
+        lat = o.mla_attention(qb, rb, scale, dc)                           # [n_q, H, dc]
+        got = np.einsum("hdc,rhc->rhd", Wuv, lat)
+        assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max()), trial
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 FAST_PINS = [p for p in ALL_PINS if p.__name__ not in ("pin_page_code3a_magnitude",)]

@@ -36,6 +36,10 @@ MUTANTS = {
     "fp8_ties_up": ("((lo & 1) == 0 ? lo : hi)", "hi"),
     "fp8_scale_not_applied": ("* (double)scales[r];", "* 1.0;"),
     "fp8_amax_of_first_element": ("if (v > amax) amax = v;", "if (d == 0) amax = v;"),
+    "mla_scores_from_latent_only": ("        for (int d = 0; d < Dk; ++d)\n          s += load_elem(q, ((size_t)r * Hq + h) * Dk + d, REF_BF16) *",
+                                    "        for (int d = 0; d < Dv; ++d)\n          s += load_elem(q, ((size_t)r * Hq + h) * Dk + d, REF_BF16) *"),
+    "mla_values_from_row_end": ("acc += p[t] * load_elem(c, (size_t)t * Dk + d, REF_BF16);",
+                                "acc += p[t] * load_elem(c, (size_t)t * Dk + d + (Dk - Dv), REF_BF16);"),
     "paged_row_shifted": ("return ((blk * Hkv + g) * bs + j % bs) * D;",
                           "return ((blk * Hkv + g) * bs + (j + 1) % bs) * D;"),
 }
