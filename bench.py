@@ -33,6 +33,8 @@ CSRC = os.path.join(ROOT, "kv_cached_decode_kvc_amd", "csrc")
 
 def kernel_of(w, mfma: bool) -> tuple[str, list[str]]:
     """Name of the dominant kernel and the sources that define it."""
+    if w.dv:
+        return "partition_mla", ["attn_mla.hip", "common.hpp"]
     if mfma:
         return "partition_mfma", ["attn_mfma.hip", "common.hpp"]
     return "partition_valu", ["attn_valu.hip", "common.hpp"]
@@ -84,18 +86,20 @@ def cpu_baseline(w, seconds: float, gpu_out=None):
             rows[b] = tuple(
                 np.concatenate([synth.cache_rows(w, x, b, int(cached[b])),
                                 synth.new_rows(w, x, b)]).transpose(1, 0, 2).copy()
-                for x in ("k", "v"))
-        k, v = rows[b]
+                for x in (("k",) if w.dv else ("k", "v")))
+        k, v = rows[b] if not w.dv else (rows[b][0], None)
         q = synth.queries(w, b)
         t0 = time.perf_counter()
-        if w.kv:  # the oracle's own quantization of the rows, dequantized exactly
+        if w.dv:  # MLA: the latent rows are keys and, in their first dv dims, values
+            want = ref.mla_attention(q, k[0], scale, w.dv)
+        elif w.kv:  # the oracle's own quantization of the rows, dequantized exactly
             kd = ref.dequantize_rows(*ref.quantize_rows(k, w.kv), w.kv)
             vd = ref.dequantize_rows(*ref.quantize_rows(v, w.kv), w.kv)
             want = ref.attention(oracle.widen(q, "bf16"), kd, vd, scale, "f64")
         else:
             want = ref.attention(q, k, v, scale, w.dtype)
         spent += time.perf_counter() - t0
-        nbytes += metrics.attended_cache_bytes([lens[b]], w.Hkv, w.kv_row_bytes)
+        nbytes += metrics.attended_cache_bytes([lens[b]], w.Hkv, w.kv_row_bytes, w.kv_tensors)
         nseq += 1
         if gpu_out is not None and nseq <= w.B:
             worst = max(worst, float(np.abs(gpu_out[b] - want).max()))
@@ -375,7 +379,8 @@ def graph_replay(w, lc, replays: int = 50):
     t_eager = (time.perf_counter() - t0) / replays
     assert lc.dev_status() == 0
     final = synth.final_lengths(w)
-    loop_bytes = sum(metrics.attended_cache_bytes(final + s * w.n_q, w.Hkv, w.kv_row_bytes)
+    loop_bytes = sum(metrics.attended_cache_bytes(final + s * w.n_q, w.Hkv, w.kv_row_bytes,
+                                                  w.kv_tensors)
                      for s in range(w.steps))
     return {
         "steps_per_replay": w.steps, "replays": replays,
@@ -438,7 +443,8 @@ def main():
     print("# building %s on the device" % w.name, file=sys.stderr, flush=True)
     lc = runner.build(w, partition_tokens=args.partition_tokens)
     torch.cuda.synchronize()
-    P = kvc.kvc_attn_partition_tokens(lc.desc, w.n_q)
+    P = (kvc.kvc_mla_partition_tokens(lc.desc, w.n_q, w.dv) if w.dv
+         else kvc.kvc_attn_partition_tokens(lc.desc, w.n_q))
     mfma = w.dtype == "bf16" and w.G * w.n_q >= 2  # bf16 and FP8 caches
 
     for _ in range(args.warmup):
@@ -463,7 +469,10 @@ def main():
     assert lc.dev_status() == 0
 
     lens = synth.final_lengths(w)
-    kv_bytes = metrics.attended_cache_bytes(lens, w.Hkv, w.kv_row_bytes)
+    kv_bytes = metrics.attended_cache_bytes(lens, w.Hkv, w.kv_row_bytes, w.kv_tensors)
+    # score and value products, 2 FLOP per multiply-add, over every visible (row, key)
+    flops = metrics.attention_flops(lens, w.n_q, w.Hq, w.D) // 2 + \
+        metrics.attention_flops(lens, w.n_q, w.Hq, w.out_dim) // 2
     ms_per_step = wall / K * 1e3
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = kv_bytes / (part_ms / 1e3) / 1e9
@@ -507,6 +516,7 @@ def main():
             "head_dim": w.D, "context": [int(lens.min()), int(lens.max())],
             "block_size": w.block_size, "query_rows": w.n_q, "partition_tokens": P,
             "accumulate": "f32", "cache": w.cache_dtype, "cache_row_bytes": w.kv_row_bytes,
+            "cache_tensors": w.kv_tensors, "out_dim": w.out_dim,
         },
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.B / (ms_per_step / 1e3), 1),
@@ -523,6 +533,9 @@ def main():
             "avg_kernel_us": round(part_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": kv_bytes,
             "source_sha256": shash,
+            "flops_per_launch": flops,
+            "achieved_tflops": round(flops / (part_ms / 1e3) / 1e12, 2),
+            "mfma_bf16_peak_tflops": 2500.0,
         },
         "cache_flushed": flushed,
     }

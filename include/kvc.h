@@ -84,7 +84,7 @@ typedef struct {
   int32_t num_q_heads;        /* Hq                                                     */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0, query head h reads KV head h/(Hq/Hkv)
                                  ([I1] "Smaller KV caches": consecutive heads share)    */
-  int32_t head_dim;           /* D in {64, 128}                                         */
+  int32_t head_dim;           /* D in {64, 128}; 576 for an MLA latent cache             */
   int32_t dtype;              /* kvc_dtype of q, caches and new rows                    */
   int32_t block_size;         /* 0: contiguous cache; else paged, a multiple of 16 and a
                                  power of two ([VN] 05 "Block table": 16 by default)     */
@@ -143,6 +143,9 @@ int kvc_block_table(const kvc_cache_desc* d, const int32_t* seq_lens, const int3
  *   slot_mapping  (device) paged: [total_new] from kvc_block_table; contiguous: NULL
  *                 (token t of sequence b goes to position seq_lens[b] + t)
  *   seq_lens_out  (device) [B] = seq_lens + new counts; must not alias seq_lens
+ *   v_new, v_cache may both be NULL: a key-only cache (the MLA latent cache,
+ *                 whose rows serve as keys and values); not for FP8 caches
+ * FP8 caches take bf16 new rows and store codes and per-row scales.
  * Contiguous: a sequence that would pass max_seq_len is not written, keeps its
  * length and reports KVC_ERR_CAPACITY.  Paged: a token whose slot lies outside
  * the pool is not written and reports KVC_ERR_DATA; lengths still advance.
@@ -296,10 +299,47 @@ int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_
  * kvc_copy_blocks -- for i < n with src[i] >= 0, copy pool block src[i] onto
  * dst[i] (all KV heads, K and V, bit for bit).  Pairs must not overlap (no
  * block both a source and a destination).  A block id >= num_blocks is
- * KVC_ERR_DATA and that pair is skipped.
+ * KVC_ERR_DATA and that pair is skipped.  FP8 pools copy the blocks' scales
+ * too; v_cache may be NULL for a key-only pool (also in kvc_cow).
  */
 int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* dst, int32_t n,
                     void* k_cache, void* v_cache, int32_t* dev_status, void* stream);
+
+/*
+ * MLA latent decode.
+ *
+ * [I1] "Smaller KV caches: MQA, GQA and MLA": MLA caches one latent vector per
+ * token, and with the key and value up-projections absorbed into the query
+ * and output projections attention runs directly over the cached latents,
+ * which serve as keys and values: one large KV head shared by every query
+ * head.  [VN] 03 "MLA": each token caches d_c + d_h^R = 512 + 64 values, the
+ * latent and a decoupled key carrying RoPE.
+ *
+ * The cache is a key-only cache (kvc_append and kvc_block_table with v_new =
+ * v_cache = NULL) described by num_kv_heads = 1, head_dim = 576, dtype bf16;
+ * each row is [latent (512) | rope key (64)].
+ *   q            (device) [B][n_q][Hq][576] bf16: per head, the absorbed latent
+ *                query (W_uk^T q_nope) followed by the rope query
+ *   value_dim    (host)   512: the first value_dim dims of a row are the value
+ *   out          (device) [B][n_q][Hq][512]: softmax(scale * q.row) weighted
+ *                latent rows (apply the absorbed value up-projection after)
+ * Verify rows (n_q > 1) see keys 0 .. L - n_q + r.  Other geometries return
+ * KVC_ERR_UNSUPPORTED.  The workspace is sized by kvc_mla_workspace_bytes.
+ */
+size_t kvc_mla_workspace_bytes(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);
+int32_t kvc_mla_partition_tokens(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);
+int kvc_mla_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q,
+                           const void* latent_cache, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t value_dim, float scale,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           void* stream);
+int kvc_mla_attn_reduce(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim,
+                        const int32_t* seq_lens, const void* workspace, size_t workspace_bytes,
+                        void* out, int32_t out_dtype, int32_t* dev_status, void* stream);
+int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* latent_cache,
+                 const int32_t* seq_lens, const int32_t* block_table, int32_t value_dim,
+                 float scale, void* out, int32_t out_dtype, void* workspace,
+                 size_t workspace_bytes, int32_t* dev_status, void* stream);
 
 /* Bytes of one cache buffer (k_cache or v_cache) for this description: FP8
  * codes and scales, or the plain elements.  0 on an invalid description. */

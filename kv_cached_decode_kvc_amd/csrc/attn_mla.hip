@@ -1,0 +1,312 @@
+// attn_mla.hip -- split-KV partition kernel of MLA latent decode.
+//
+// "Inference-1" (brunomaga.github.io), "Smaller KV caches: MQA, GQA and MLA":
+// with the key and value up-projections absorbed into the query and output
+// projections, attention runs directly over the cached latent vectors, which
+// serve as both keys and values -- one large KV head shared by every query
+// head.  "Inference o quy mo lon" (truongducdung.dev), 03 "MLA": each token
+// caches d_c + d_h^R = 512 + 64 values (latent, then the decoupled RoPE key).
+// A cache row is therefore [latent (512) | rope key (64)]: scores use the
+// whole 576-wide row against each head's absorbed query, values are the
+// row's first 512 dims, and the output of a (head, row) is the weighted
+// latent, combined across partitions by the usual reduce.
+//
+// Every query row of a sequence (Hq heads x n_q verify rows) reads the same
+// latent rows, so a workgroup of four wavefronts owns one (sequence, group of
+// up to 64 rows, partition): its threads load each 16-key tile (16 x 1152
+// bytes, one contiguous run) cooperatively into one LDS tile, and each
+// wavefront contracts its 16 rows against it on the matrix cores:
+//   S^T = K . Q^T   (18 steps of v_mfma_f32_16x16x32_bf16, Q^T in registers)
+//   O^T += V^T . P^T (32 column tiles; V^T via ds_read_b64_tr_b16; the
+//                     weights as bf16 hi + lo pairs along the reduction index,
+//                     as in the grouped-query kernel).
+// Online softmax per row as in the other partition kernels; verify row r
+// sees keys 0 .. L - n_q + r.
+//
+// A wavefront holds 16 rows of queries (72 VGPRs) and of 512-wide fp32
+// accumulators (128), so it runs alone on its SIMD (512 registers) and a
+// workgroup fills a CU; latency is hidden by a ring of PF register stages,
+// PF - 1 tiles ahead of the one in use.  Row groups of the same (sequence,
+// partition) get workgroup ids 8 apart: launches place workgroup i on XCD
+// i mod 8, so they share one XCD's L2 and run at the same time, and the tile
+// comes from HBM once.
+#include "launch.hpp"
+
+namespace kvc {
+
+namespace {
+
+typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kMlaWaves = 4;
+constexpr int kMlaMaxTiles = 1024;  // tiles of one partition: partition length <= 16384
+constexpr int kMlaThreads = kMlaWaves * kWave;
+
+}  // namespace
+
+template <int PF>
+__global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
+  constexpr int NT = 1;
+  constexpr int DK = kMlaKeyDim;          // 576
+  constexpr int DV = kMlaValueDim;        // 512
+  constexpr int KK = DK / 32;             // 18 QK^T steps
+  constexpr int DT = DV / 16;             // 32 output column tiles
+  constexpr int CPR = DK * 2 / 16;        // 72 16-byte chunks per row
+  constexpr int TCH = kTile * CPR;        // 1152 chunks per tile
+  constexpr int PER = (TCH + kMlaThreads - 1) / kMlaThreads;  // chunks per thread
+  constexpr int ROWB = DK * 2 + 16;       // padded LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * ROWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  const int R = p.Hq * p.n_q;                 // rows sharing the latent cache
+  const int rows_wg = 16 * NT * kMlaWaves;
+  const int n_rg = (R + rows_wg - 1) / rows_wg;
+  // workgroup id = (chunk * n_rg + rg) * 8 + j: unit (sequence, partition)
+  // = chunk * 8 + j, so its row groups sit 8 ids apart on one XCD
+  const long wg = blockIdx.x;
+  const int rg = (int)((wg / 8) % n_rg);
+  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);  // b * max_parts + part
+  if (unit >= (long)p.B * p.max_parts) return;
+  const int part = (int)(unit % p.max_parts);
+  const int b = (int)(unit / p.max_parts);
+  const int L = p.seq_lens[b];
+  if (L < p.n_q || L > p.cap) {
+    if (part == 0 && rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+    return;  // whole workgroup
+  }
+  const int nparts = (L + p.P - 1) / p.P;
+  if (part >= nparts) return;  // whole workgroup
+  const int start = part * kTile, stride = nparts * kTile, end = L;
+
+  // this wavefront's rows: i = r * Hq + h
+  int lvis[NT];
+  bool rvalid[NT];
+  long qoff[NT], wrow[NT];
+  bool any_row = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int i = (rg * kMlaWaves + wave) * 16 * NT + nt * 16 + col;
+    rvalid[nt] = i < R;
+    const int r = rvalid[nt] ? i / p.Hq : 0;
+    const int h = rvalid[nt] ? i % p.Hq : 0;
+    lvis[nt] = rvalid[nt] ? L - p.n_q + r + 1 : L;
+    qoff[nt] = (((long)b * p.n_q + r) * p.Hq + h) * DK;
+    wrow[nt] = ((long)b * p.Hq + h) * p.n_q + r;
+    any_row |= rvalid[nt];
+  }
+  const bool active = __any(any_row);  // wave-uniform: this wavefront has rows
+
+  bf16x8_t qf[NT][KK];
+  const uint16_t* qbase = (const uint16_t*)p.q;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (rvalid[nt]) w = *reinterpret_cast<const uint4*>(qbase + qoff[nt] + kk * 32 + grp * 8);
+      qf[nt][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+
+  f32x4_t oacc[NT][DT];
+  float m[NT], l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // The block ids of the partition's tiles, staged in LDS once: read from
+  // global memory inside the loop they would be the newest load in flight,
+  // and waiting for one would wait for every tile load behind it.
+  const int n_tiles = (end - start + stride - 1) / stride;  // <= kMlaMaxTiles (plan)
+  const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  __shared__ int s_blk[kMlaMaxTiles];
+  if (p.table != nullptr) {
+    for (int n = tid; n < n_tiles; n += kMlaThreads)
+      s_blk[n] = p.table[(long)b * p.max_blocks + ((start + n * stride) >> bs_shift)];
+  }
+  __syncthreads();
+  auto tile_base = [&](int n) -> long {  // element offset of tile n's first key; -1: bad block
+    const int tile = start + n * stride;
+    if (p.table == nullptr) return ((long)b * p.S_max + tile) * DK;
+    const int blk = s_blk[n];
+    if (blk < 0 || blk >= p.N) return -1;
+    return ((long)blk * p.bs + (tile & (p.bs - 1))) * DK;
+  };
+  uint4 stage[PF][PER];  // ring of register stages
+  long stb[PF];          // tile base of each stage (-1: none or bad block)
+  // Every stage issues exactly PER loads, whatever the tile (past the end of
+  // the partition, a bad block, threads beyond the tile's chunks): addresses
+  // are clamped to valid rows instead of branching, so the compiler can wait
+  // for one stage's loads alone and the ring keeps PF - 1 tiles in flight.
+  auto fetch = [&](uint4 (&st)[PER], long& tbs, int n) {
+    const int tile = start + n * stride;
+    const bool in = tile < end;
+    const long tb = tile_base(in ? n : 0);
+    tbs = in ? tb : -1;
+    const uint16_t* base = (const uint16_t*)p.k + (tb >= 0 ? tb : 0);
+    const int last = in ? min(kTile, end - tile) - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      // past the end (or a bad block) every thread reads the cache's first 16
+      // bytes: one cache line, so the padding steps cost no HBM traffic
+      const int idx = tbs >= 0 ? min(u * kMlaThreads + tid, TCH - 1) : 0;
+      const int row = min(idx / CPR, last);  // masked keys re-read a visible row
+      st[u] = load_stream(base + row * DK + (idx % CPR) * 8);
+    }
+  };
+  auto store_tile = [&](const uint4 (&st)[PER]) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = u * kMlaThreads + tid;
+      if (idx < TCH)
+        *reinterpret_cast<uint4*>(lds + (idx / CPR) * ROWB + (idx % CPR) * 16) = st[u];
+    }
+  };
+  // tile n of the partition is start + n * stride; it lives in stage n % PF
+  const uint8_t* ka_ptr = lds + col * ROWB + grp * 16;
+  const uint8_t* va_ptr = lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+  constexpr float kLazy = 8.f;
+
+  // A wavefront runs alone on its SIMD, so nothing hides LDS latency but its
+  // own batching: all K fragments of the tile are read before the score
+  // products, and value fragments come in groups of 8, each group issued
+  // while the previous group's products run (sched_barrier keeps the
+  // scheduler from interleaving them back one by one).
+  auto compute = [&](int tile) {
+    bf16x8_t pb[NT];
+    bf16x8_t kf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};  // two chains
+#pragma unroll
+      for (int kk = 0; kk < KK; kk += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[nt][kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk + 1], qf[nt][kk + 1], s1, 0, 0, 0);
+      }
+      const f32x4_t s = s0 + s1;
+      const int key0 = tile + grp * 4;
+      float sv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool move = mx > m[nt] + kLazy;
+      if (__any(move)) {
+        const float m_new = move ? mx : m[nt];
+        const float alpha = m[nt] == -INFINITY ? 0.f : fast_exp2(m[nt] - m_new);
+        l[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha;
+        m[nt] = m_new;
+      }
+      const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
+      const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+      const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+      l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+      const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+      const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+      const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+      pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                       __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    constexpr int VG = 8;  // value fragments per group
+    auto read_v = [&](bf16x4_t (&va)[VG], int g) {
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+            (__attribute__((address_space(3))) uint8_t*)(va_ptr + (g * VG + i) * 32));
+        va[i] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+      }
+    };
+    bf16x4_t vcur[VG], vnext[VG];
+    read_v(vcur, 0);
+#pragma unroll
+    for (int g = 0; g < DT / VG; ++g) {
+      if (g + 1 < DT / VG) read_v(vnext, g + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const bf16x8_t va2 = __builtin_shufflevector(vcur[i], vcur[i], 0, 1, 2, 3, 0, 1, 2, 3);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          oacc[nt][g * VG + i] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[nt], oacc[nt][g * VG + i], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < VG; ++i) vcur[i] = vnext[i];
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fetch(stage[j], stb[j], j);
+  store_tile(stage[0]);
+  __syncthreads();
+  for (int n0 = 0; n0 < n_tiles; n0 += PF) {
+    // The body is the same on every path (fetch, barrier, store, barrier),
+    // only the compute depends on n: a store skipped on one path would leave
+    // its stage's loads pending at the loop's back edge, and the compiler
+    // would then drain every load in flight at the top of each iteration.
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {  // tile n = n0 + j: in LDS, from stage j
+      const int n = n0 + j;
+      const long tb = stb[j];
+      fetch(stage[j], stb[j], n + PF);  // stage j is free again: PF tiles ahead
+      if (n < n_tiles) {
+        if (tb >= 0) {
+          if (active) compute(start + n * stride);
+        } else if (tid == 0) {
+          report(p.status, KVC_ERR_DATA);
+        }
+      }
+      __syncthreads();  // every wavefront is done reading the tile
+      store_tile(stage[(j + 1) % PF]);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float lt = l[nt] + __shfl_xor(l[nt], 16);
+    lt += __shfl_xor(lt, 32);
+    if (!rvalid[nt]) continue;
+    float* wo = p.ws_o + (wrow[nt] * p.max_parts + part) * DV;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(wo + dt * 16 + grp * 4) = oacc[nt][dt];
+    if (grp == 0) {
+      float* wml = p.ws_ml + (wrow[nt] * p.max_parts + part) * 2;
+      wml[0] = m[nt];
+      wml[1] = lt;
+    }
+  }
+}
+
+hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s) {
+  const int R = p.Hq * p.n_q;
+  const long n_rg = (R + 16 * kMlaWaves - 1) / (16 * kMlaWaves);
+  const long units = (long)p.B * p.max_parts;
+  const long n_wg = (units + 7) / 8 * 8 * n_rg;
+  if (units == 0) return hipSuccess;
+  if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((partition_mla<2>), dim3((unsigned)n_wg), dim3(kMlaThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

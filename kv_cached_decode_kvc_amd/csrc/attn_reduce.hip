@@ -35,7 +35,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
     // Round trip 1: every lane fetches one partition's (m, l) and, independently,
     // the first kEarly partitions' outputs for its columns.
-    constexpr int kEarly = 16;
+    constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
     float early[kEarly][CPL];
 #pragma unroll
     for (int j = 0; j < kEarly; ++j)
@@ -103,7 +103,10 @@ hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kWave);
   const bool bf = out_dtype == KVC_BF16;
-  if (p.D == 128) {
+  if (p.D == 512) {  // MLA: weighted latents
+    if (bf) hipLaunchKernelGGL((reduce_kernel<512, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((reduce_kernel<512, false>), grid, block, 0, s, p);
+  } else if (p.D == 128) {
     if (bf) hipLaunchKernelGGL((reduce_kernel<128, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((reduce_kernel<128, false>), grid, block, 0, s, p);
   } else {

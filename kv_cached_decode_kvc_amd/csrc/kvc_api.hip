@@ -14,7 +14,10 @@ int check_desc(const kvc_cache_desc* d) {
   if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0) return KVC_ERR_SHAPE;
   if (d->batch >= kMaxBatch) return KVC_ERR_UNSUPPORTED;  // one grid row per sequence
   if (d->num_q_heads % d->num_kv_heads != 0) return KVC_ERR_SHAPE;
-  if (d->head_dim != 64 && d->head_dim != 128) return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != kMlaKeyDim)
+    return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim == kMlaKeyDim && (d->dtype != KVC_BF16 || d->num_kv_heads != 1))
+    return KVC_ERR_UNSUPPORTED;  // MLA latent caches: one bf16 head of 576
   if (d->dtype < KVC_BF16 || d->dtype > KVC_FP8_E5M2) return KVC_ERR_UNSUPPORTED;
   if (d->block_size < 0) return KVC_ERR_SHAPE;
   if (d->block_size == 0) {
@@ -97,12 +100,47 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
+// MLA latent decode: one bf16 latent head of 576 (512 latent + 64 RoPE key),
+// values = the 512-wide latent.  A workgroup of four wavefronts covers 64 query
+// rows and fills a CU, so a round of resident work is 256 workgroups; the
+// partition length follows the same rule as make_plan with that round.
+int check_mla(const kvc_cache_desc* d, int n_q, int value_dim) {
+  const int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->head_dim != kMlaKeyDim || value_dim != kMlaValueDim) return KVC_ERR_UNSUPPORTED;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->partition_tokens > 16384) return KVC_ERR_UNSUPPORTED;  // the kernel stages <= 1024 tiles
+  return KVC_OK;
+}
+
+Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
+  Plan pl{};
+  const long n_rg = ((long)d->num_q_heads * n_q + 63) / 64;
+  const long units = (long)d->batch * n_rg;
+  const int cap = capacity(d);
+  if (d->partition_tokens > 0) {
+    pl.P = d->partition_tokens;
+  } else {
+    const long one_round = 256;
+    pl.P = 256;
+    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 2 * one_round) pl.P += 256;
+    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
+  }
+  pl.max_parts = (cap + pl.P - 1) / pl.P;
+  const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
+  const size_t o_bytes = rows * pl.max_parts * kMlaValueDim * sizeof(float);
+  pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
+  pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
+  return pl;
+}
+
 int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, const void* v,
                const int32_t* seq_lens, const int32_t* table, float scale, const void* ws,
                size_t ws_bytes) {
   int st = check_desc(d);
   if (st != KVC_OK) return st;
   if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // the kvc_mla_* calls
   if (d->batch == 0) return KVC_OK;
   if (!q || !k || !v || !seq_lens || !ws) return KVC_ERR_ARG;
   if ((d->block_size > 0) != (table != nullptr)) return KVC_ERR_ARG;
@@ -186,9 +224,11 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
   if (st != KVC_OK) return st;
   if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
   if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
-  if (!seq_lens || !cu_new || !k_cache || !v_cache || !seq_lens_out) return KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !k_cache || !seq_lens_out) return KVC_ERR_ARG;
+  if ((v_cache == nullptr) != (v_new == nullptr)) return KVC_ERR_ARG;  // both NULL: keys only
+  if (!v_cache && fp8_format(d)) return KVC_ERR_UNSUPPORTED;
   if (seq_lens_out == seq_lens) return KVC_ERR_ARG;
-  if (total_new > 0 && (!k_new || !v_new)) return KVC_ERR_ARG;
+  if (total_new > 0 && !k_new) return KVC_ERR_ARG;
   if (d->block_size > 0 && total_new > 0 && !slot_mapping) return KVC_ERR_ARG;
   if (d->block_size == 0 && slot_mapping) return KVC_ERR_ARG;
   AppendArgs a{};
@@ -238,6 +278,7 @@ int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_len
   int st = check_desc(d);
   if (st != KVC_OK) return st;
   if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // kvc_mla_attn_reduce
   if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (d->batch == 0) return KVC_OK;
   if (!seq_lens || !workspace || !out) return KVC_ERR_ARG;
@@ -346,7 +387,7 @@ int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* 
   if (d->block_size == 0) return KVC_ERR_ARG;
   if (n < 0 || n >= kMaxBatch) return KVC_ERR_ARG;
   if (n == 0) return KVC_OK;
-  if (!src || !dst || !k_cache || !v_cache) return KVC_ERR_ARG;
+  if (!src || !dst || !k_cache) return KVC_ERR_ARG;  // v_cache NULL: a key-only pool
   CopyArgs c{};
   c.src = src;
   c.dst = dst;
@@ -372,7 +413,7 @@ int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_
   if (d->num_blocks > kMaxPoolBlocks) return KVC_ERR_UNSUPPORTED;
   if (d->batch == 0) return KVC_OK;
   if (!seq_lens || !cu_new || !block_table || !free_list || !free_head_in || !free_head_out ||
-      !ref_counts || !k_cache || !v_cache || !cow_src || !cow_dst)
+      !ref_counts || !k_cache || !cow_src || !cow_dst)
     return KVC_ERR_ARG;
   LifecycleArgs a{};
   a.seq_lens = seq_lens;
@@ -392,6 +433,78 @@ int kvc_cow(const kvc_cache_desc* d, const int32_t* seq_lens, const int32_t* cu_
   hipError_t e = launch_cow(a, (hipStream_t)stream);
   if (e != hipSuccess) return KVC_ERR_HIP;
   return kvc_copy_blocks(d, cow_src, cow_dst, d->batch, k_cache, v_cache, dev_status, stream);
+}
+
+size_t kvc_mla_workspace_bytes(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim) {
+  if (check_mla(d, n_q, value_dim) != KVC_OK) return 0;
+  return make_mla_plan(d, n_q).bytes;
+}
+
+int32_t kvc_mla_partition_tokens(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim) {
+  const int st = check_mla(d, n_q, value_dim);
+  return st != KVC_OK ? st : make_mla_plan(d, n_q).P;
+}
+
+int kvc_mla_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q,
+                           const void* latent_cache, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t value_dim, float scale,
+                           void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                           void* stream) {
+  int st = check_mla(d, n_q, value_dim);
+  if (st != KVC_OK) return st;
+  if (d->batch == 0) return KVC_OK;
+  if (!q || !latent_cache || !seq_lens || !workspace) return KVC_ERR_ARG;
+  if ((d->block_size > 0) != (block_table != nullptr)) return KVC_ERR_ARG;
+  if (!isfinite(scale)) return KVC_ERR_ARG;
+  if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
+  const Plan pl = make_mla_plan(d, n_q);
+  if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
+  const AttnParams p = attn_params(d, pl, n_q, q, latent_cache, latent_cache, seq_lens,
+                                   block_table, scale, workspace, dev_status);
+  return hip_status(launch_partition_mla(p, (hipStream_t)stream));
+}
+
+int kvc_mla_attn_reduce(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim,
+                        const int32_t* seq_lens, const void* workspace, size_t workspace_bytes,
+                        void* out, int32_t out_dtype, int32_t* dev_status, void* stream) {
+  int st = check_mla(d, n_q, value_dim);
+  if (st != KVC_OK) return st;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!seq_lens || !workspace || !out) return KVC_ERR_ARG;
+  if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
+  const Plan pl = make_mla_plan(d, n_q);
+  if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
+  ReduceParams p{};
+  p.ws_o = (const float*)workspace;
+  p.ws_ml = (const float*)((const char*)workspace + pl.ml_offset);
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.status = dev_status;
+  p.B = d->batch;
+  p.n_q = n_q;
+  p.Hq = d->num_q_heads;
+  p.D = kMlaValueDim;
+  p.P = pl.P;
+  p.max_parts = pl.max_parts;
+  p.cap = capacity(d);
+  return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
+}
+
+int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* latent_cache,
+                 const int32_t* seq_lens, const int32_t* block_table, int32_t value_dim,
+                 float scale, void* out, int32_t out_dtype, void* workspace,
+                 size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  int st = check_mla(d, n_q, value_dim);
+  if (st != KVC_OK) return st;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!out) return KVC_ERR_ARG;
+  st = kvc_mla_attn_partition(d, q, n_q, latent_cache, seq_lens, block_table, value_dim, scale,
+                              workspace, workspace_bytes, dev_status, stream);
+  if (st != KVC_OK) return st;
+  return kvc_mla_attn_reduce(d, n_q, value_dim, seq_lens, workspace, workspace_bytes, out,
+                             out_dtype, dev_status, stream);
 }
 
 size_t kvc_cache_bytes(const kvc_cache_desc* d) {

@@ -77,7 +77,11 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s);
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)
+constexpr int kMlaKeyDim = 576;    // MLA cache row: latent (512) + decoupled RoPE key (64)
+constexpr int kMlaValueDim = 512;  // the latent part, which also serves as the value
+
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s);
+hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s);
 hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, int fp8, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s);
 

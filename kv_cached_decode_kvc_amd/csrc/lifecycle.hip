@@ -252,15 +252,19 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
   if (off < a.scale_bytes) {  // FP8 pools: the block's per-row scales travel with it
     const long so = a.scale_off + off;
     const uint4 ks = *reinterpret_cast<const uint4*>(a.k + so + (long)src * a.scale_bytes);
-    const uint4 vs = *reinterpret_cast<const uint4*>(a.v + so + (long)src * a.scale_bytes);
     *reinterpret_cast<uint4*>(a.k + so + (long)dst * a.scale_bytes) = ks;
-    *reinterpret_cast<uint4*>(a.v + so + (long)dst * a.scale_bytes) = vs;
+    if (a.v) {
+      const uint4 vs = *reinterpret_cast<const uint4*>(a.v + so + (long)src * a.scale_bytes);
+      *reinterpret_cast<uint4*>(a.v + so + (long)dst * a.scale_bytes) = vs;
+    }
   }
   if (off >= a.block_bytes) return;
   const uint4 kv = *reinterpret_cast<const uint4*>(a.k + (long)src * a.block_bytes + off);
-  const uint4 vv = *reinterpret_cast<const uint4*>(a.v + (long)src * a.block_bytes + off);
   *reinterpret_cast<uint4*>(a.k + (long)dst * a.block_bytes + off) = kv;
-  *reinterpret_cast<uint4*>(a.v + (long)dst * a.block_bytes + off) = vv;
+  if (a.v) {  // NULL: a key-only (MLA latent) pool
+    const uint4 vv = *reinterpret_cast<const uint4*>(a.v + (long)src * a.block_bytes + off);
+    *reinterpret_cast<uint4*>(a.v + (long)dst * a.block_bytes + off) = vv;
+  }
 }
 
 hipError_t launch_fork(const LifecycleArgs& a, hipStream_t s) {

@@ -193,9 +193,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     }
     const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
     const uint4 kv = *reinterpret_cast<const uint4*>(a.k_new + src);
-    const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
     *reinterpret_cast<uint4*>(a.k_cache + dst) = kv;
-    *reinterpret_cast<uint4*>(a.v_cache + dst) = vv;
+    if (a.v_cache) {  // NULL: a key-only cache (MLA latent rows serve as keys and values)
+      const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
+      *reinterpret_cast<uint4*>(a.v_cache + dst) = vv;
+    }
   }
 }
 

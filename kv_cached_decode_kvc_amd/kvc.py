@@ -26,7 +26,9 @@ STATUS_NAMES = {0: "KVC_OK", -1: "KVC_ERR_ARG", -2: "KVC_ERR_SHAPE", -3: "KVC_ER
 EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn",
            "kvc_attn_partition", "kvc_attn_reduce", "kvc_attn_workspace_bytes",
            "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
-           "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_status_string")
+           "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_mla_workspace_bytes",
+           "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
+           "kvc_mla_attn", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -78,6 +80,17 @@ def lib() -> ctypes.CDLL:
             getattr(L, n).restype = ctypes.c_int
         L.kvc_attn_workspace_bytes.argtypes = [D, I]
         L.kvc_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.kvc_mla_workspace_bytes.argtypes = [D, I, I]
+        L.kvc_mla_workspace_bytes.restype = ctypes.c_size_t
+        L.kvc_mla_partition_tokens.argtypes = [D, I, I]
+        L.kvc_mla_partition_tokens.restype = ctypes.c_int32
+        L.kvc_mla_attn_partition.argtypes = [D, P, I, P, P, P, I, ctypes.c_float, P,
+                                             ctypes.c_size_t, P, P]
+        L.kvc_mla_attn_reduce.argtypes = [D, I, I, P, P, ctypes.c_size_t, P, I, P, P]
+        L.kvc_mla_attn.argtypes = [D, P, I, P, P, P, I, ctypes.c_float, P, I, P, ctypes.c_size_t,
+                                   P, P]
+        for n in ("kvc_mla_attn_partition", "kvc_mla_attn_reduce", "kvc_mla_attn"):
+            getattr(L, n).restype = ctypes.c_int
         L.kvc_cache_bytes.argtypes = [D]
         L.kvc_cache_bytes.restype = ctypes.c_size_t
         L.kvc_attn_partition_tokens.argtypes = [D, I]
@@ -227,6 +240,42 @@ def kvc_attn_workspace_bytes(desc, n_q) -> int:
 
 def kvc_attn_partition_tokens(desc, n_q) -> int:
     return int(lib().kvc_attn_partition_tokens(ctypes.byref(desc), int(n_q)))
+
+
+def kvc_mla_workspace_bytes(desc, n_q, value_dim) -> int:
+    return int(lib().kvc_mla_workspace_bytes(ctypes.byref(desc), int(n_q), int(value_dim)))
+
+
+def kvc_mla_partition_tokens(desc, n_q, value_dim) -> int:
+    return int(lib().kvc_mla_partition_tokens(ctypes.byref(desc), int(n_q), int(value_dim)))
+
+
+def kvc_mla_attn_partition(desc, q, n_q, latent_cache, seq_lens, block_table, value_dim, scale,
+                           workspace, dev_status=None, stream=None):
+    _check("kvc_mla_attn_partition", lib().kvc_mla_attn_partition(
+        ctypes.byref(desc), _ptr(q, "q"), int(n_q), _ptr(latent_cache, "latent_cache"),
+        _ptr(seq_lens, "seq_lens", I32), _ptr(block_table, "block_table", I32), int(value_dim),
+        float(scale), _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", I32), _stream(stream)))
+
+
+def kvc_mla_attn_reduce(desc, n_q, value_dim, seq_lens, workspace, out, dev_status=None,
+                        stream=None, out_dtype=None):
+    _check("kvc_mla_attn_reduce", lib().kvc_mla_attn_reduce(
+        ctypes.byref(desc), int(n_q), int(value_dim), _ptr(seq_lens, "seq_lens", I32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out"), _out_dtype(out, out_dtype), _ptr(dev_status, "dev_status", I32),
+        _stream(stream)))
+
+
+def kvc_mla_attn(desc, q, n_q, latent_cache, seq_lens, block_table, value_dim, scale, out,
+                 workspace, dev_status=None, stream=None, out_dtype=None):
+    _check("kvc_mla_attn", lib().kvc_mla_attn(
+        ctypes.byref(desc), _ptr(q, "q"), int(n_q), _ptr(latent_cache, "latent_cache"),
+        _ptr(seq_lens, "seq_lens", I32), _ptr(block_table, "block_table", I32), int(value_dim),
+        float(scale), _ptr(out, "out"), _out_dtype(out, out_dtype), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(dev_status, "dev_status", I32),
+        _stream(stream)))
 
 
 def kvc_cache_bytes(desc) -> int:

@@ -26,11 +26,12 @@ def attended_kv_bytes(seq_lens, n_kv_heads: int, head_dim: int, bytes_per_value:
         1, n_kv_heads, head_dim, bytes_per_value)
 
 
-def attended_cache_bytes(seq_lens, n_kv_heads: int, row_bytes: int) -> int:
-    """K and V cache bytes one attention call reads, for any cache format:
-    every attended row (token, KV head) of K and of V once, `row_bytes` each
-    (FP8: codes plus the row's scale)."""
-    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * n_kv_heads * 2 * row_bytes
+def attended_cache_bytes(seq_lens, n_kv_heads: int, row_bytes: int, tensors: int = 2) -> int:
+    """Cache bytes one attention call reads, for any cache format: every
+    attended row (token, KV head) of each cache tensor once, `row_bytes` each
+    (FP8: codes plus the row's scale).  tensors = 2 for K and V, 1 for an MLA
+    latent cache whose rows serve as both."""
+    return int(np.asarray(seq_lens, dtype=np.int64).sum()) * n_kv_heads * tensors * row_bytes
 
 
 def attention_flops(seq_lens, n_q: int, n_q_heads: int, head_dim: int) -> int:

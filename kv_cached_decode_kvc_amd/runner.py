@@ -78,7 +78,8 @@ class LayerCache:
                 self.v.fill_(0x7F)
         else:
             self.k = torch.full(shape, fill, dtype=tdt, device=dev)
-            self.v = torch.full(shape, fill, dtype=tdt, device=dev)
+            # MLA: one latent cache whose rows serve as keys and values
+            self.v = None if w.dv else torch.full(shape, fill, dtype=tdt, device=dev)
         self.seq_lens = torch.zeros(w.B, dtype=torch.int32, device=dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.n_q = w.n_q
@@ -109,7 +110,8 @@ class LayerCache:
                                 self.head, self.head, slots, self.status)
         out = torch.empty_like(self.seq_lens)
         kvc.kvc_append(self.desc, to_dev(k_rows, w.dtype, self.dev),
-                       to_dev(v_rows, w.dtype, self.dev), self.seq_lens, cu_d, total,
+                       None if v_rows is None else to_dev(v_rows, w.dtype, self.dev),
+                       self.seq_lens, cu_d, total,
                        int(counts.max()) if len(counts) else 0, slots, self.k, self.v, out,
                        self.status)
         self.seq_lens = out
@@ -119,25 +121,33 @@ class LayerCache:
         """The cached rows of every sequence (the generator's stream of cached keys/values)."""
         w = self.w
         return self.add_tokens(synth.packed_cache_rows(w, "k", lengths),
-                               synth.packed_cache_rows(w, "v", lengths), lengths)
+                               None if w.dv else synth.packed_cache_rows(w, "v", lengths),
+                               lengths)
 
     def step_rows(self, step=0):
         w = self.w
         return self.add_tokens(synth.packed_new_rows(w, "k", step),
-                               synth.packed_new_rows(w, "v", step), [w.n_q] * w.B)
+                               None if w.dv else synth.packed_new_rows(w, "v", step),
+                               [w.n_q] * w.B)
 
     def workspace(self, n_q):
-        nbytes = kvc.kvc_attn_workspace_bytes(self.desc, n_q)
+        if self.w.dv:
+            nbytes = kvc.kvc_mla_workspace_bytes(self.desc, n_q, self.w.dv)
+        else:
+            nbytes = kvc.kvc_attn_workspace_bytes(self.desc, n_q)
         return torch.empty(max((nbytes + 3) // 4, 4), dtype=torch.float32, device=self.dev)
 
     def attend(self, q: torch.Tensor, n_q: int, out_dtype=torch.float32, scale=None,
                seq_lens=None) -> torch.Tensor:
         w = self.w
         scale = self.scale if scale is None else scale
-        out = torch.empty((w.B, n_q, w.Hq, w.D), dtype=out_dtype, device=self.dev)
+        out = torch.empty((w.B, n_q, w.Hq, w.out_dim), dtype=out_dtype, device=self.dev)
         ws = self.workspace(n_q)
         sl = self.seq_lens if seq_lens is None else seq_lens
-        if n_q == 1:
+        if w.dv:
+            kvc.kvc_mla_attn(self.desc, q, n_q, self.k, sl, self.table, w.dv, scale, out, ws,
+                             self.status)
+        elif n_q == 1:
             kvc.kvc_decode_attn(self.desc, q, self.k, self.v, sl, self.table, scale, out, ws,
                                 self.status)
         else:
@@ -159,9 +169,11 @@ class LayerCache:
         self.s_cu = i32(synth.cu_from_counts([w.n_q] * w.B), self.dev)
         self.s_total = w.n_q * w.B
         self.s_k = to_dev(synth.packed_new_rows(w, "k", step), w.dtype, self.dev)
-        self.s_v = to_dev(synth.packed_new_rows(w, "v", step), w.dtype, self.dev)
+        self.s_v = None if w.dv else to_dev(synth.packed_new_rows(w, "v", step), w.dtype,
+                                              self.dev)
         self.s_q = to_dev(synth.packed_queries(w, step), w.dtype, self.dev)
-        self.s_out = torch.empty((w.B, w.n_q, w.Hq, w.D), dtype=torch.float32, device=self.dev)
+        self.s_out = torch.empty((w.B, w.n_q, w.Hq, w.out_dim), dtype=torch.float32,
+                                 device=self.dev)
         self.s_ws = self.workspace(w.n_q)
         if self.bs:
             self.s_head0 = self.head.clone()  # free-list head before the step: never written
@@ -179,12 +191,25 @@ class LayerCache:
         kvc.kvc_append(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu, self.s_total,
                        self.w.n_q, self.s_slots, self.k, self.v, self.s_len1, self.status)
 
+    def partition(self, q, n_q, lens, ws):
+        if self.w.dv:
+            kvc.kvc_mla_attn_partition(self.desc, q, n_q, self.k, lens, self.table, self.w.dv,
+                                       self.scale, ws, self.status)
+        else:
+            kvc.kvc_attn_partition(self.desc, q, n_q, self.k, self.v, lens, self.table,
+                                   self.scale, ws, self.status)
+
+    def reduce(self, n_q, lens, ws, out):
+        if self.w.dv:
+            kvc.kvc_mla_attn_reduce(self.desc, n_q, self.w.dv, lens, ws, out, self.status)
+        else:
+            kvc.kvc_attn_reduce(self.desc, n_q, lens, ws, out, self.status)
+
     def step_partition(self):
-        kvc.kvc_attn_partition(self.desc, self.s_q, self.w.n_q, self.k, self.v, self.s_len1,
-                               self.table, self.scale, self.s_ws, self.status)
+        self.partition(self.s_q, self.w.n_q, self.s_len1, self.s_ws)
 
     def step_reduce(self):
-        kvc.kvc_attn_reduce(self.desc, self.w.n_q, self.s_len1, self.s_ws, self.s_out, self.status)
+        self.reduce(self.w.n_q, self.s_len1, self.s_ws, self.s_out)
 
     def step(self):
         self.step_front()
@@ -205,9 +230,11 @@ class DecodeLoop:
         self.lc, self.w, self.S = lc, w, w.steps
         self.lens = [lc.seq_lens.clone()] + [torch.empty_like(lc.seq_lens) for _ in range(w.steps)]
         self.k = [to_dev(synth.packed_new_rows(w, "k", s), w.dtype, dev) for s in range(w.steps)]
-        self.v = [to_dev(synth.packed_new_rows(w, "v", s), w.dtype, dev) for s in range(w.steps)]
+        self.v = [None if w.dv else to_dev(synth.packed_new_rows(w, "v", s), w.dtype, dev)
+                  for s in range(w.steps)]
         self.q = [to_dev(synth.packed_queries(w, s), w.dtype, dev) for s in range(w.steps)]
-        self.out = torch.empty((w.steps, w.B, w.n_q, w.Hq, w.D), dtype=torch.float32, device=dev)
+        self.out = torch.empty((w.steps, w.B, w.n_q, w.Hq, w.out_dim), dtype=torch.float32,
+                               device=dev)
         self.cu = i32(synth.cu_from_counts([w.n_q] * w.B), dev)
         self.total = w.n_q * w.B
         self.ws = lc.workspace(w.n_q)
@@ -227,9 +254,8 @@ class DecodeLoop:
                                     lc.status)
             kvc.kvc_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total, w.n_q,
                            slots, lc.k, lc.v, self.lens[s + 1], lc.status)
-            kvc.kvc_attn_partition(lc.desc, self.q[s], w.n_q, lc.k, lc.v, self.lens[s + 1],
-                                   lc.table, lc.scale, self.ws, lc.status)
-            kvc.kvc_attn_reduce(lc.desc, w.n_q, self.lens[s + 1], self.ws, self.out[s], lc.status)
+            lc.partition(self.q[s], w.n_q, self.lens[s + 1], self.ws)
+            lc.reduce(w.n_q, self.lens[s + 1], self.ws, self.out[s])
         return self.out
 
     def capture(self):

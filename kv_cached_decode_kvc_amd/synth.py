@@ -39,6 +39,7 @@ class Workload:
     steps: int = 1  # successive decode steps (the cache grows by n_q each step)
     description: str = ""
     kv: str = ""  # "": the cache holds dtype; "e4m3" / "e5m2": FP8 codes + a scale per row
+    dv: int = 0   # MLA: value dims of a latent row (its leading dims); 0 = separate K and V
 
     @property
     def esize(self) -> int:
@@ -47,6 +48,15 @@ class Workload:
     @property
     def cache_dtype(self) -> str:
         return "fp8_" + self.kv if self.kv else self.dtype
+
+    @property
+    def kv_tensors(self) -> int:
+        """Cache tensors read per attended row: K and V, or one latent row (MLA)."""
+        return 1 if self.dv else 2
+
+    @property
+    def out_dim(self) -> int:
+        return self.dv or self.D
 
     @property
     def kv_row_bytes(self) -> int:
@@ -83,6 +93,23 @@ WORKLOADS = {w.name: w for w in [
 
 # short aliases, in the order the workloads are listed above
 ALIASES = {"C%d" % (i + 1): n for i, n in enumerate(WORKLOADS)}
+
+# MLA latent decode (DeepSeek-V2/V3 geometry: latent 512 + RoPE key 64, one
+# latent head shared by all query heads, block 64): all 128 heads on one GPU,
+# and the 16 heads of one GPU when the heads are split 8 ways.
+for _w in [
+    Workload("mla-h128-paged64-b32-ctx1024to4096", seed=7, B=32, Hq=128, Hkv=1, D=576,
+             dtype="bf16", block_size=64, n_q=1, len_lo=1024, len_hi=4096,
+             description="MLA latent decode, 128 heads on one latent head of 576 (512 + 64 "
+                         "RoPE), paged block 64, batch 32, lengths U[1024, 4096]", dv=512),
+    Workload("mla-h16-paged64-b128-ctx1024to8192", seed=8, B=128, Hq=16, Hkv=1, D=576,
+             dtype="bf16", block_size=64, n_q=1, len_lo=1024, len_hi=8192,
+             description="MLA latent decode, 16 heads (128 split 8 ways), paged block 64, "
+                         "batch 128, lengths U[1024, 8192]", dv=512),
+]:
+    WORKLOADS[_w.name] = _w
+ALIASES["M1"], ALIASES["M2"] = ("mla-h128-paged64-b32-ctx1024to4096",
+                                "mla-h16-paged64-b128-ctx1024to8192")
 
 # The same four full-size workloads over an FP8 (E4M3) cache: same seeds, so the
 # same lengths and rows, quantized on append.
@@ -210,7 +237,7 @@ def packed_queries(w: Workload, step: int = 0) -> np.ndarray:
 
 
 def custom(name="custom", seed=0, B=2, Hq=4, Hkv=4, D=64, dtype="bf16", block_size=0, n_q=1,
-           len_lo=16, len_hi=16, steps=1, kv="") -> Workload:
+           len_lo=16, len_hi=16, steps=1, kv="", dv=0) -> Workload:
     """A small workload for tests (same generators, other sizes)."""
     return Workload(name, seed, B, Hq, Hkv, D, dtype, block_size, n_q, len_lo, len_hi, steps,
-                    kv=kv)
+                    kv=kv, dv=dv)

@@ -41,6 +41,8 @@ def logical_rows(w, b, which, cached_len, steps=1):
 def oracle_attention(ref, w, q, k, v, scale):
     """The oracle's attention over generator rows; an FP8 cache holds the
     oracle's own quantization of those rows (dequantized exactly)."""
+    if w.dv:  # MLA: one latent head whose rows are keys; values = their first dv dims
+        return ref.mla_attention(q, k[0], scale, w.dv)
     if not w.kv:
         return ref.attention(q, k, v, scale, w.dtype)
     kd = ref.dequantize_rows(*ref.quantize_rows(k, w.kv), w.kv)
@@ -48,15 +50,15 @@ def oracle_attention(ref, w, q, k, v, scale):
     return ref.attention(oracle.widen(q, "bf16"), kd, vd, scale, "f64")
 
 
-def oracle_outputs(ref, w, b_list, cached, steps=1, step_q=None):
+def oracle_outputs(ref, w, b_list, cached, steps=1, step_q=None, scale=None):
     """Oracle attention (float64) of the given sequences at the last step, from
-    generator rows only: {b: [n_q, Hq, D]}."""
-    scale = 1.0 / math.sqrt(w.D)
+    generator rows only: {b: [n_q, Hq, out_dim]}."""
+    scale = 1.0 / math.sqrt(w.D) if scale is None else scale
     s = steps - 1 if step_q is None else step_q
     out = {}
     for b in b_list:
         k = logical_rows(w, b, "k", int(cached[b]), steps)
-        v = logical_rows(w, b, "v", int(cached[b]), steps)
+        v = None if w.dv else logical_rows(w, b, "v", int(cached[b]), steps)
         out[b] = oracle_attention(ref, w, synth.queries(w, b, s), k, v, scale)
     return out
 

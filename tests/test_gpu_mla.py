@@ -1,0 +1,119 @@
+"""GPU parity of MLA latent decode: attention of every head's absorbed query
+over the shared latent rows (keys = whole 576-wide rows, values = their first
+512 dims) against the oracle, for decode and verify rows, contiguous and
+paged caches; the full-size workloads are sampled."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cached_decode_kvc_amd import kvc, runner, synth
+from gpu_harness import GpuCache, assert_close, oracle_outputs, queries_dev
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(192)  # the per-head scale of the original 128 + 64 head dims
+
+# (name, Hq, n_q, block_size, B, len_hi, partition_tokens, capacity)
+CASES = [
+    ("h16-paged64", 16, 1, 64, 4, 700, 0, None),
+    ("h128-paged64-two-row-groups", 128, 1, 64, 3, 500, 0, None),
+    ("h64-contig-cap301", 64, 1, 0, 3, 300, 0, 301),
+    ("verify2-h128-paged16-four-row-groups", 128, 2, 16, 2, 400, 0, None),
+    ("verify5-h16-paged16-P32", 16, 5, 16, 3, 300, 32, None),
+    ("h8-half-wave-P16", 8, 1, 64, 3, 200, 16, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_mla_parity(ref, case):
+    name, Hq, n_q, bs, B, hi, P, cap = case
+    w = synth.custom(name=name, seed=3000 + Hq + n_q, B=B, Hq=Hq, Hkv=1, D=576, dtype="bf16",
+                     block_size=bs, n_q=n_q, len_lo=n_q, len_hi=hi, dv=512)
+    lengths = synth.final_lengths(w)
+    cached = lengths - n_q
+    gc = GpuCache(w, partition_tokens=P, block_size=bs if bs else None, capacity=cap)
+    assert gc.v is None
+    gc.prefill(cached)
+    gc.step_rows(0)
+    out = gc.attend(queries_dev(w), n_q, scale=SCALE)
+    assert gc.dev_status() == 0
+    assert out.shape == (B, n_q, Hq, 512)
+    want = oracle_outputs(ref, w, range(B), cached, scale=SCALE)
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert_close(got[b], want[b], "%s b=%d L=%d" % (name, b, int(lengths[b])))
+
+
+def test_mla_bf16_output_and_refusals(ref):
+    w = synth.custom(name="o", seed=3100, B=2, Hq=16, Hkv=1, D=576, dtype="bf16", block_size=64,
+                     n_q=1, len_lo=1, len_hi=300, dv=512)
+    lengths = synth.final_lengths(w)
+    gc = GpuCache(w, block_size=64)
+    gc.prefill(lengths - 1)
+    gc.step_rows(0)
+    out = gc.attend(queries_dev(w), 1, out_dtype=torch.bfloat16, scale=SCALE)
+    assert gc.dev_status() == 0
+    want = oracle_outputs(ref, w, range(2), lengths - 1, scale=SCALE)
+    got = out.float().cpu().numpy()
+    for b in range(2):
+        err = np.abs(got[b] - want[b])
+        assert np.all(err <= 2e-3 + 1e-2 * np.abs(want[b]) + np.abs(want[b]) * 2.0 ** -8)
+    # the ordinary attention calls refuse the latent geometry, MLA refuses others
+    ws = gc.workspace(1)
+    o2 = torch.empty((2, 1, 16, 576), dtype=torch.float32, device="cuda")
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_decode_attn(gc.desc, queries_dev(w), gc.k, gc.k, gc.seq_lens, gc.table, SCALE,
+                            o2, ws)
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_mla_attn(gc.desc, queries_dev(w), 1, gc.k, gc.seq_lens, gc.table, 448, SCALE,
+                         out, ws)
+
+
+@pytest.mark.parametrize("name", ["M1", "M2"])
+def test_mla_full_size_sampled(ref, name):
+    w = synth.get(name)
+    print("full-size MLA workload", w.name, flush=True)
+    lc = runner.build(w)
+    out1 = lc.step().clone()
+    out2 = lc.step().clone()
+    assert lc.dev_status() == 0
+    assert torch.equal(out1, out2)
+    lens = synth.final_lengths(w)
+    cached = synth.cached_lengths(w)
+    sample = sorted({0, w.B - 1, int(np.argmax(lens)), int(np.argmin(lens))})
+    want = oracle_outputs(ref, w, sample, cached)
+    got = out1.cpu().numpy()
+    for b in sample:
+        assert_close(got[b], want[b], "%s b=%d L=%d" % (name, b, lens[b]))
+    del lc
+    torch.cuda.empty_cache()
+
+
+def test_mla_graph_replay_and_key_only_copies(ref):
+    """A captured MLA decode loop (block table, key-only append, latent
+    attention) replays bit for bit; block copies on a key-only pool move the
+    latent rows."""
+    w = synth.custom(name="g", seed=3200, B=3, Hq=32, Hkv=1, D=576, dtype="bf16", block_size=64,
+                     n_q=1, len_lo=200, len_hi=400, steps=3, dv=512)  # >= 4 blocks each
+    gc = GpuCache(w, block_size=64)
+    gc.prefill(synth.cached_lengths(w))
+    loop = runner.DecodeLoop(gc)
+    eager = loop.run().clone()
+    assert gc.dev_status() == 0
+    g = loop.capture()
+    for r in range(3):
+        loop.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loop.out, eager), r
+    k0 = gc.k.clone()
+    free = int(gc.head.item())
+    blocks = gc.free_list[free:free + 2].clone()  # two unused blocks
+    kvc.kvc_copy_blocks(gc.desc, gc.table[0, :2].contiguous(), blocks, 2, gc.k, None, gc.status)
+    assert gc.dev_status() == 0
+    t0 = gc.table[0, :2].cpu().tolist()
+    for s_, d_ in zip(t0, blocks.cpu().tolist()):
+        assert torch.equal(gc.k[d_], k0[s_])
