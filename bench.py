@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV HBM GB/s (% of peak) + sequences·steps/sec at given ctx"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+PREFILL_METRIC = "prefill attention TFLOP/s (causal visible pairs x 4 x head_dim x q heads)"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kv_cached_decode_kvc_amd", "csrc")
 
@@ -35,6 +37,8 @@ def kernel_of(w, mfma: bool) -> tuple[str, list[str]]:
     """Name of the dominant kernel and the sources that define it."""
     if w.dv:
         return "partition_mla", ["attn_mla.hip", "common.hpp"]
+    if w.prefill:
+        return "prefill_mfma", ["attn_prefill.hip", "common.hpp"]
     if mfma:
         return "partition_mfma", ["attn_mfma.hip", "common.hpp"]
     return "partition_valu", ["attn_valu.hip", "common.hpp"]
@@ -539,9 +543,19 @@ def main():
         },
         "cache_flushed": flushed,
     }
+    if w.prefill:  # compute-bound: the line reports FLOP/s against the matrix-core peak
+        line["metric"] = PREFILL_METRIC
+        line["value"] = round(flops / (ms_per_step / 1e3) / 1e12, 2)
+        line["unit"] = "TFLOP/s"
+        line["tokens_per_s"] = round(w.B * w.n_q / (ms_per_step / 1e3), 1)
+        rf = line["roofline"]
+        rf.update({"bound": "mfma", "achieved": rf["achieved_tflops"],
+                   "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(rf["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "hbm_gbs": round(achieved, 2)})
     if graph is not None:
         line["graph_replay"] = graph
-    if args.no_cpu_baseline:
+    if args.no_cpu_baseline or w.prefill:  # prefill: the oracle takes minutes per sequence
         line["cpu_baseline"] = None
     else:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, gpu_out)

@@ -341,6 +341,32 @@ int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void
                  float scale, void* out, int32_t out_dtype, void* workspace,
                  size_t workspace_bytes, int32_t* dev_status, void* stream);
 
+/*
+ * kvc_prefill_attn -- causal attention of a chunk of new rows per sequence
+ * over everything cached (prefill, or one chunk of a chunked prefill).
+ *
+ * [I1] "FlashAttention": a block of queries loops over tiles of keys and
+ * values with the online softmax, never writing the score matrix, and skips
+ * the tiles above the causal diagonal.  [I1] "Chunked prefill" and [VN] 05
+ * "Chunked prefill": long prompts are processed in chunks, each over the
+ * whole cache.  Append the chunk first (kvc_block_table, kvc_append); then
+ * sequence b holds seq_lens[b] keys and its n_b = cu_q[b+1] - cu_q[b] query
+ * rows sit at positions seq_lens[b] - n_b + r: row r sees keys
+ * 0 .. seq_lens[b] - n_b + r ([I1] "KV cache": the shifted causal mask).
+ *
+ *   q        (device) [total_q][Hq][D] bf16, sequence b's rows at cu_q[b] ..
+ *   cu_q     (device) [B+1] offsets; max_q (host) >= every n_b (sizes the grid)
+ *   seq_lens (device) [B] lengths after the append, n_b <= seq_lens[b]
+ *   out      (device) [total_q][Hq][D], out_dtype bf16 or f32
+ * bf16 caches with head_dim 64 or 128 (others KVC_ERR_UNSUPPORTED); paged
+ * caches with max_blocks_per_seq <= 4096.  No workspace: each query block
+ * covers all its keys.  Bad lengths or offsets: KVC_ERR_DATA, rows skipped.
+ */
+int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q, int32_t total_q,
+                     int32_t max_q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const int32_t* block_table, float scale, void* out,
+                     int32_t out_dtype, int32_t* dev_status, void* stream);
+
 /* Bytes of one cache buffer (k_cache or v_cache) for this description: FP8
  * codes and scales, or the plain elements.  0 on an invalid description. */
 size_t kvc_cache_bytes(const kvc_cache_desc* d);

@@ -1,0 +1,279 @@
+// attn_prefill.hip -- (chunked) prefill attention over the KV cache.
+//
+// "Inference-1" (brunomaga.github.io), "FlashAttention": for a block of
+// queries, loop over tiles of keys and values, keep a running maximum, sum
+// and unnormalised output per query (online softmax) and never write the
+// score matrix; tiles entirely above the causal diagonal are skipped.
+// "Inference-1", "Chunked prefill" and "Inference o quy mo lon", 05 "Chunked
+// prefill": a long prompt is processed in chunks, each attending over
+// everything already cached.  The chunk's rows have been appended first
+// (kvc_block_table, kvc_append), so sequence b holds L_b keys and its n_b new
+// query rows sit at positions L_b - n_b + r; row r sees keys 0 .. L_b - n_b + r
+// ("Inference-1", "KV cache": the causal mask shifted by the cached length).
+//
+// A workgroup of four wavefronts owns one (sequence, KV head, block of
+// 4 * 16 * NT rows); a row is (query position, query head of the group), so
+// the grouped heads share every K/V tile ("Efficient Inference", GQA passage).
+// The threads load each 32-key tile of K and V (one contiguous run per
+// tensor) cooperatively into LDS through a two-stage register ring; each
+// wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 as in the
+// decode kernel (S^T = K.Q^T with Q^T in registers; O^T += V^T.P^T with V^T via
+// ds_read_b64_tr_b16 and the weights as bf16 hi + lo pairs) and skips the
+// tiles that lie entirely above its rows' diagonal.  Outputs are normalised
+// and written directly: there is no split over keys.
+#include "launch.hpp"
+
+namespace kvc {
+
+namespace {
+
+typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfKeys = 32;  // keys per LDS tile (two 16-key MFMA tiles)
+constexpr int kPfMaxIds = 4096;  // block ids of one sequence staged in LDS
+
+}  // namespace
+
+template <int D, int NT, bool BF16_OUT>
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
+  constexpr int KK = D / 32, DT = D / 16;
+  constexpr int CPR = D * 2 / 16;              // 16-byte chunks per row
+  constexpr int TCH = kPfKeys * CPR;           // chunks per tile and tensor
+  constexpr int PER = (TCH + kPfThreads - 1) / kPfThreads;
+  constexpr int ROWB = D * 2 + 16;
+  constexpr int PF = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPfKeys * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kPfKeys * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int q0 = p.cu_q[b], n_b = p.cu_q[b + 1] - q0;
+  const int rows_wg = kPfWaves * 16 * NT;
+  const int R = n_b * p.G;                      // rows of this (sequence, KV head)
+  const int row0 = blockIdx.x * rows_wg;
+  if (blockIdx.x == 0 && g == 0 && tid == 0 && (long)R > (long)gridDim.x * rows_wg)
+    report(p.status, KVC_ERR_DATA);  // a chunk longer than max_q: its last rows are not computed
+  if (row0 >= R) return;  // whole workgroup
+  const int L = p.seq_lens[b];
+  if (n_b < 0 || L < n_b || L > p.cap || q0 < 0 || q0 + n_b > p.total_q) {
+    if (blockIdx.x == 0 && g == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+    return;
+  }
+  const int cached = L - n_b;
+
+  int lvis[NT];
+  bool rvalid[NT];
+  long qoff[NT];
+  int wave_vis = 0;  // keys this wavefront's rows see (the largest lvis)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int i = row0 + wave * 16 * NT + nt * 16 + col;
+    rvalid[nt] = i < R;
+    const int r = rvalid[nt] ? i / p.G : 0;
+    const int h = g * p.G + (rvalid[nt] ? i % p.G : 0);
+    lvis[nt] = rvalid[nt] ? cached + r + 1 : 0;
+    qoff[nt] = ((long)(q0 + r) * p.Hq + h) * D;
+    wave_vis = max(wave_vis, lvis[nt]);
+  }
+  for (int m = 1; m < kWave; m <<= 1) wave_vis = max(wave_vis, __shfl_xor(wave_vis, m));
+  // keys the workgroup needs: up to its last row's position
+  const int last_row = min(row0 + rows_wg, R) - 1;
+  const int end = cached + last_row / p.G + 1;  // <= L
+
+  bf16x8_t qf[NT][KK];
+  const uint16_t* qbase = (const uint16_t*)p.q;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (rvalid[nt]) w = *reinterpret_cast<const uint4*>(qbase + qoff[nt] + kk * 32 + grp * 8);
+      qf[nt][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  f32x4_t oacc[NT][DT];
+  float m[NT], l[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  // The sequence's block ids up to `end`, staged in LDS: read from global
+  // memory inside the loop, an id would be the newest load in flight and
+  // waiting for it would wait for every tile load behind it.
+  __shared__ int s_ids[kPfMaxIds];  // max_blocks <= kPfMaxIds (checked on the host)
+  const int n_ids = p.table ? ((end - 1) >> bs_shift) + 1 : 0;
+  for (int i = tid; i < n_ids; i += kPfThreads) s_ids[i] = p.table[(long)b * p.max_blocks + i];
+  __syncthreads();
+  // element offset of key `t` (a multiple of 16) of (b, g); -1: bad block
+  auto key_base = [&](int t) -> long {
+    if (p.table == nullptr) return (((long)b * p.Hkv + g) * p.S_max + t) * D;
+    const int blk = s_ids[t >> bs_shift];
+    if (blk < 0 || blk >= p.N) return -1;
+    return (((long)blk * p.Hkv + g) * p.bs + (t & (p.bs - 1))) * D;
+  };
+  const int n_tiles = (end + kPfKeys - 1) / kPfKeys;
+  struct Stage {
+    uint4 k[PER], v[PER];
+    bool ok;
+  };
+  Stage st[PF];
+  // Every stage issues the same loads on every path (clamped addresses), so
+  // the compiler waits for one stage at a time.  A 32-key tile is two 16-key
+  // halves, each inside one block (block sizes are multiples of 16).
+  auto fetch = [&](Stage& s, int n) {
+    const int t = n * kPfKeys;
+    const bool in = t < end;
+    const long b0 = key_base(in ? t : 0);
+    const long b1 = key_base(in && t + 16 < end ? t + 16 : (in ? t : 0));
+    s.ok = in && b0 >= 0 && b1 >= 0;
+    const int last = in ? min(kPfKeys, end - t) - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = s.ok ? min(u * kPfThreads + tid, TCH - 1) : 0;
+      const int row = min(idx / CPR, last);
+      const long base = s.ok ? (row < 16 ? b0 : b1 - 16 * D) : 0;
+      const long off = base + (long)row * D + (idx % CPR) * 8;
+      s.k[u] = load_stream((const uint16_t*)p.k + off);
+      s.v[u] = load_stream((const uint16_t*)p.v + off);
+    }
+  };
+  auto store = [&](const Stage& s) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = u * kPfThreads + tid;
+      if (idx < TCH) {
+        const int o = (idx / CPR) * ROWB + (idx % CPR) * 16;
+        *reinterpret_cast<uint4*>(k_lds + o) = s.k[u];
+        *reinterpret_cast<uint4*>(v_lds + o) = s.v[u];
+      }
+    }
+  };
+  constexpr float kLazy = 8.f;
+  auto compute16 = [&](int t16, int half) {  // keys t16 .. t16 + 15 from LDS rows half*16..
+    const uint8_t* ka_ptr = k_lds + (half * 16 + col) * ROWB + grp * 16;
+    const uint8_t* va_ptr = v_lds + (half * 16 + grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+    bf16x8_t ka[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
+    bf16x8_t pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], s, 0, 0, 0);
+      const int key0 = t16 + grp * 4;
+      float sv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool move = mx > m[nt] + kLazy;
+      if (__any(move)) {
+        const float m_new = move ? mx : m[nt];
+        const float alpha = m[nt] == -INFINITY ? 0.f : fast_exp2(m[nt] - m_new);
+        l[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha;
+        m[nt] = m_new;
+      }
+      const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
+      const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+      const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+      l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+      const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+      const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+      const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+      pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                       __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+          (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
+      const bf16x4_t va = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+      const bf16x8_t va2 = __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[nt], oacc[nt][dt], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fetch(st[j], j);
+  store(st[0]);
+  __syncthreads();
+  for (int n0 = 0; n0 < n_tiles; n0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int n = n0 + j;
+      const bool ok = st[j].ok;
+      fetch(st[j], n + PF);
+      const int t = n * kPfKeys;
+      if (n < n_tiles) {
+        if (!ok) {
+          if (tid == 0) report(p.status, KVC_ERR_DATA);
+        } else {
+          if (t < wave_vis) compute16(t, 0);       // tiles above the diagonal are skipped
+          if (t + 16 < wave_vis) compute16(t + 16, 1);
+        }
+      }
+      __syncthreads();
+      store(st[(j + 1) % PF]);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float lt = l[nt] + __shfl_xor(l[nt], 16);
+    lt += __shfl_xor(lt, 32);
+    if (!rvalid[nt]) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const long o = qoff[nt] + dt * 16 + grp * 4;
+      const f32x4_t v = oacc[nt][dt] * inv;
+      if constexpr (BF16_OUT) {
+        uint16_t* out = (uint16_t*)p.out + o;
+        *reinterpret_cast<uint2*>(out) = make_uint2(
+            f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+            f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+      } else {
+        *reinterpret_cast<f32x4_t*>((float*)p.out + o) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int out_dtype, hipStream_t s) {
+  constexpr int NT = 2;
+  const long rows_wg = kPfWaves * 16 * NT;
+  const long n_rt = ((long)p.max_q * p.G + rows_wg - 1) / rows_wg;
+  if (n_rt == 0 || p.B == 0) return hipSuccess;
+  if (n_rt > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n_rt, p.Hkv, p.B), block(kPfThreads);
+  const bool bf = out_dtype == KVC_BF16;
+  if (p.D == 128) {
+    if (bf) hipLaunchKernelGGL((prefill_mfma<128, NT, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((prefill_mfma<128, NT, false>), grid, block, 0, s, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((prefill_mfma<64, NT, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((prefill_mfma<64, NT, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -36,6 +36,19 @@ struct AttnParams {
   const float* v_scale;
 };
 
+struct PrefillParams {
+  const void* q;            // [total_q][Hq][D] bf16, sequence b's rows at cu_q[b] ..
+  const int32_t* cu_q;      // [B + 1]
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;  // lengths after the chunk was appended
+  const int32_t* table;     // NULL for a contiguous cache
+  void* out;                // [total_q][Hq][D]
+  int32_t* status;
+  int B, Hq, Hkv, G, D, bs, S_max, max_blocks, N, cap, total_q, max_q;
+  float scale_log2;
+};
+
 struct ReduceParams {
   const float* ws_o;
   const float* ws_ml;

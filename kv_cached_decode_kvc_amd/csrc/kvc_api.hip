@@ -225,10 +225,10 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
   if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
   if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
   if (!seq_lens || !cu_new || !k_cache || !seq_lens_out) return KVC_ERR_ARG;
-  if ((v_cache == nullptr) != (v_new == nullptr)) return KVC_ERR_ARG;  // both NULL: keys only
+  if (!v_cache && v_new) return KVC_ERR_ARG;  // v_cache NULL: a key-only cache
   if (!v_cache && fp8_format(d)) return KVC_ERR_UNSUPPORTED;
   if (seq_lens_out == seq_lens) return KVC_ERR_ARG;
-  if (total_new > 0 && !k_new) return KVC_ERR_ARG;
+  if (total_new > 0 && (!k_new || (v_cache && !v_new))) return KVC_ERR_ARG;
   if (d->block_size > 0 && total_new > 0 && !slot_mapping) return KVC_ERR_ARG;
   if (d->block_size == 0 && slot_mapping) return KVC_ERR_ARG;
   AppendArgs a{};
@@ -505,6 +505,45 @@ int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void
   if (st != KVC_OK) return st;
   return kvc_mla_attn_reduce(d, n_q, value_dim, seq_lens, workspace, workspace_bytes, out,
                              out_dtype, dev_status, stream);
+}
+
+int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q, int32_t total_q,
+                     int32_t max_q, const void* k_cache, const void* v_cache,
+                     const int32_t* seq_lens, const int32_t* block_table, float scale, void* out,
+                     int32_t out_dtype, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->dtype != KVC_BF16 || d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (total_q < 0 || max_q < 0) return KVC_ERR_ARG;
+  if (d->block_size > 0 && d->max_blocks_per_seq > 4096) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0 || total_q == 0) return KVC_OK;
+  if (!q || !cu_q || !k_cache || !v_cache || !seq_lens || !out) return KVC_ERR_ARG;
+  if ((d->block_size > 0) != (block_table != nullptr)) return KVC_ERR_ARG;
+  if (!isfinite(scale)) return KVC_ERR_ARG;
+  PrefillParams p{};
+  p.q = q;
+  p.cu_q = cu_q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.seq_lens = seq_lens;
+  p.table = block_table;
+  p.out = out;
+  p.status = dev_status;
+  p.B = d->batch;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.G = d->num_q_heads / d->num_kv_heads;
+  p.D = d->head_dim;
+  p.bs = d->block_size;
+  p.S_max = d->max_seq_len;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.N = d->num_blocks;
+  p.cap = capacity(d);
+  p.total_q = total_q;
+  p.max_q = max_q;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(launch_prefill(p, out_dtype, (hipStream_t)stream));
 }
 
 size_t kvc_cache_bytes(const kvc_cache_desc* d) {

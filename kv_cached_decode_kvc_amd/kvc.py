@@ -28,7 +28,7 @@ EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn"
            "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
            "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_mla_workspace_bytes",
            "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
-           "kvc_mla_attn", "kvc_status_string")
+           "kvc_mla_attn", "kvc_prefill_attn", "kvc_status_string")
 
 
 class KvcError(RuntimeError):
@@ -89,7 +89,9 @@ def lib() -> ctypes.CDLL:
         L.kvc_mla_attn_reduce.argtypes = [D, I, I, P, P, ctypes.c_size_t, P, I, P, P]
         L.kvc_mla_attn.argtypes = [D, P, I, P, P, P, I, ctypes.c_float, P, I, P, ctypes.c_size_t,
                                    P, P]
-        for n in ("kvc_mla_attn_partition", "kvc_mla_attn_reduce", "kvc_mla_attn"):
+        L.kvc_prefill_attn.argtypes = [D, P, P, I, I, P, P, P, P, ctypes.c_float, P, I, P, P]
+        for n in ("kvc_mla_attn_partition", "kvc_mla_attn_reduce", "kvc_mla_attn",
+                  "kvc_prefill_attn"):
             getattr(L, n).restype = ctypes.c_int
         L.kvc_cache_bytes.argtypes = [D]
         L.kvc_cache_bytes.restype = ctypes.c_size_t
@@ -276,6 +278,15 @@ def kvc_mla_attn(desc, q, n_q, latent_cache, seq_lens, block_table, value_dim, s
         float(scale), _ptr(out, "out"), _out_dtype(out, out_dtype), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(dev_status, "dev_status", I32),
         _stream(stream)))
+
+
+def kvc_prefill_attn(desc, q, cu_q, total_q, max_q, k_cache, v_cache, seq_lens, block_table,
+                     scale, out, dev_status=None, stream=None, out_dtype=None):
+    _check("kvc_prefill_attn", lib().kvc_prefill_attn(
+        ctypes.byref(desc), _ptr(q, "q"), _ptr(cu_q, "cu_q", I32), int(total_q), int(max_q),
+        _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"), _ptr(seq_lens, "seq_lens", I32),
+        _ptr(block_table, "block_table", I32), float(scale), _ptr(out, "out"),
+        _out_dtype(out, out_dtype), _ptr(dev_status, "dev_status", I32), _stream(stream)))
 
 
 def kvc_cache_bytes(desc) -> int:

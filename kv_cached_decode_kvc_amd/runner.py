@@ -174,7 +174,7 @@ class LayerCache:
         self.s_q = to_dev(synth.packed_queries(w, step), w.dtype, self.dev)
         self.s_out = torch.empty((w.B, w.n_q, w.Hq, w.out_dim), dtype=torch.float32,
                                  device=self.dev)
-        self.s_ws = self.workspace(w.n_q)
+        self.s_ws = None if w.prefill else self.workspace(w.n_q)
         if self.bs:
             self.s_head0 = self.head.clone()  # free-list head before the step: never written
             self.s_head1 = torch.empty_like(self.head)
@@ -205,11 +205,20 @@ class LayerCache:
         else:
             kvc.kvc_attn_reduce(self.desc, n_q, lens, ws, out, self.status)
 
+    def prefill_attn(self, q, cu_q, total_q, max_q, lens, out):
+        kvc.kvc_prefill_attn(self.desc, q, cu_q, total_q, max_q, self.k, self.v, lens, self.table,
+                             self.scale, out, self.status)
+
     def step_partition(self):
-        self.partition(self.s_q, self.w.n_q, self.s_len1, self.s_ws)
+        if self.w.prefill:  # one kernel: no split over keys, no reduce
+            self.prefill_attn(self.s_q, self.s_cu, self.s_total, self.w.n_q, self.s_len1,
+                              self.s_out)
+        else:
+            self.partition(self.s_q, self.w.n_q, self.s_len1, self.s_ws)
 
     def step_reduce(self):
-        self.reduce(self.w.n_q, self.s_len1, self.s_ws, self.s_out)
+        if not self.w.prefill:
+            self.reduce(self.w.n_q, self.s_len1, self.s_ws, self.s_out)
 
     def step(self):
         self.step_front()

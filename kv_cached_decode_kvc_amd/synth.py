@@ -40,6 +40,7 @@ class Workload:
     description: str = ""
     kv: str = ""  # "": the cache holds dtype; "e4m3" / "e5m2": FP8 codes + a scale per row
     dv: int = 0   # MLA: value dims of a latent row (its leading dims); 0 = separate K and V
+    prefill: bool = False  # the step's n_q new rows attend causally (kvc_prefill_attn)
 
     @property
     def esize(self) -> int:
@@ -110,6 +111,23 @@ for _w in [
     WORKLOADS[_w.name] = _w
 ALIASES["M1"], ALIASES["M2"] = ("mla-h128-paged64-b32-ctx1024to4096",
                                 "mla-h16-paged64-b128-ctx1024to8192")
+
+# Prefill and chunked prefill (GQA 32/8, head 128, paged block 16): a whole
+# 4096-token prompt for 4 sequences, and 512-token chunks on top of 3584
+# cached tokens for 16 sequences.
+for _w in [
+    Workload("prefill-gqa32x8-paged-b4-prompt4096", seed=9, B=4, Hq=32, Hkv=8, D=128,
+             dtype="bf16", block_size=16, n_q=4096, len_lo=4096, len_hi=4096,
+             description="prefill of a 4096-token prompt, GQA 32/8, head 128, paged block 16, "
+                         "batch 4", prefill=True),
+    Workload("chunked-prefill-gqa32x8-paged-b16-chunk512-ctx4096", seed=10, B=16, Hq=32,
+             Hkv=8, D=128, dtype="bf16", block_size=16, n_q=512, len_lo=4096, len_hi=4096,
+             description="chunked prefill: 512-token chunks over 3584 cached tokens, GQA "
+                         "32/8, head 128, paged block 16, batch 16", prefill=True),
+]:
+    WORKLOADS[_w.name] = _w
+ALIASES["P1"], ALIASES["P2"] = ("prefill-gqa32x8-paged-b4-prompt4096",
+                                "chunked-prefill-gqa32x8-paged-b16-chunk512-ctx4096")
 
 # The same four full-size workloads over an FP8 (E4M3) cache: same seeds, so the
 # same lengths and rows, quantized on append.
@@ -237,7 +255,7 @@ def packed_queries(w: Workload, step: int = 0) -> np.ndarray:
 
 
 def custom(name="custom", seed=0, B=2, Hq=4, Hkv=4, D=64, dtype="bf16", block_size=0, n_q=1,
-           len_lo=16, len_hi=16, steps=1, kv="", dv=0) -> Workload:
+           len_lo=16, len_hi=16, steps=1, kv="", dv=0, prefill=False) -> Workload:
     """A small workload for tests (same generators, other sizes)."""
     return Workload(name, seed, B, Hq, Hkv, D, dtype, block_size, n_q, len_lo, len_hi, steps,
-                    kv=kv, dv=dv)
+                    kv=kv, dv=dv, prefill=prefill)

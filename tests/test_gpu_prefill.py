@@ -1,0 +1,131 @@
+"""GPU parity of (chunked) prefill attention: every new row of every sequence
+attends causally over its cached keys and the chunk's own keys, against the
+oracle's attention definition with the chunk's rows as verify rows (row r
+sees keys 0 .. L - n + r)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cached_decode_kvc_amd import kvc, runner, synth
+from gpu_harness import GpuCache, assert_close, i32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (name, dtype-out, D, Hq, Hkv, block_size, B, chunk_hi, cached_hi)
+CASES = [
+    ("mha-d128-paged", "f32", 128, 4, 4, 16, 4, 200, 300),
+    ("gqa4-d128-paged-bs32", "f32", 128, 8, 2, 32, 3, 300, 200),
+    ("gqa8-d64-contig", "f32", 64, 8, 1, 0, 3, 150, 150),
+    ("mha-d64-paged-prompt-only", "f32", 64, 2, 2, 16, 3, 260, 0),
+    ("gqa4-d128-paged-bf16-out", "bf16", 128, 8, 2, 16, 3, 180, 120),
+]
+
+
+def _chunk_case(ref, name, out_dtype, D, Hq, Hkv, bs, B, chunk_hi, cached_hi, seed=0):
+    rng = np.random.default_rng(5000 + D + Hq + seed)
+    w = synth.custom(name=name, seed=5100 + seed, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                     block_size=bs, n_q=1, len_lo=1, len_hi=chunk_hi + cached_hi + 1,
+                     prefill=True)
+    cached = rng.integers(0, cached_hi + 1, size=B)
+    chunk = rng.integers(0, chunk_hi + 1, size=B)
+    chunk[0] = max(chunk[0], 1)
+    if B > 2:
+        chunk[1] = 0  # a sequence with nothing to prefill in this call
+    cap = int((cached + chunk).max()) + 3
+    gc = GpuCache(w, block_size=bs if bs else None, capacity=cap)
+    gc.prefill(cached)
+    total = int(chunk.sum())
+    kr = synth.normal(w, (total, Hkv, D), synth.S_KNEW, 55, seed)
+    vr = synth.normal(w, (total, Hkv, D), synth.S_VNEW, 55, seed)
+    q = synth.normal(w, (total, Hq, D), synth.S_Q, 55, seed)
+    gc.add_tokens(kr, vr, chunk)
+    cu = synth.cu_from_counts(chunk)
+    out = torch.full((max(total, 1), Hq, D), float("nan"), device="cuda",
+                     dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    scale = 1.0 / math.sqrt(D)
+    kvc.kvc_prefill_attn(gc.desc, to_dev(q, "bf16"), i32(cu), total, int(chunk.max()), gc.k, gc.v,
+                         gc.seq_lens, gc.table, scale, out, gc.status)
+    assert gc.dev_status() == 0
+    got = out.float().cpu().numpy()
+    for b in range(B):
+        n = int(chunk[b])
+        if n == 0:
+            continue
+        k = np.concatenate([synth.cache_rows(w, "k", b, int(cached[b])), kr[cu[b]:cu[b + 1]]])
+        v = np.concatenate([synth.cache_rows(w, "v", b, int(cached[b])), vr[cu[b]:cu[b + 1]]])
+        want = ref.attention(q[cu[b]:cu[b + 1]], k.transpose(1, 0, 2).copy(),
+                             v.transpose(1, 0, 2).copy(), scale, "bf16")
+        g = got[cu[b]:cu[b + 1]]
+        if out_dtype == "bf16":
+            err = np.abs(g - want)
+            assert np.all(err <= 2e-3 + 1e-2 * np.abs(want) + np.abs(want) * 2.0 ** -8), (name, b)
+        else:
+            assert_close(g, want, "%s b=%d cached=%d chunk=%d" % (name, b, cached[b], n))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_parity(ref, case):
+    _chunk_case(ref, *case)
+
+
+def test_prefill_chunks_equal_one_pass(ref):
+    """A prompt prefilled in three chunks gives the same rows (to the
+    tolerance) as the oracle's attention over the whole prompt at once."""
+    D, Hq, Hkv, n = 128, 8, 2, 300
+    w = synth.custom(name="c", seed=5200, B=1, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", block_size=16,
+                     n_q=1, len_lo=n, len_hi=n, prefill=True)
+    gc = GpuCache(w, block_size=16, capacity=n)
+    kr = synth.normal(w, (n, Hkv, D), synth.S_KNEW, 1)
+    vr = synth.normal(w, (n, Hkv, D), synth.S_VNEW, 1)
+    q = synth.normal(w, (n, Hq, D), synth.S_Q, 1)
+    outs = []
+    for a, e in ((0, 97), (97, 160), (160, n)):
+        gc.add_tokens(kr[a:e], vr[a:e], [e - a])
+        out = torch.empty((e - a, Hq, D), dtype=torch.float32, device="cuda")
+        kvc.kvc_prefill_attn(gc.desc, to_dev(q[a:e], "bf16"), i32([0, e - a]), e - a, e - a, gc.k,
+                             gc.v, gc.seq_lens, gc.table, 1 / math.sqrt(D), out, gc.status)
+        outs.append(out.cpu().numpy())
+    assert gc.dev_status() == 0
+    want = ref.attention(q, kr.transpose(1, 0, 2).copy(), vr.transpose(1, 0, 2).copy(),
+                         1 / math.sqrt(D), "bf16")
+    assert_close(np.concatenate(outs), want, "chunked prefill")
+
+
+@pytest.mark.parametrize("name", ["P1", "P2"])
+def test_prefill_full_size_sampled(ref, name):
+    """Full-size workloads in the benchmark's launch configuration: sampled rows
+    (first, middle, last of two sequences) against the oracle's one-row
+    attention over each row's visible keys."""
+    w = synth.get(name)
+    print("full-size prefill workload", w.name, flush=True)
+    lc = runner.build(w)
+    out1 = lc.step().clone()
+    out2 = lc.step().clone()
+    assert lc.dev_status() == 0
+    assert torch.equal(out1, out2)
+    got = out1.cpu().numpy()  # [B, n_q, Hq, D]
+    cached = synth.cached_lengths(w)
+    scale = 1.0 / math.sqrt(w.D)
+    for b in (0, w.B - 1):
+        k = np.concatenate([synth.cache_rows(w, "k", b, int(cached[b])), synth.new_rows(w, "k", b)])
+        v = np.concatenate([synth.cache_rows(w, "v", b, int(cached[b])), synth.new_rows(w, "v", b)])
+        q = synth.queries(w, b)
+        for r in (0, w.n_q // 2, w.n_q - 1):
+            L = int(cached[b]) + r + 1
+            want = ref.attention(q[r:r + 1], k[:L].transpose(1, 0, 2).copy(),
+                                 v[:L].transpose(1, 0, 2).copy(), scale, "bf16")
+            assert_close(got[b, r:r + 1], want, "%s b=%d r=%d" % (name, b, r))
+    del lc
+    torch.cuda.empty_cache()
+
+
+def test_prefill_refusals():
+    w = synth.custom(name="r", seed=1, B=1, Hq=2, Hkv=2, D=64, dtype="f32", block_size=16,
+                     n_q=1, len_lo=4, len_hi=4)
+    gc = GpuCache(w, block_size=16, capacity=32)
+    out = torch.empty((4, 2, 64), device="cuda")
+    with pytest.raises(kvc.KvcError):  # fp32 caches: not supported by the prefill kernel
+        kvc.kvc_prefill_attn(gc.desc, out, i32([0, 4]), 4, 4, gc.k, gc.v, gc.seq_lens, gc.table,
+                             0.125, out, gc.status)
