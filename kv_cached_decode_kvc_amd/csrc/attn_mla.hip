@@ -25,8 +25,9 @@
 //
 // A wavefront holds 16 rows of queries (72 VGPRs) and of 512-wide fp32
 // accumulators (128), so it runs alone on its SIMD (512 registers) and a
-// workgroup fills a CU; latency is hidden by a ring of PF register stages,
-// PF - 1 tiles ahead of the one in use.  Row groups of the same (sequence,
+// workgroup fills a CU.  Two LDS tiles let the score products of tile n + 1
+// be issued before the softmax of tile n, which does not depend on them;
+// a ring of PF register stages keeps the following tiles in flight.  Row groups of the same (sequence,
 // partition) get workgroup ids 8 apart: launches place workgroup i on XCD
 // i mod 8, so they share one XCD's L2 and run at the same time, and the tile
 // comes from HBM once.
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
   constexpr int TCH = kTile * CPR;        // 1152 chunks per tile
   constexpr int PER = (TCH + kMlaThreads - 1) / kMlaThreads;  // chunks per thread
   constexpr int ROWB = DK * 2 + 16;       // padded LDS row
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTile * ROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,69 +164,65 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
       st[u] = load_stream(base + row * DK + (idx % CPR) * 8);
     }
   };
-  auto store_tile = [&](const uint4 (&st)[PER]) {
+  auto store_tile = [&](int buf, const uint4 (&st)[PER]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = u * kMlaThreads + tid;
       if (idx < TCH)
-        *reinterpret_cast<uint4*>(lds + (idx / CPR) * ROWB + (idx % CPR) * 16) = st[u];
+        *reinterpret_cast<uint4*>(lds[buf] + (idx / CPR) * ROWB + (idx % CPR) * 16) = st[u];
     }
   };
   // tile n of the partition is start + n * stride; it lives in stage n % PF
-  const uint8_t* ka_ptr = lds + col * ROWB + grp * 16;
-  const uint8_t* va_ptr = lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+  // Two LDS tiles: while tile n's softmax runs on the vector ALUs, tile
+  // n + 1's score products run on the matrix cores (they do not depend on
+  // each other), then tile n's value products follow.
   constexpr float kLazy = 8.f;
-
-  // A wavefront runs alone on its SIMD, so nothing hides LDS latency but its
-  // own batching: all K fragments of the tile are read before the score
-  // products, and value fragments come in groups of 8, each group issued
-  // while the previous group's products run (sched_barrier keeps the
-  // scheduler from interleaving them back one by one).
-  auto compute = [&](int tile) {
-    bf16x8_t pb[NT];
+  auto qk = [&](int buf) -> f32x4_t {  // S^T of the tile in `buf`: this lane's 4 keys of row col
+    const uint8_t* ka = lds[buf] + col * ROWB + grp * 16;
     bf16x8_t kf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
-    __builtin_amdgcn_sched_barrier(0);
+      kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + kk * 64));
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};  // two chains
-#pragma unroll
-      for (int kk = 0; kk < KK; kk += 2) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[nt][kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk + 1], qf[nt][kk + 1], s1, 0, 0, 0);
-      }
-      const f32x4_t s = s0 + s1;
-      const int key0 = tile + grp * 4;
-      float sv[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool move = mx > m[nt] + kLazy;
-      if (__any(move)) {
-        const float m_new = move ? mx : m[nt];
-        const float alpha = m[nt] == -INFINITY ? 0.f : fast_exp2(m[nt] - m_new);
-        l[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] *= alpha;
-        m[nt] = m_new;
-      }
-      const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
-      const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
-      const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
-      l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
-      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
-      const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
-      const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
-      const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
-      pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
-                                       __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
-                                       0, 1, 2, 3, 4, 5, 6, 7);
+    for (int kk = 0; kk < KK; kk += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[0][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk + 1], qf[0][kk + 1], s1, 0, 0, 0);
     }
-    constexpr int VG = 8;  // value fragments per group
+    return s0 + s1;
+  };
+  // online softmax of one tile, branch free; returns the weights (bf16 hi +
+  // lo) and the factor the accumulators must be rescaled by (1: none)
+  float alpha = 1.f;
+  bool rescale = false;
+  auto softmax = [&](const f32x4_t& s, int tile, bool ok) -> bf16x8_t {
+    const int key0 = tile + grp * 4;
+    float sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = ok && key0 + v < lvis[0] ? s[v] * p.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m[0] + kLazy;
+    rescale = __any(move);
+    const float m_new = move ? mx : m[0];
+    alpha = m[0] == -INFINITY ? 0.f : fast_exp2(m[0] - m_new);
+    m[0] = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+    const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+    l[0] = l[0] * alpha + ((p01[0] + p01[1]) + (p23[0] + p23[1]));
+    const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+    const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+    const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+    const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+    return __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                   __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto pv = [&](int buf, const bf16x8_t& pb) {  // O^T += V^T . P^T, value fragments in groups
+    const uint8_t* va_ptr = lds[buf] + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+    constexpr int VG = 8;
     auto read_v = [&](bf16x4_t (&va)[VG], int g) {
 #pragma unroll
       for (int i = 0; i < VG; ++i) {
@@ -243,10 +240,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < VG; ++i) {
         const bf16x8_t va2 = __builtin_shufflevector(vcur[i], vcur[i], 0, 1, 2, 3, 0, 1, 2, 3);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          oacc[nt][g * VG + i] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[nt], oacc[nt][g * VG + i], 0, 0, 0);
+        oacc[0][g * VG + i] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb, oacc[0][g * VG + i], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -254,30 +249,44 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
     }
   };
 
+  // prologue: tiles 0 and 1 in LDS, tiles 2 .. PF + 1 in flight, scores of
+  // tile 0.  Stage (n + 2) % PF holds tile n + 2 until step n stores it into
+  // LDS buffer n % 2, then takes tile n + 2 + PF.
 #pragma unroll
-  for (int j = 0; j < PF; ++j) fetch(stage[j], stb[j], j);
-  store_tile(stage[0]);
+  for (int k = 0; k < PF; ++k) fetch(stage[k], stb[k], k);
+  store_tile(0, stage[0]);
+  store_tile(1, stage[1]);
+  bool bok[2] = {stb[0] >= 0, stb[1] >= 0};
   __syncthreads();
+  fetch(stage[0], stb[0], PF);
+  fetch(stage[1], stb[1], PF + 1);
+  f32x4_t s_cur = {0.f, 0.f, 0.f, 0.f};
+  if (active) s_cur = qk(0);
   for (int n0 = 0; n0 < n_tiles; n0 += PF) {
-    // The body is the same on every path (fetch, barrier, store, barrier),
-    // only the compute depends on n: a store skipped on one path would leave
-    // its stage's loads pending at the loop's back edge, and the compiler
-    // would then drain every load in flight at the top of each iteration.
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {  // tile n = n0 + j: in LDS, from stage j
-      const int n = n0 + j;
-      const long tb = stb[j];
-      fetch(stage[j], stb[j], n + PF);  // stage j is free again: PF tiles ahead
+    for (int jj = 0; jj < PF; ++jj) {  // tile n in buffer j, tile n + 1 in buffer 1 - j
+      const int n = n0 + jj;
+      const int j = jj & 1;
+      const int sg = (jj + 2) % PF;  // the stage holding tile n + 2
+      f32x4_t s_next = {0.f, 0.f, 0.f, 0.f};
       if (n < n_tiles) {
-        if (tb >= 0) {
-          if (active) compute(start + n * stride);
-        } else if (tid == 0) {
-          report(p.status, KVC_ERR_DATA);
+        if (active) {
+          s_next = qk(1 - j);  // tile n + 1 (results unused past the end)
+          const bf16x8_t pb = softmax(s_cur, start + n * stride, bok[j]);
+          if (rescale) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[0][dt] *= alpha;
+          }
+          if (bok[j]) pv(j, pb);  // a bad block's tile holds no usable rows
         }
+        if (!bok[j] && tid == 0) report(p.status, KVC_ERR_DATA);
       }
-      __syncthreads();  // every wavefront is done reading the tile
-      store_tile(stage[(j + 1) % PF]);
+      __syncthreads();  // every wavefront is done with buffer j
+      store_tile(j, stage[sg]);  // tile n + 2
+      bok[j] = stb[sg] >= 0;
+      fetch(stage[sg], stb[sg], n + 2 + PF);
       __syncthreads();
+      s_cur = s_next;
     }
   }
 
