@@ -162,3 +162,39 @@ def test_fp8_copy_blocks_carry_scales():
                 wc[d_], ws[d_] = c0[s_], s0[s_]
         assert torch.equal(codes, wc)
         assert torch.equal(scales.view(torch.int32), ws.view(torch.int32))
+
+
+def test_fp8_parallel_samples_copy_on_write(ref):
+    """Sharing on an FP8 pool: prompts forked into samples that then append
+    different tokens; copy-on-write copies codes and scales, and every sample's
+    attention matches the oracle's attention over its own quantized rows
+    (prompt rows, then its new token)."""
+    bs, B, fmt = 16, 6, "e4m3"
+    w = synth.custom(name="s", seed=88, B=B, Hq=8, Hkv=2, D=128, dtype="bf16", block_size=bs,
+                     n_q=1, len_lo=1, len_hi=200, kv=fmt)
+    gc = GpuCache(w, block_size=bs, capacity=256, pool_blocks=120)
+    refs = torch.zeros(gc.N, dtype=torch.int32, device="cuda")
+    prompt = [150, 77, 0, 0, 0, 0]
+    gc.prefill(prompt)
+    kvc.kvc_fork(gc.desc, i32([0, 0, 1, 1]), i32([2, 3, 4, 5]), 4, gc.seq_lens, gc.table, refs,
+                 gc.status)
+    rows_k = synth.normal(w, (B, w.Hkv, w.D), synth.S_KNEW, 7)
+    rows_v = synth.normal(w, (B, w.Hkv, w.D), synth.S_VNEW, 7)
+    src = torch.empty(B, dtype=torch.int32, device="cuda")
+    dst = torch.empty(B, dtype=torch.int32, device="cuda")
+    kvc.kvc_cow(gc.desc, gc.seq_lens, i32(synth.cu_from_counts([1] * B)), gc.table, gc.free_list,
+                gc.head, gc.head, refs, gc.k, gc.v, src, dst, gc.status)
+    gc.add_tokens(rows_k, rows_v, [1] * B)
+    assert gc.dev_status() == 0
+    assert int((src >= 0).sum().item()) == B  # every sharer copied its partly filled block
+    q = synth.normal(w, (B, 1, w.Hq, w.D), synth.S_Q, 7)
+    got = gc.attend(to_dev(q, "bf16"), 1).cpu().numpy()
+    parent = [0, 1, 0, 0, 1, 1]
+    for b in range(B):
+        pb = parent[b]
+        k = np.concatenate([synth.cache_rows(w, "k", pb, prompt[pb]), rows_k[b:b + 1]])
+        v = np.concatenate([synth.cache_rows(w, "v", pb, prompt[pb]), rows_v[b:b + 1]])
+        kd = ref.dequantize_rows(*ref.quantize_rows(k.transpose(1, 0, 2).copy(), fmt), fmt)
+        vd = ref.dequantize_rows(*ref.quantize_rows(v.transpose(1, 0, 2).copy(), fmt), fmt)
+        want = ref.attention(oracle.widen(q[b], "bf16"), kd, vd, 1 / math.sqrt(w.D), "f64")
+        assert_close(got[b], want, "fp8 sample %d" % b)
