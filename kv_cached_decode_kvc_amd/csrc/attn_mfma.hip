@@ -6,8 +6,11 @@
 // KV head is read from HBM once per group ("Efficient Inference",
 // learn.obvix.io: the repeated heads are never materialised).
 //
-// Per wavefront: one (sequence b, KV head g, block of 16*NT rows, partition).
-// Partition p of n owns the 16-key tiles p, p + n, ... (as in the VALU kernel).
+// Per wavefront (one per workgroup): one (sequence b, KV head g, block of 16*NT
+// rows, partition), spread over the XCDs with xcd_item (common.hpp).
+// Partition p of n owns the 16-key tiles p, p + n, ... (as in the VALU kernel);
+// in a paged cache their block ids are fetched 64 at a time into one register
+// and picked out with v_readlane.
 // Per tile of TK keys:
 //   1. K and V rows arrive with coalesced non-temporal 16-byte loads (one
 //      instruction = RPL whole rows, contiguous) one tile ahead, and are
@@ -41,7 +44,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 // everything after it stay bf16: codes are widened exactly on the way in, the
 // key scales multiply the scores and the value scales join the weights).
 template <int D, int NT, int MINW, int F>
-__global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
+__global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
   constexpr int KK = D / 32;          // QK^T steps of 32 along D
   constexpr int DT = D / 16;          // PV output column tiles
   constexpr int EB = F ? 1 : 2;       // bytes per cache element in HBM
@@ -50,28 +53,20 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   constexpr int U = kTile / RPL;      // loads per tile, each of K and V
   constexpr int ROWB = D * 2 + 16;    // LDS row stride: one 16-byte pad per key row
   constexpr int TILEB = kTile * ROWB;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][2 * TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[2 * TILEB];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA row/column index of this lane
   const int grp = lane >> 4;  // which quarter of the reduction index
-  uint8_t* k_lds = lds_all[wave];
-  uint8_t* v_lds = lds_all[wave] + TILEB;
+  uint8_t* k_lds = lds_all;
+  uint8_t* v_lds = lds_all + TILEB;
 
   const int R = p.G * p.n_q;  // rows sharing this KV head
   const int rows_item = 16 * NT;
   const int n_rb = (R + rows_item - 1) / rows_item;
-  const long item = (long)blockIdx.x * 4 + wave;
-  const long n_items = (long)p.B * p.Hkv * n_rb * p.max_parts;
-  if (item >= n_items) return;
-  // item = ((b * Hkv + g) * n_rb + rb) * max_parts + part; all wave-uniform
-  const int part = __builtin_amdgcn_readfirstlane((int)(item % p.max_parts));
-  long t = item / p.max_parts;
-  const int rb = __builtin_amdgcn_readfirstlane((int)(t % n_rb));
-  t /= n_rb;
-  const int g = __builtin_amdgcn_readfirstlane((int)(t % p.Hkv));
-  const int b = __builtin_amdgcn_readfirstlane((int)(t / p.Hkv));
+  const WorkItem wi = xcd_item(blockIdx.x, p.Hkv * n_rb, p.max_parts);  // u = g * n_rb + rb
+  if (!wi.live) return;
+  const int b = wi.b, part = wi.part, rb = wi.u % n_rb, g = wi.u / n_rb;
 
   const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
   if (L < p.n_q || L > p.cap) {
@@ -124,12 +119,24 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   const int lr = lane / CH;   // key row of a wave load
   const int pos = lane % CH;  // 16-byte chunk of that row
   const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
-  // wave-uniform element offset of key `tile` of (b, g); -1 when the block
-  // table points outside the pool (the tile is then skipped)
-  auto tile_base = [&](int tile) -> long {
-    if (p.table == nullptr) return (((long)b * p.Hkv + g) * p.S_max + tile) * D;
-    const int blk = __builtin_amdgcn_readfirstlane(
-        p.table[(long)b * p.max_blocks + (tile >> bs_shift)]);
+  // paged: lane i holds the block of the partition's tile number j * 64 + i
+  const bool paged = p.table != nullptr;
+  const int32_t* trow = paged ? p.table + (long)b * p.max_blocks : nullptr;
+  auto load_ids = [&](int j) -> int {
+    const int tk = start + (j * kWave + lane) * stride;
+    return tk < end ? trow[tk >> bs_shift] : 0;
+  };
+  int ids = 0, ids_next = 0;
+  if (paged && start < end) {
+    ids = load_ids(0);
+    if (start + kWave * stride < end) ids_next = load_ids(1);
+  }
+  // wave-uniform element offset of key `tile`, the partition's tile number idx,
+  // of (b, g); -1 when the block table points outside the pool (the tile is
+  // then skipped)
+  auto tile_base = [&](int tile, int idx) -> long {
+    if (!paged) return (((long)b * p.Hkv + g) * p.S_max + tile) * D;
+    const int blk = __builtin_amdgcn_readlane(ids, idx & (kWave - 1));
     if (blk < 0 || blk >= p.N) return -1;
     return (((long)blk * p.Hkv + g) * p.bs + (tile & (p.bs - 1))) * D;
   };
@@ -183,7 +190,8 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
   constexpr float kLazy = 8.f;  // the reference maximum moves only past m + 8 (p <= 2^8)
 
   if (start < end) {
-    long tb = tile_base(start);
+    int idx = 0;
+    long tb = tile_base(start, 0);
     if (tb >= 0) load_tile(start, tb);
     store_tile();
     if constexpr (F != 0) {
@@ -191,12 +199,17 @@ __global__ __launch_bounds__(256, MINW) void partition_mfma(AttnParams p) {
       for (int v = 0; v < 4; ++v) ks_cur[v] = ks_next[v], vs_cur[v] = vs_next[v];
     }
     wave_lds_fence();
-    for (int tile = start; tile < end; tile += stride) {
+    for (int tile = start; tile < end; tile += stride, ++idx) {
       const int next = tile + stride;
       const bool ok = tb >= 0;
       long tb_next = -1;
       if (next < end) {
-        tb_next = tile_base(next);
+        if (paged && ((idx + 1) & (kWave - 1)) == 0) {  // the next 64 tiles' ids
+          const int j = (idx + 1) / kWave;
+          ids = ids_next;
+          if (start + (j + 1) * kWave * stride < end) ids_next = load_ids(j + 1);
+        }
+        tb_next = tile_base(next, idx + 1);
         if (tb_next >= 0) load_tile(next, tb_next);  // in flight while this tile computes
       }
       if (ok) {
@@ -309,9 +322,10 @@ void launch_mfma_fmt(const AttnParams& p, int rows_per_item, dim3 grid, dim3 blo
 hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, int fp8, hipStream_t s) {
   const int R = p.G * p.n_q;
   const int n_rb = (R + rows_per_item - 1) / rows_per_item;
-  const long n_items = (long)p.B * p.Hkv * n_rb * p.max_parts;
-  if (n_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n_items + 3) / 4)), block(256);
+  const long n_wg = xcd_grid(p.B, p.Hkv * n_rb, p.max_parts);
+  if (n_wg == 0) return hipSuccess;
+  if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n_wg), block(64);
   if (fp8 == kFp8E4M3) launch_mfma_fmt<kFp8E4M3>(p, rows_per_item, grid, block, s);
   else if (fp8 == kFp8E5M2) launch_mfma_fmt<kFp8E5M2>(p, rows_per_item, grid, block, s);
   else launch_mfma_fmt<0>(p, rows_per_item, grid, block, s);

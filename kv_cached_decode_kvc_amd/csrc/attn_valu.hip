@@ -21,7 +21,11 @@
 // read neighbouring tiles at the same time.  Any split of the keys gives the
 // same softmax once the partials are combined; this one keeps the memory
 // traffic of concurrent wavefronts inside a narrow window.  Keys are streamed
-// with non-temporal loads: they are read exactly once.
+// with non-temporal loads: they are read exactly once.  Work items are spread
+// over the XCDs with xcd_item (common.hpp); in a paged cache the block ids of
+// a partition's tiles are fetched 64 at a time into one register (one per
+// lane) and picked out with v_readlane, so no table load waits between one
+// tile's arrival and the next tile's loads.
 //
 // Layout of the work: a wavefront streams 16-key tiles.  A key row of D
 // elements is split over LPR lanes holding 16 bytes each, so one 16-byte load
@@ -143,22 +147,15 @@ struct Elem<Fp8<F>> {  // FP8 codes: a 16-byte load holds 16 elements; q is 16 b
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
+__global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
   constexpr bool kF8 = IsFp8<T>::kFormat != 0;
   constexpr int TPI = kF8 ? 2 : 1;  // tiles per loop iteration
-  const int lane = threadIdx.x & 63;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
-  if (item >= n_items) return;
-  // item = ((b * Hq + h) * n_q + r) * max_parts + part
-  const int part = (int)(item % p.max_parts);
-  long t = item / p.max_parts;
-  const int r = (int)(t % p.n_q);
-  t /= p.n_q;
-  const int h = (int)(t % p.Hq);
-  const int b = (int)(t / p.Hq);
+  const int lane = threadIdx.x;
+  const WorkItem wi = xcd_item(blockIdx.x, p.Hq * p.n_q, p.max_parts);  // u = h * n_q + r
+  if (!wi.live) return;
+  const int b = wi.b, part = wi.part, r = wi.u % p.n_q, h = wi.u / p.n_q;
 
   const int L = p.seq_lens[b];
   if (L < p.n_q || L > p.cap) {
@@ -187,6 +184,19 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
     const T* vbase = (const T*)p.v;
     const typename Elem<T>::Q qv =
         Elem<T>::load_q(p.q, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
+    // paged: lane i holds the block of the partition's tile number j * 64 + i
+    const bool paged = p.table != nullptr;
+    const int32_t* trow = paged ? p.table + (long)b * p.max_blocks : nullptr;
+    auto load_ids = [&](int j) -> int {
+      const int tk = start + (j * kWave + lane) * stride;
+      return tk < end ? trow[tk / p.bs] : 0;
+    };
+    int ids = 0, ids_next = 0;
+    if (paged) {
+      ids = load_ids(0);
+      if (start + kWave * stride < end) ids_next = load_ids(1);
+    }
+    int idx = 0;  // number of the iteration's first tile within the partition
     // TPI tiles of the partition per iteration: their loads are all issued
     // before any of them is used (FP8 tiles carry half the bytes, so two keep
     // as many bytes in flight per wavefront as one bf16 tile)
@@ -200,10 +210,15 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
         nvalid[i] = 0;
         if (ti >= end) continue;
         long tbase;  // element offset of key `ti` of (b, g)
-        if (p.table == nullptr) {
+        if (!paged) {
           tbase = (((long)b * p.Hkv + g) * p.S_max + ti) * D;
         } else {
-          const int blk = p.table[(long)b * p.max_blocks + ti / p.bs];
+          const int ii = idx + i;
+          if (ii > 0 && (ii & (kWave - 1)) == 0) {  // the next 64 tiles' ids
+            ids = ids_next;
+            if (start + (ii + kWave) * stride < end) ids_next = load_ids(ii / kWave + 1);
+          }
+          const int blk = __builtin_amdgcn_readlane(ids, ii & (kWave - 1));
           if (blk < 0 || blk >= p.N) {
             if (lane == 0) report(p.status, KVC_ERR_DATA);
             continue;
@@ -224,6 +239,7 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
           }
         }
       }
+      idx += TPI;
       float s[TPI][U];
       float mx = -INFINITY;
 #pragma unroll
@@ -275,9 +291,10 @@ __global__ __launch_bounds__(256) void partition_valu(AttnParams p) {
 }
 
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) {
-  const long n_items = (long)p.B * p.Hq * p.n_q * p.max_parts;
-  if (n_items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n_items + 3) / 4)), block(256);
+  const long n_wg = xcd_grid(p.B, p.Hq * p.n_q, p.max_parts);
+  if (n_wg == 0) return hipSuccess;
+  if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n_wg), block(64);
   if (dtype == KVC_BF16) {
     if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((partition_valu<uint16_t, 64>), grid, block, 0, s, p);

@@ -58,6 +58,45 @@ struct ReduceParams {
   int B, n_q, Hq, D, P, max_parts, cap;
 };
 
+// Work items of the split-KV partition kernels: (sequence b, partition part,
+// unit u), one wavefront each, one wavefront per workgroup.  The hardware
+// hands workgroups to the eight XCDs round robin (workgroup i runs on XCD
+// i % 8), so the id is split as i = 8 t + x and XCD x takes, of every
+// sequence, the items k = part * U + u with k = 8 m + x', where x' is x
+// rotated by the sequence number.  Every sequence's work is then spread evenly
+// over the XCDs whatever its length (an order with the partition index
+// innermost would hand the high partitions, which only long sequences have,
+// to a fixed subset of XCDs), and an XCD's items of one sequence are
+// dispatched together, so they stream neighbouring tiles at the same time.
+constexpr int kXcds = 8;
+
+struct WorkItem {
+  int b, part, u;
+  bool live;  // false: padding beyond max_parts * U
+};
+
+__device__ __forceinline__ WorkItem xcd_item(long wg, int U, int max_parts) {
+  const int x = (int)(wg % kXcds);
+  const long t = wg / kXcds;
+  const int K = max_parts * U;
+  const int M = (K + kXcds - 1) / kXcds;
+  WorkItem w;
+  w.b = (int)(t / M);
+  const int m = (int)(t % M);
+  const int xr = (x + kXcds - (w.b % kXcds)) % kXcds;
+  const int k = m * kXcds + xr;
+  w.live = k < K;
+  w.part = k / U;
+  w.u = k % U;
+  return w;
+}
+
+// workgroups of a partition launch (B sequences, U units, max_parts partitions)
+inline long xcd_grid(int B, int U, int max_parts) {
+  const long M = ((long)max_parts * U + kXcds - 1) / kXcds;
+  return (long)B * M * kXcds;
+}
+
 __device__ __forceinline__ void report(int32_t* status, int code) {
   if (status) atomicMin(status, code);
 }

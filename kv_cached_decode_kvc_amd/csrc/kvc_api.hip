@@ -61,36 +61,48 @@ struct Plan {
   int rows_per_item;  // mfma: 16 or 32 rows per wavefront
   int P;              // partition length in tokens
   int max_parts;      // partitions of a full-capacity sequence
+  int units;          // work units of a sequence per partition (rows, or row blocks per KV head)
+  long grid;          // workgroups of the partition launch
   size_t ml_offset;   // byte offset of the (m, l) array inside the workspace
   size_t bytes;       // workspace size
 };
 
-// Work is one wavefront per (rows, partition).  The default partition length
-// is the smallest multiple of 256 keys such that a batch at full capacity
-// gives at most two rounds of resident wavefronts (the kernel's wavefronts
-// per SIMD x 4 SIMDs x 256 CUs; the VALU kernel keeps 5 per SIMD, the MFMA
-// kernel 4 for 16-row blocks and 2 for 32-row blocks); short caches halve it,
-// down to 64, while there would be less than one round.
+// Work is one wavefront per (rows, partition).  A wavefront pays a few
+// dependent memory latencies (length, block ids, first tile) before it
+// streams, and a loaded memory system answers in microseconds, so partitions
+// are long; a full MI355X needs only about 1,300 wavefronts with one 8 KiB
+// tile in flight each to keep HBM busy.  Default partition length: 1024 keys
+// for a contiguous cache (each wavefront streams one long run); for a paged
+// cache the power of two nearest an eighth of the capacity, within [256,
+// 2048], so that sequences of
+// any length still split into a few partitions and the last of them finish
+// together.  It is halved (down to 64) while a full-capacity batch would give
+// fewer than 1024 wavefronts, and doubled (up to 8192) while it would give
+// more than 65536.
 Plan make_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int G = d->num_q_heads / d->num_kv_heads;
   const int R = G * n_q;
   pl.mfma = d->dtype != KVC_F32 && R >= 2;
   pl.rows_per_item = R > 16 ? 32 : 16;
-  const long units = pl.mfma ? (long)d->batch * d->num_kv_heads *
-                                   ((R + pl.rows_per_item - 1) / pl.rows_per_item)
-                             : (long)d->batch * d->num_q_heads * n_q;
+  pl.units = pl.mfma ? d->num_kv_heads * ((R + pl.rows_per_item - 1) / pl.rows_per_item)
+                     : d->num_q_heads * n_q;
+  const long units = (long)d->batch * pl.units;
   const int cap = capacity(d);
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
-    const int waves_per_simd = !pl.mfma ? 5 : (pl.rows_per_item == 16 ? 4 : 2);
-    const long one_round = (long)waves_per_simd * 4 * 256;
-    pl.P = 256;
-    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 2 * one_round) pl.P += 256;
-    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
+    if (d->block_size == 0) {
+      pl.P = 1024;
+    } else {
+      pl.P = 256;
+      while (pl.P < 2048 && pl.P * 2.0 <= cap / 8.0 * 1.4142135623730951) pl.P <<= 1;
+    }
+    while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 1024) pl.P >>= 1;
+    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 65536) pl.P <<= 1;
   }
   pl.max_parts = (cap + pl.P - 1) / pl.P;
+  pl.grid = xcd_grid(d->batch, pl.units, pl.max_parts);
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * d->head_dim * sizeof(float);
   pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
@@ -146,7 +158,9 @@ int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, c
   if ((d->block_size > 0) != (table != nullptr)) return KVC_ERR_ARG;
   if (!isfinite(scale)) return KVC_ERR_ARG;
   if (((uintptr_t)ws & 15) != 0) return KVC_ERR_ARG;
-  if (ws_bytes < make_plan(d, n_q).bytes) return KVC_ERR_WORKSPACE;
+  const Plan pl = make_plan(d, n_q);
+  if (pl.grid > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;  // one workgroup per work item
+  if (ws_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
   return KVC_OK;
 }
 

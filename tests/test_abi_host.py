@@ -102,23 +102,24 @@ def test_paging_argument_errors(lib):
 
 def test_workspace_and_partition_sizes(lib):
     d = desc()  # 16 x 40 heads, contiguous, 2048 tokens
-    assert kvc.kvc_attn_partition_tokens(d, 1) == 256
-    rows, parts = 16 * 40, 2048 // 256
+    assert kvc.kvc_attn_partition_tokens(d, 1) == 1024  # contiguous: long runs
+    rows, parts = 16 * 40, 2048 // 1024
     o = rows * parts * 128 * 4
     assert kvc.kvc_attn_workspace_bytes(d, 1) == ((o + 255) // 256) * 256 + rows * parts * 2 * 4
     small = desc(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=64, max_seq_len=288, dtype=1)
-    assert kvc.kvc_attn_partition_tokens(small, 1) == 64  # halved while fewer than 4096 items
+    assert kvc.kvc_attn_partition_tokens(small, 1) == 64  # halved while fewer than 1024 items
     assert kvc.kvc_attn_partition_tokens(desc(partition_tokens=48), 1) == 48
     assert kvc.kvc_attn_workspace_bytes(desc(head_dim=80), 1) == 0
     assert kvc.kvc_attn_partition_tokens(desc(head_dim=80), 1) == -3
-    for name in ("C2", "C3", "C4", "C5"):
+    # paged: the power of two nearest an eighth of the capacity (4000, 8176, 4112 tokens)
+    for name, want in (("C2", 1024), ("C3", 512), ("C4", 1024), ("C5", 512)):
         w = synth.get(name)
         dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
                   block_size=w.block_size, max_seq_len=synth.capacity_tokens(w),
                   max_blocks_per_seq=synth.max_blocks_per_seq(w) if w.block_size else 0,
                   num_blocks=synth.pool_blocks(w) if w.block_size else 0)
         P = kvc.kvc_attn_partition_tokens(dd, w.n_q)
-        assert P > 0 and P % 16 == 0
+        assert P == want, (name, P)
         assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) > 0
 
 
