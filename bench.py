@@ -10,7 +10,8 @@ time; the cache and all inputs are resident in HBM before the timed region.
 
 Printed: one JSON line.  value = KV bytes attended per step / time per step
 (GB/s); roofline.achieved = the same bytes / the partition kernel's average
-duration, measured with HIP events on the stream the kernels run on.
+duration, measured with HIP events around K back-to-back launches of it on
+the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -457,19 +458,22 @@ def main():
     assert lc.dev_status() == 0, "device status %d" % lc.dev_status()
 
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        lc.step_front()
-        ev0[i].record()
-        lc.step_partition()
-        ev1[i].record()
-        lc.step_reduce()
+        lc.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    assert lc.dev_status() == 0
+    # the dominant kernel alone: K back-to-back launches on the stream the
+    # library launches on (torch's current stream), between two HIP events
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(K):
+        lc.step_partition()
+    ev1.record()
+    torch.cuda.synchronize()
+    part_ms = ev0.elapsed_time(ev1) / K
     assert lc.dev_status() == 0
 
     lens = synth.final_lengths(w)
