@@ -33,9 +33,12 @@
  * Layouts (element = 2 bytes for KVC_BF16, 4 for KVC_F32, 1 for FP8; row-major)
  *   contiguous cache (block_size == 0): k_cache, v_cache [batch][num_kv_heads][max_seq_len][head_dim]
  *   paged pool       (block_size  > 0): k_cache, v_cache [num_blocks][num_kv_heads][block_size][head_dim]
- *   FP8 caches: each buffer holds those codes (rows x head_dim bytes) and then,
- *                at the next multiple of 256 bytes, one float32 scale per row
- *                in the same row order; kvc_cache_bytes() gives the size.  A
+ *   FP8 caches: rows are numbered as above (a contiguous cache pads each
+ *                (sequence, head) run to a multiple of 16 rows) and stored in
+ *                tiles of 16 consecutive rows: tile t is the bytes
+ *                [t * (16 * head_dim + 64), (t + 1) * (16 * head_dim + 64)),
+ *                the 16 rows' codes (head_dim bytes each) followed by their
+ *                16 float32 scales; kvc_cache_bytes() gives the size.  A
  *                row's scale s is its largest |x| over the format's largest
  *                value and each code is the nearest FP8 value to x / s (ties
  *                to even, saturating); the cached value is code * s.

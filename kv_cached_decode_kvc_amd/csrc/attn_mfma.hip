@@ -143,8 +143,10 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
   uint4 kreg[U], vreg[U];
   float ks_next[4], vs_next[4];  // FP8: scales of keys grp*4 .. +3 of the tile in flight
   auto load_tile = [&](int tile, long tb) {
-    const uint8_t* kt = (const uint8_t*)p.k + tb * EB;  // uniform bases, 32-bit lane offsets
-    const uint8_t* vt = (const uint8_t*)p.v + tb * EB;
+    // uniform bases, 32-bit lane offsets; FP8: the tile's run of codes, then scales
+    const long tbyte = F ? (tb / (16 * D)) * fp8_tile_bytes(D) : tb * EB;
+    const uint8_t* kt = (const uint8_t*)p.k + tbyte;
+    const uint8_t* vt = (const uint8_t*)p.v + tbyte;
     const int last = min(kTile, end - tile) - 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -154,12 +156,14 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
       vreg[u] = load_stream(vt + off);
     }
     if constexpr (F != 0) {
-      const long row0 = tb / D;  // cache row of the tile's first key
+      // scales of keys grp*4 .. +3, non-temporal like the codes (a cached
+      // load would allocate in the last-level caches and wait on their
+      // evictions); masked keys re-read a visible row's scale
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int key = min(grp * 4 + v, last);
-        ks_next[v] = p.k_scale[row0 + key];
-        vs_next[v] = p.v_scale[row0 + key];
+        ks_next[v] = __builtin_nontemporal_load(reinterpret_cast<const float*>(kt + 16 * D + key * 4));
+        vs_next[v] = __builtin_nontemporal_load(reinterpret_cast<const float*>(vt + 16 * D + key * 4));
       }
     }
   };

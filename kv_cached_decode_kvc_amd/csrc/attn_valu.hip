@@ -209,9 +209,9 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
         const int ti = tile + i * stride;
         nvalid[i] = 0;
         if (ti >= end) continue;
-        long tbase;  // element offset of key `ti` of (b, g)
+        long row0;  // cache row of key `ti` of (b, g)
         if (!paged) {
-          tbase = (((long)b * p.Hkv + g) * p.S_max + ti) * D;
+          row0 = ((long)b * p.Hkv + g) * p.S_max + ti;
         } else {
           const int ii = idx + i;
           if (ii > 0 && (ii & (kWave - 1)) == 0) {  // the next 64 tiles' ids
@@ -223,19 +223,29 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
             if (lane == 0) report(p.status, KVC_ERR_DATA);
             continue;
           }
-          tbase = (((long)blk * p.Hkv + g) * p.bs + (ti % p.bs)) * D;
+          row0 = ((long)blk * p.Hkv + g) * p.bs + (ti % p.bs);
         }
         nvalid[i] = min(kTile, end - ti);  // >= 1
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           int tt = u * RPL + r0;
           tt = tt < nvalid[i] ? tt : nvalid[i] - 1;  // masked lanes re-read a visible row
-          const long off = tbase + (long)tt * D + c * VE;
-          kr[i][u] = load_stream(kbase + off);
-          vr[i][u] = load_stream(vbase + off);
-          if constexpr (kF8) {
-            ksc[i][u] = p.k_scale[tbase / D + tt];
-            vsc[i][u] = p.v_scale[tbase / D + tt];
+          if constexpr (kF8) {  // row0 starts a 16-row tile: codes, then scales
+            const long t0 = (row0 >> 4) * fp8_tile_bytes(D);
+            const long off = t0 + (long)tt * D + c * VE;
+            kr[i][u] = load_stream(kbase + off);
+            vr[i][u] = load_stream(vbase + off);
+            // scales: non-temporal like the codes (a cached load would
+            // allocate in the last-level caches and wait on their evictions)
+            const long so = t0 + 16L * D + tt * 4;
+            ksc[i][u] = __builtin_nontemporal_load(
+                reinterpret_cast<const float*>((const uint8_t*)p.k + so));
+            vsc[i][u] = __builtin_nontemporal_load(
+                reinterpret_cast<const float*>((const uint8_t*)p.v + so));
+          } else {
+            const long off = (row0 + tt) * D + c * VE;
+            kr[i][u] = load_stream(kbase + off);
+            vr[i][u] = load_stream(vbase + off);
           }
         }
       }

@@ -32,8 +32,6 @@ struct AttnParams {
   int P, max_parts;
   int cap;               // tokens a sequence may hold
   float scale_log2;      // scale * log2(e): scores go straight into exp2
-  const float* k_scale;  // FP8 caches: one scale per cache row (token, KV head)
-  const float* v_scale;
 };
 
 struct PrefillParams {
@@ -197,6 +195,22 @@ struct Fp8Format<kFp8E5M2> {
   static constexpr float kMax = 57344.f;
   static constexpr uint32_t kTop = 0x7B;
 };
+
+// FP8 cache layout.  Rows are numbered as in a bf16 cache (a contiguous cache
+// pads every (sequence, head) run to a multiple of 16 rows) and grouped in
+// tiles of 16 consecutive rows; tile t occupies bytes [t * TB, (t + 1) * TB)
+// of the buffer, TB = 16 * D + 64: the 16 rows' codes, then their 16 float32
+// scales.  A kernel reading one 16-key tile of one head finds its codes and
+// scales in one run of TB bytes, instead of a 64-byte scale read in a distant
+// region for every tile (which costs HBM a row activation per 64 bytes).
+__host__ __device__ __forceinline__ long fp8_tile_bytes(int D) { return 16L * D + 64; }
+__host__ __device__ __forceinline__ long fp8_code_offset(long row, int D) {
+  return (row >> 4) * fp8_tile_bytes(D) + (row & 15) * (long)D;
+}
+__host__ __device__ __forceinline__ long fp8_scale_offset(long row, int D) {
+  return (row >> 4) * fp8_tile_bytes(D) + 16L * D + (row & 15) * 4;
+}
+__host__ __device__ __forceinline__ long fp8_padded_rows(long rows) { return (rows + 15) & ~15L; }
 
 // Code of the FP8 value nearest to the finite y, ties to the even code,
 // saturated to the largest finite value.  Scaling by powers of two is exact,

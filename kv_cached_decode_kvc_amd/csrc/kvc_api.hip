@@ -46,14 +46,12 @@ size_t elem_bytes(const kvc_cache_desc* d) {
 }
 size_t input_bytes(const kvc_cache_desc* d) { return d->dtype == KVC_F32 ? 4 : 2; }
 
+// rows of one cache buffer; an FP8 contiguous cache pads each (sequence, head)
+// run to whole 16-row tiles
 size_t cache_rows(const kvc_cache_desc* d) {
-  return d->block_size ? (size_t)d->num_blocks * d->num_kv_heads * d->block_size
-                       : (size_t)d->batch * d->num_kv_heads * d->max_seq_len;
-}
-
-// FP8: byte offset of the scales inside a cache buffer (after the codes)
-size_t scale_offset(const kvc_cache_desc* d) {
-  return (cache_rows(d) * d->head_dim + 255) & ~(size_t)255;
+  if (d->block_size) return (size_t)d->num_blocks * d->num_kv_heads * d->block_size;
+  const long s = fp8_format(d) ? fp8_padded_rows(d->max_seq_len) : d->max_seq_len;
+  return (size_t)d->batch * d->num_kv_heads * s;
 }
 
 struct Plan {
@@ -76,7 +74,8 @@ struct Plan {
 // cache the power of two nearest an eighth of the capacity, within [256,
 // 2048], so that sequences of
 // any length still split into a few partitions and the last of them finish
-// together.  It is halved (down to 64) while a full-capacity batch would give
+// together; at most 512 for FP8 caches, whose wavefronts move half the bytes
+// per key.  It is halved (down to 64) while a full-capacity batch would give
 // fewer than 1024 wavefronts, and doubled (up to 8192) while it would give
 // more than 65536.
 Plan make_plan(const kvc_cache_desc* d, int n_q) {
@@ -98,6 +97,7 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
       pl.P = 256;
       while (pl.P < 2048 && pl.P * 2.0 <= cap / 8.0 * 1.4142135623730951) pl.P <<= 1;
     }
+    if (fp8_format(d) && pl.P > 512) pl.P = 512;  // half the bytes per key: more wavefronts
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 1024) pl.P >>= 1;
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 65536) pl.P <<= 1;
   }
@@ -190,10 +190,7 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  if (fp8_format(d)) {
-    p.k_scale = (const float*)((const char*)k + scale_offset(d));
-    p.v_scale = (const float*)((const char*)v + scale_offset(d));
-  }
+  if (fp8_format(d) && d->block_size == 0) p.S_max = (int)fp8_padded_rows(d->max_seq_len);
   return p;
 }
 
@@ -260,7 +257,6 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
   a.head_bytes = (int)(d->head_dim * input_bytes(d));  // bytes of one new row of one head
   a.fp8 = fp8_format(d);
   a.D = d->head_dim;
-  a.scale_off = fp8_format(d) ? (long)scale_offset(d) : 0;
   a.bs = d->block_size;
   a.S_max = d->max_seq_len;
   a.N = d->num_blocks;
@@ -407,11 +403,10 @@ int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* 
   c.dst = dst;
   c.k = (uint8_t*)k_cache;
   c.v = (uint8_t*)v_cache;
-  c.block_bytes = (long)d->num_kv_heads * d->block_size * d->head_dim * (long)elem_bytes(d);
-  if (fp8_format(d)) {
-    c.scale_off = (long)scale_offset(d);
-    c.scale_bytes = d->num_kv_heads * d->block_size * (int)sizeof(float);
-  }
+  c.block_bytes = fp8_format(d) ? (long)d->num_kv_heads * (d->block_size / kTile) *
+                                      fp8_tile_bytes(d->head_dim)
+                                : (long)d->num_kv_heads * d->block_size * d->head_dim *
+                                      (long)elem_bytes(d);
   c.N = d->num_blocks;
   c.status = dev_status;
   return hip_status(launch_copy_blocks(c, n, (hipStream_t)stream));
@@ -562,7 +557,7 @@ int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q
 
 size_t kvc_cache_bytes(const kvc_cache_desc* d) {
   if (check_desc(d) != KVC_OK) return 0;
-  if (fp8_format(d)) return scale_offset(d) + cache_rows(d) * sizeof(float);
+  if (fp8_format(d)) return cache_rows(d) / kTile * (size_t)fp8_tile_bytes(d->head_dim);
   return cache_rows(d) * d->head_dim * elem_bytes(d);
 }
 

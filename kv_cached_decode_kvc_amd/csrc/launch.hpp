@@ -33,8 +33,7 @@ struct AppendArgs {
   int B, Hkv, head_bytes, bs, S_max, N, max_new, total_new;
   int tok_per_wg;  // set by the launcher
   int fp8;         // 0: rows copied bit for bit; kFp8E4M3 / kFp8E5M2: bf16 rows quantized
-  int D;           // FP8: codes per row
-  long scale_off;  // FP8: byte offset of the per-row scales inside each cache buffer
+  int D;           // FP8: codes per row (16-row tiles of codes and scales, common.hpp)
 };
 
 constexpr int kMaxBatch = 65536;        // sequences per call (one grid row each)
@@ -63,9 +62,7 @@ struct CopyArgs {
   const int32_t* dst;
   uint8_t* k;
   uint8_t* v;
-  long block_bytes;  // element bytes of one pool block (all KV heads)
-  long scale_off;    // FP8: byte offset of the per-row scales (0: none)
-  int scale_bytes;   // FP8: scale bytes of one pool block
+  long block_bytes;  // bytes of one pool block (all KV heads; FP8: codes and scales)
   int N;
   int32_t* status;
 };

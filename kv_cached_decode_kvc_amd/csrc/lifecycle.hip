@@ -249,15 +249,6 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
     return;
   }
   const long off = ((long)blockIdx.x * kCopyThreads + threadIdx.x) * 16;
-  if (off < a.scale_bytes) {  // FP8 pools: the block's per-row scales travel with it
-    const long so = a.scale_off + off;
-    const uint4 ks = *reinterpret_cast<const uint4*>(a.k + so + (long)src * a.scale_bytes);
-    *reinterpret_cast<uint4*>(a.k + so + (long)dst * a.scale_bytes) = ks;
-    if (a.v) {
-      const uint4 vs = *reinterpret_cast<const uint4*>(a.v + so + (long)src * a.scale_bytes);
-      *reinterpret_cast<uint4*>(a.v + so + (long)dst * a.scale_bytes) = vs;
-    }
-  }
   if (off >= a.block_bytes) return;
   const uint4 kv = *reinterpret_cast<const uint4*>(a.k + (long)src * a.block_bytes + off);
   *reinterpret_cast<uint4*>(a.k + (long)dst * a.block_bytes + off) = kv;

@@ -252,8 +252,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
   if (idx >= vec_per_tok) return;  // whole rows: vec_per_tok is a multiple of the row's lanes
   const int g = idx / vec_per_head;
   const int w = idx - g * vec_per_head;
-  float* k_scale = reinterpret_cast<float*>(a.k_cache + a.scale_off);
-  float* v_scale = reinterpret_cast<float*>(a.v_cache + a.scale_off);
+  const long s_row = fp8_padded_rows(a.S_max);  // contiguous: rows per (sequence, head)
   const int t0 = tchunk * tok_per_wg;
   const int t1 = min(t0 + tok_per_wg, n);
   for (int t = t0; t < t1; ++t) {  // every lane of a row takes the same branches
@@ -271,7 +270,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
       }
       row = ((slot / a.bs) * a.Hkv + g) * a.bs + slot % a.bs;
     } else {
-      row = ((long)b * a.Hkv + g) * a.S_max + len + t;
+      row = ((long)b * a.Hkv + g) * s_row + len + t;
     }
     const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
     const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
@@ -282,12 +281,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
       vm = fmaxf(vm, __shfl_xor(vm, off));
     }
     const float ks = __fdiv_rn(km, Fm::kMax), vs = __fdiv_rn(vm, Fm::kMax);
-    const long dst = row * a.D + w * 8;
+    const long dst = fp8_code_offset(row, a.D) + w * 8;
     *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8<F>(kx, ks);
     *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8<F>(vx, vs);
     if (w == 0) {
-      k_scale[row] = ks;
-      v_scale[row] = vs;
+      const long so = fp8_scale_offset(row, a.D);
+      *reinterpret_cast<float*>(a.k_cache + so) = ks;
+      *reinterpret_cast<float*>(a.v_cache + so) = vs;
     }
   }
 }

@@ -86,13 +86,26 @@ class LayerCache:
         self.scale = 1.0 / math.sqrt(w.D)
 
     def fp8_parts(self, which: str):
-        """FP8 cache: (codes uint8 [*shape], scales float32 [*shape[:-1]]) views."""
+        """FP8 cache: views of its 16-row tiles, codes uint8 [lead0, lead1,
+        tiles, 16, D] and scales float32 [lead0, lead1, tiles, 16], where
+        (lead0, lead1) = (blocks, KV heads) or (batch, KV heads) and a
+        contiguous cache's rows are padded to whole tiles."""
         buf = self.k if which == "k" else self.v
-        rows = int(np.prod(self.shape[:-1]))
-        off = (rows * self.w.D + 255) // 256 * 256
-        codes = buf[:rows * self.w.D].view(self.shape)
-        scales = buf[off:off + 4 * rows].view(torch.float32).view(self.shape[:-1])
+        D = self.w.D
+        tb = 16 * D + 64  # one tile: 16 rows of codes, then their 16 scales
+        rows = -(-self.shape[2] // 16) * 16
+        lead = (self.shape[0], self.shape[1], rows // 16)
+        tiles = buf[:int(np.prod(lead)) * tb].view(-1, tb)
+        codes = tiles[:, :16 * D].view(*lead, 16, D)
+        scales = tiles[:, 16 * D:].view(torch.float32).view(*lead, 16)
         return codes, scales
+
+    def fp8_rows(self, which: str):
+        """FP8 cache on the host, row by row: (codes [lead0, lead1, rows, D],
+        scales [lead0, lead1, rows]) numpy arrays."""
+        codes, scales = (t.cpu().numpy() for t in self.fp8_parts(which))
+        c, s = codes.reshape(*codes.shape[:2], -1, codes.shape[-1]), scales.reshape(*scales.shape[:2], -1)
+        return c[:, :, :self.shape[2]], s[:, :, :self.shape[2]]
 
     # -- building the cache ----------------------------------------------
     def add_tokens(self, k_rows: np.ndarray, v_rows: np.ndarray, counts):

@@ -18,8 +18,7 @@ pytestmark = pytest.mark.gpu
 
 def gpu_rows(gc, which, b, L):
     """Sequence b's first L rows of the FP8 cache: (codes [Hkv, L, D], scales [Hkv, L])."""
-    codes, scales = gc.fp8_parts(which)
-    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    codes, scales = gc.fp8_rows(which)
     if gc.bs == 0:
         return codes[b, :, :L], scales[b, :, :L]
     table = gc.table.cpu().numpy()
