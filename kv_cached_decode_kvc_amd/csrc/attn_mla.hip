@@ -13,24 +13,28 @@
 //
 // Every query row of a sequence (Hq heads x n_q verify rows) reads the same
 // latent rows, so a workgroup of four wavefronts owns one (sequence, group of
-// up to 64 rows, partition): its threads load each 16-key tile (16 x 1152
-// bytes, one contiguous run) cooperatively into one LDS tile, and each
-// wavefront contracts its 16 rows against it on the matrix cores:
+// rows, partition): its threads load each 16-key tile (16 x 1152 bytes, one
+// contiguous run) cooperatively into one LDS tile, and each wavefront
+// contracts a block of 16 rows against it on the matrix cores:
 //   S^T = K . Q^T   (18 steps of v_mfma_f32_16x16x32_bf16, Q^T in registers)
-//   O^T += V^T . P^T (32 column tiles; V^T via ds_read_b64_tr_b16; the
-//                     weights as bf16 hi + lo pairs along the reduction index,
-//                     as in the grouped-query kernel).
+//   O^T += V^T . P^T (its column tiles of the 512; V^T via ds_read_b64_tr_b16;
+//                     the weights as bf16 hi + lo pairs along the reduction
+//                     index, as in the grouped-query kernel).
 // Online softmax per row as in the other partition kernels; verify row r
 // sees keys 0 .. L - n_q + r.
 //
-// A wavefront holds 16 rows of queries (72 VGPRs) and of 512-wide fp32
-// accumulators (128), so it runs alone on its SIMD (512 registers) and a
-// workgroup fills a CU.  Two LDS tiles let the score products of tile n + 1
-// be issued before the softmax of tile n, which does not depend on them;
-// a ring of PF register stages keeps the following tiles in flight.  Row groups of the same (sequence,
-// partition) get workgroup ids 8 apart: launches place workgroup i on XCD
-// i mod 8, so they share one XCD's L2 and run at the same time, and the tile
-// comes from HBM once.
+// C wavefronts share a row block and split its 512 output columns (C = 1, 2
+// or 4): each computes the block's scores and softmax itself (cheap next to
+// the value products) and accumulates 512 / C columns.  With C = 1 a
+// wavefront holds 16 rows of queries (72 VGPRs) and 512-wide fp32
+// accumulators (128) and runs alone on its SIMD; with C >= 2 two fit per
+// SIMD, and a sequence with only 16 rows (16 heads) still keeps all four
+// wavefronts of its workgroup busy.  Two LDS tiles let the score products of
+// tile n + 1 be issued before the softmax of tile n, which does not depend on
+// them; a ring of PF register stages keeps the following tiles in flight.
+// Row groups of the same (sequence, partition) get workgroup ids 8 apart:
+// launches place workgroup i on XCD i mod 8, so they share one XCD's L2 and
+// run at the same time, and the tile comes from HBM once.
 #include "launch.hpp"
 
 namespace kvc {
@@ -46,13 +50,14 @@ constexpr int kMlaThreads = kMlaWaves * kWave;
 
 }  // namespace
 
-template <int PF>
-__global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
+template <int PF, int C>
+__global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(AttnParams p) {
   constexpr int NT = 1;
   constexpr int DK = kMlaKeyDim;          // 576
   constexpr int DV = kMlaValueDim;        // 512
   constexpr int KK = DK / 32;             // 18 QK^T steps
-  constexpr int DT = DV / 16;             // 32 output column tiles
+  constexpr int DT = DV / 16 / C;         // output column tiles of one wavefront
+  constexpr int RB = kMlaWaves / C;       // row blocks of a workgroup
   constexpr int CPR = DK * 2 / 16;        // 72 16-byte chunks per row
   constexpr int TCH = kTile * CPR;        // 1152 chunks per tile
   constexpr int PER = (TCH + kMlaThreads - 1) / kMlaThreads;  // chunks per thread
@@ -66,7 +71,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
   const int grp = lane >> 4;
 
   const int R = p.Hq * p.n_q;                 // rows sharing the latent cache
-  const int rows_wg = 16 * NT * kMlaWaves;
+  const int rows_wg = 16 * NT * RB;
+  const int cc = wave % C;                    // this wavefront's column chunk
   const int n_rg = (R + rows_wg - 1) / rows_wg;
   // workgroup id = (chunk * n_rg + rg) * 8 + j: unit (sequence, partition)
   // = chunk * 8 + j, so its row groups sit 8 ids apart on one XCD
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
   bool any_row = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int i = (rg * kMlaWaves + wave) * 16 * NT + nt * 16 + col;
+    const int i = (rg * RB + wave / C) * 16 * NT + nt * 16 + col;
     rvalid[nt] = i < R;
     const int r = rvalid[nt] ? i / p.Hq : 0;
     const int h = rvalid[nt] ? i % p.Hq : 0;
@@ -179,15 +185,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
   constexpr float kLazy = 8.f;
   auto qk = [&](int buf) -> f32x4_t {  // S^T of the tile in `buf`: this lane's 4 keys of row col
     const uint8_t* ka = lds[buf] + col * ROWB + grp * 16;
-    bf16x8_t kf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + kk * 64));
+    constexpr int KG = C == 1 ? KK : 6;  // K fragments read per batch (registers)
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
-    for (int kk = 0; kk < KK; kk += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[0][kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk + 1], qf[0][kk + 1], s1, 0, 0, 0);
+    for (int k0 = 0; k0 < KK; k0 += KG) {
+      bf16x8_t kf[KG];
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk)
+        kf[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + (k0 + kk) * 64));
+#pragma unroll
+      for (int kk = 0; kk < KG; kk += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[0][k0 + kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk + 1], qf[0][k0 + kk + 1], s1, 0, 0, 0);
+      }
     }
     return s0 + s1;
   };
@@ -221,8 +231,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
                                    0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto pv = [&](int buf, const bf16x8_t& pb) {  // O^T += V^T . P^T, value fragments in groups
-    const uint8_t* va_ptr = lds[buf] + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
-    constexpr int VG = 8;
+    const uint8_t* va_ptr =
+        lds[buf] + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8 + cc * (DV / C) * 2;
+    constexpr int VG = DT < 8 ? DT : 8;
     auto read_v = [&](bf16x4_t (&va)[VG], int g) {
 #pragma unroll
       for (int i = 0; i < VG; ++i) {
@@ -295,11 +306,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
     float lt = l[nt] + __shfl_xor(l[nt], 16);
     lt += __shfl_xor(lt, 32);
     if (!rvalid[nt]) continue;
-    float* wo = p.ws_o + (wrow[nt] * p.max_parts + part) * DV;
+    float* wo = p.ws_o + (wrow[nt] * p.max_parts + part) * DV + cc * (DV / C);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<f32x4_t*>(wo + dt * 16 + grp * 4) = oacc[nt][dt];
-    if (grp == 0) {
+    if (grp == 0 && cc == 0) {  // every column chunk holds the same statistics
       float* wml = p.ws_ml + (wrow[nt] * p.max_parts + part) * 2;
       wml[0] = m[nt];
       wml[1] = lt;
@@ -307,14 +318,24 @@ __global__ __launch_bounds__(kMlaThreads, 1) void partition_mla(AttnParams p) {
   }
 }
 
+// Up to 16 rows (one row block): four wavefronts split the columns, so all of
+// them compute.  More rows: each wavefront owns a row block with all 512
+// columns (with two per block the accumulators and stages no longer fit two
+// wavefronts per SIMD without spilling, measured 1.7x slower).
+int mla_col_split(int rows) { return rows <= 16 ? 4 : 1; }
+
 hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s) {
   const int R = p.Hq * p.n_q;
-  const long n_rg = (R + 16 * kMlaWaves - 1) / (16 * kMlaWaves);
+  const int C = mla_col_split(R);
+  const long rows_wg = 16L * (kMlaWaves / C);
+  const long n_rg = (R + rows_wg - 1) / rows_wg;
   const long units = (long)p.B * p.max_parts;
   const long n_wg = (units + 7) / 8 * 8 * n_rg;
   if (units == 0) return hipSuccess;
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((partition_mla<2>), dim3((unsigned)n_wg), dim3(kMlaThreads), 0, s, p);
+  const dim3 grid((unsigned)n_wg), block(kMlaThreads);
+  if (C == 4) hipLaunchKernelGGL((partition_mla<2, 4>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((partition_mla<2, 1>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

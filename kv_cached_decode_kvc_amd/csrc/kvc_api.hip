@@ -113,9 +113,12 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
 // MLA latent decode: one bf16 latent head of 576 (512 latent + 64 RoPE key),
-// values = the 512-wide latent.  A workgroup of four wavefronts covers 64 query
-// rows and fills a CU, so a round of resident work is 256 workgroups; the
-// partition length follows the same rule as make_plan with that round.
+// values = the 512-wide latent.  A workgroup of four wavefronts covers 64 /
+// C query rows (C wavefronts per 16-row block split the output columns); it
+// fills a CU when C = 1 and two fit per CU otherwise, so a round of resident
+// work is 256 or 512 workgroups.  The partition length grows in steps of 256
+// keys until a full-capacity batch gives at most two rounds, and halves
+// (down to 64) while it would give less than one.
 int check_mla(const kvc_cache_desc* d, int n_q, int value_dim) {
   const int st = check_desc(d);
   if (st != KVC_OK) return st;
@@ -127,13 +130,16 @@ int check_mla(const kvc_cache_desc* d, int n_q, int value_dim) {
 
 Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
-  const long n_rg = ((long)d->num_q_heads * n_q + 63) / 64;
+  const int R = d->num_q_heads * n_q;
+  const int C = mla_col_split(R);
+  const long rows_wg = 16L * (4 / C);  // four wavefronts, C per 16-row block
+  const long n_rg = (R + rows_wg - 1) / rows_wg;
   const long units = (long)d->batch * n_rg;
   const int cap = capacity(d);
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
-    const long one_round = 256;
+    const long one_round = C == 1 ? 256 : 512;  // workgroups resident at once
     pl.P = 256;
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 2 * one_round) pl.P += 256;
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
