@@ -117,8 +117,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 // C query rows (C wavefronts per 16-row block split the output columns); it
 // fills a CU when C = 1 and two fit per CU otherwise, so a round of resident
 // work is 256 or 512 workgroups.  The partition length grows in steps of 256
-// keys until a full-capacity batch gives at most two rounds, and halves
-// (down to 64) while it would give less than one.
+// keys until a full-capacity batch fits in one round (a workgroup then
+// streams its partition without a second round behind it; two rounds
+// measured 10-12% slower), and halves (down to 64) while it would not fill
+// one.
 int check_mla(const kvc_cache_desc* d, int n_q, int value_dim) {
   const int st = check_desc(d);
   if (st != KVC_OK) return st;
@@ -141,7 +143,7 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   } else {
     const long one_round = C == 1 ? 256 : 512;  // workgroups resident at once
     pl.P = 256;
-    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 2 * one_round) pl.P += 256;
+    while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > one_round) pl.P += 256;
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
   }
   pl.max_parts = (cap + pl.P - 1) / pl.P;
