@@ -24,6 +24,21 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const int b = (int)(bh / p.Hq);
   const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + lane * CPL;
 
+  // One round trip: the length, the first kEarly partitions' outputs for this
+  // lane's columns and one partition's (m, l) per lane are all requested
+  // together, for every partition slot the workspace has (slots beyond the
+  // sequence's partitions hold stale bytes and are discarded by selection,
+  // never multiplied, once the length is known).
+  constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
+  const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
+  float early[kEarly][CPL];
+#pragma unroll
+  for (int j = 0; j < kEarly; ++j)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) early[j][c] = j < p.max_parts ? po[(long)j * D + c] : 0.f;
+  float2 mine_raw = make_float2(-INFINITY, 0.f);
+  if (lane < p.max_parts) mine_raw = ml[lane];
   const int L = p.seq_lens[b];
   float acc[CPL];
 #pragma unroll
@@ -31,18 +46,11 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   float den = 0.f;
   if (L >= p.n_q && L <= p.cap) {
     const int nparts = (L + p.P - 1) / p.P;
-    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
-    const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
-    // Round trip 1: every lane fetches one partition's (m, l) and, independently,
-    // the first kEarly partitions' outputs for its columns.
-    constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
-    float early[kEarly][CPL];
 #pragma unroll
     for (int j = 0; j < kEarly; ++j)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) early[j][c] = j < nparts ? po[(long)j * D + c] : 0.f;
-    float2 mine = make_float2(-INFINITY, 0.f);
-    if (lane < nparts) mine = ml[lane];
+      for (int c = 0; c < CPL; ++c) early[j][c] = j < nparts ? early[j][c] : 0.f;
+    const float2 mine = lane < nparts ? mine_raw : make_float2(-INFINITY, 0.f);
     float mstar = mine.x;
     for (int q0 = kWave; q0 < nparts; q0 += kWave)  // more than 64 partitions
       if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[q0 + lane].x);
