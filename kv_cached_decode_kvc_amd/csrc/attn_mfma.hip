@@ -93,6 +93,12 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
     qoff[nt] = (((long)b * p.n_q + r) * p.Hq + h) * D;
     wrow[nt] = ((long)b * p.Hq + h) * p.n_q + r;
   }
+  // keys every row of this wavefront sees: tiles below it need no mask
+  int vis_min = lvis[0];
+#pragma unroll
+  for (int nt = 1; nt < NT; ++nt) vis_min = min(vis_min, lvis[nt]);
+  for (int mm = 1; mm < kWave; mm <<= 1) vis_min = min(vis_min, __shfl_xor(vis_min, mm));
+  vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
   // Q^T as the B operand of S^T = K Q^T: lane holds Q[row col][kk*32 + grp*8 .. +8]
   bf16x8_t qf[NT][KK];
@@ -235,7 +241,11 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
           const int key0 = tile + grp * 4;
           float sv[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * sl[v] : -INFINITY;
+          for (int v = 0; v < 4; ++v) sv[v] = s[v] * sl[v];
+          if (tile + kTile > vis_min) {  // the tile reaches past some row's last key
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? sv[v] : -INFINITY;
+          }
           float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
           mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));

@@ -80,6 +80,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
     wave_vis = max(wave_vis, lvis[nt]);
   }
   for (int m = 1; m < kWave; m <<= 1) wave_vis = max(wave_vis, __shfl_xor(wave_vis, m));
+  // keys every valid row of this wavefront sees: tiles below it need no mask
+  int vis_min = 0x7fffffff;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) vis_min = min(vis_min, rvalid[nt] ? lvis[nt] : 0x7fffffff);
+  for (int m = 1; m < kWave; m <<= 1) vis_min = min(vis_min, __shfl_xor(vis_min, m));
+  vis_min = __builtin_amdgcn_readfirstlane(vis_min);
   // keys the workgroup needs: up to its last row's position
   const int last_row = min(row0 + rows_wg, R) - 1;
   const int end = cached + last_row / p.G + 1;  // <= L
@@ -174,7 +180,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       const int key0 = t16 + grp * 4;
       float sv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? s[v] * p.scale_log2 : -INFINITY;
+      for (int v = 0; v < 4; ++v) sv[v] = s[v] * p.scale_log2;
+      if (t16 + 16 > vis_min) {  // the tile reaches past some row's last key
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? sv[v] : -INFINITY;
+      }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));

@@ -264,3 +264,39 @@ def test_peaked_weights_large_values(ref, n_q):
     st, want = ref.cache_attention(q, kc, vc, lens, scale, "bf16")
     assert st == 0
     assert_close(got, want, "peaked n_q=%d" % n_q)
+
+
+@pytest.mark.parametrize("dv", [0, 512])
+def test_stale_workspace_bytes_do_not_matter(dv):
+    """The reduce requests every partition slot of a row before it knows the
+    row's partition count and discards the extra slots by selection: a
+    workspace full of NaN (stale bytes) gives the same outputs bit for bit.
+    Lengths from 1 to 700 with 32-key partitions give rows with 1 to 22
+    partitions (past the 16 the reduce fetches early) next to unused slots."""
+    if dv:
+        w = synth.custom(name="ws-mla", seed=77, B=5, Hq=16, Hkv=1, D=576, dtype="bf16",
+                         block_size=64, n_q=1, len_lo=1, len_hi=700, dv=512)
+    else:
+        w = synth.custom(name="ws", seed=77, B=5, Hq=8, Hkv=2, D=128, dtype="bf16",
+                         block_size=16, n_q=1, len_lo=1, len_hi=700)
+    lengths = synth.final_lengths(w)
+    for P in (32, 0):
+        gc = GpuCache(w, partition_tokens=P)
+        gc.prefill(lengths - 1)
+        gc.step_rows(0)
+        q = queries_dev(w)
+        outs = []
+        for fill in (0.0, float("nan")):
+            ws = gc.workspace(1)
+            ws.fill_(fill)
+            out = torch.empty((w.B, 1, w.Hq, w.out_dim), dtype=torch.float32, device="cuda")
+            if dv:
+                kvc.kvc_mla_attn(gc.desc, q, 1, gc.k, gc.seq_lens, gc.table, dv, gc.scale, out, ws,
+                                 gc.status)
+            else:
+                kvc.kvc_decode_attn(gc.desc, q, gc.k, gc.v, gc.seq_lens, gc.table, gc.scale, out,
+                                    ws, gc.status)
+            outs.append(out)
+        assert gc.dev_status() == 0
+        assert bool(torch.isfinite(outs[1]).all()), P
+        assert torch.equal(outs[0], outs[1]), P
