@@ -148,6 +148,15 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
     if (blk < 0 || blk >= p.N) return -1;
     return ((long)blk * p.bs + (tile & (p.bs - 1))) * DK;
   };
+  // this thread's chunks of a tile: row and byte offset within the row
+  int frow[PER];
+  uint32_t fchk[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = min(u * kMlaThreads + tid, TCH - 1);  // extra threads repeat the last chunk
+    frow[u] = idx / CPR;
+    fchk[u] = (uint32_t)(idx % CPR) * 16;
+  }
   uint4 stage[PF][PER];  // ring of register stages
   long stb[PF];          // tile base of each stage (-1: none or bad block)
   // Every stage issues exactly PER loads, whatever the tile (past the end of
@@ -159,16 +168,13 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
     const bool in = tile < end;
     const long tb = tile_base(in ? n : 0);
     tbs = in ? tb : -1;
-    const uint16_t* base = (const uint16_t*)p.k + (tb >= 0 ? tb : 0);
-    const int last = in ? min(kTile, end - tile) - 1 : 0;
+    // past the end (or a bad block) the rows clamp to the cache's first row:
+    // one row's worth of lines, so the padding steps cost no HBM traffic
+    const uint8_t* base = (const uint8_t*)p.k + (tbs >= 0 ? tb : 0) * 2;
+    const int last = tbs >= 0 ? min(kTile, end - tile) - 1 : 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      // past the end (or a bad block) every thread reads the cache's first 16
-      // bytes: one cache line, so the padding steps cost no HBM traffic
-      const int idx = tbs >= 0 ? min(u * kMlaThreads + tid, TCH - 1) : 0;
-      const int row = min(idx / CPR, last);  // masked keys re-read a visible row
-      st[u] = load_stream(base + row * DK + (idx % CPR) * 8);
-    }
+    for (int u = 0; u < PER; ++u)  // masked keys re-read a visible row
+      st[u] = load_stream(base + ((uint32_t)min(frow[u], last) * (DK * 2) + fchk[u]));
   };
   auto store_tile = [&](int buf, const uint4 (&st)[PER]) {
 #pragma unroll
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
   constexpr float kLazy = 8.f;
   auto qk = [&](int buf) -> f32x4_t {  // S^T of the tile in `buf`: this lane's 4 keys of row col
     const uint8_t* ka = lds[buf] + col * ROWB + grp * 16;
-    constexpr int KG = C == 1 ? KK : 6;  // K fragments read per batch (registers)
+    constexpr int KG = 6;  // K fragments read per batch (registers)
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
     for (int k0 = 0; k0 < KK; k0 += KG) {
@@ -284,9 +290,17 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
         if (active) {
           s_next = qk(1 - j);  // tile n + 1 (results unused past the end)
           const bf16x8_t pb = softmax(s_cur, start + n * stride, bok[j]);
-          if (rescale) {
+          if (__builtin_expect(rescale, 0)) {
+            // The empty asm statements hand the accumulators to the vector
+            // ALUs only inside this rare branch; without them the 512-column
+            // form (C = 1) copies them between register files on every tile
+            // and spills to scratch.
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[0][dt] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) {
+              asm volatile("" : "+v"(oacc[0][dt]));
+              oacc[0][dt] *= alpha;
+              asm volatile("" : "+v"(oacc[0][dt]));
+            }
           }
           if (bok[j]) pv(j, pb);  // a bad block's tile holds no usable rows
         }

@@ -35,6 +35,44 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfKeys = 32;  // keys per LDS tile (two 16-key MFMA tiles)
 constexpr int kPfMaxIds = 4096;  // block ids of one sequence staged in LDS
 
+// Work placement.  A launch places workgroup i on XCD i mod 8, and each XCD
+// has its own L2, so the row blocks of one (sequence, KV head) pair, which
+// all read the same K/V rows, are kept on one XCD: pair x + 8j belongs to
+// XCD x, which runs its row blocks one pair after another.  The pairs left
+// over when their count is not a multiple of 8 have their row blocks dealt
+// round-robin over the XCDs.  Within a pair the last row blocks, which see
+// the most keys, start first.
+struct PfItem {
+  int b, g, rt;
+  bool live;
+};
+__device__ __forceinline__ PfItem pf_item(long wg, int pairs, int n_rt, int Hkv) {
+  const int x = (int)(wg % kXcds);
+  const long t = wg / kXcds;
+  const int whole = pairs / kXcds, rem = pairs % kXcds;
+  const long first = (long)whole * n_rt;
+  PfItem it;
+  int pair, rb;
+  if (t < first) {
+    pair = x + kXcds * (int)(t / n_rt);
+    rb = (int)(t % n_rt);
+    it.live = true;
+  } else {
+    const long k = (t - first) * kXcds + x;
+    pair = whole * kXcds + (int)(k / n_rt);
+    rb = (int)(k % n_rt);
+    it.live = k < (long)rem * n_rt;
+  }
+  it.rt = n_rt - 1 - rb;
+  it.b = pair / Hkv;
+  it.g = pair % Hkv;
+  return it;
+}
+inline long pf_grid(int pairs, int n_rt) {
+  const int whole = pairs / kXcds, rem = pairs % kXcds;
+  return (long)kXcds * ((long)whole * n_rt + ((long)rem * n_rt + kXcds - 1) / kXcds);
+}
+
 }  // namespace
 
 template <int D, int NT, bool BF16_OUT>
@@ -50,17 +88,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int q0 = p.cu_q[b], n_b = p.cu_q[b + 1] - q0;
   const int rows_wg = kPfWaves * 16 * NT;
+  const int n_rt = (int)(((long)p.max_q * p.G + rows_wg - 1) / rows_wg);
+  const PfItem it = pf_item(blockIdx.x, p.B * p.Hkv, n_rt, p.Hkv);
+  if (!it.live) return;
+  const int b = it.b, g = it.g;
+  const int q0 = p.cu_q[b], n_b = p.cu_q[b + 1] - q0;
   const int R = n_b * p.G;                      // rows of this (sequence, KV head)
-  const int row0 = blockIdx.x * rows_wg;
-  if (blockIdx.x == 0 && g == 0 && tid == 0 && (long)R > (long)gridDim.x * rows_wg)
+  const int row0 = it.rt * rows_wg;
+  if (it.rt == 0 && g == 0 && tid == 0 && (long)R > (long)n_rt * rows_wg)
     report(p.status, KVC_ERR_DATA);  // a chunk longer than max_q: its last rows are not computed
   if (row0 >= R) return;  // whole workgroup
   const int L = p.seq_lens[b];
   if (n_b < 0 || L < n_b || L > p.cap || q0 < 0 || q0 + n_b > p.total_q) {
-    if (blockIdx.x == 0 && g == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+    if (it.rt == 0 && g == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
     return;
   }
   const int cached = L - n_b;
@@ -272,9 +313,11 @@ hipError_t launch_prefill(const PrefillParams& p, int out_dtype, hipStream_t s) 
   constexpr int NT = 2;
   const long rows_wg = kPfWaves * 16 * NT;
   const long n_rt = ((long)p.max_q * p.G + rows_wg - 1) / rows_wg;
-  if (n_rt == 0 || p.B == 0) return hipSuccess;
-  if (n_rt > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)n_rt, p.Hkv, p.B), block(kPfThreads);
+  if (n_rt == 0 || p.B == 0 || p.Hkv == 0) return hipSuccess;
+  if (n_rt > 0x7fffffffL || (long)p.B * p.Hkv > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const long n_wg = pf_grid(p.B * p.Hkv, (int)n_rt);
+  if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n_wg), block(kPfThreads);
   const bool bf = out_dtype == KVC_BF16;
   if (p.D == 128) {
     if (bf) hipLaunchKernelGGL((prefill_mfma<128, NT, true>), grid, block, 0, s, p);
