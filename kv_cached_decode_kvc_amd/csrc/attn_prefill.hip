@@ -16,11 +16,12 @@
 // the grouped heads share every K/V tile ("Efficient Inference", GQA passage).
 // The threads load each 32-key tile of K and V (one contiguous run per
 // tensor) cooperatively into LDS through a two-stage register ring; each
-// wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 as in the
-// decode kernel (S^T = K.Q^T with Q^T in registers; O^T += V^T.P^T with V^T via
-// ds_read_b64_tr_b16 and the weights as bf16 hi + lo pairs) and skips the
-// tiles that lie entirely above its rows' diagonal.  Outputs are normalised
-// and written directly: there is no split over keys.
+// wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 (S^T =
+// K.Q^T with Q^T in registers, two 16-key halves; one online-softmax step
+// per 32 keys; O^T += V^T.P^T with V^T via ds_read_b64_tr_b16 and the weights
+// as bf16 hi and lo parts) and skips the tiles that lie entirely above its
+// rows' diagonal.  Outputs are normalised and written directly: there is no
+// split over keys.
 #include "launch.hpp"
 
 namespace kvc {
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   vis_min = __builtin_amdgcn_readfirstlane(vis_min);
   // keys the workgroup needs: up to its last row's position
   const int last_row = min(row0 + rows_wg, R) - 1;
-  const int end = cached + last_row / p.G + 1;  // <= L
+  const int end = __builtin_amdgcn_readfirstlane(cached + last_row / p.G + 1);  // <= L
 
   bf16x8_t qf[NT][KK];
   const uint16_t* qbase = (const uint16_t*)p.q;
@@ -162,9 +163,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   // element offset of key `t` (a multiple of 16) of (b, g); -1: bad block
   auto key_base = [&](int t) -> long {
     if (p.table == nullptr) return (((long)b * p.Hkv + g) * p.S_max + t) * D;
-    const int blk = s_ids[t >> bs_shift];
+    const int blk = __builtin_amdgcn_readfirstlane(s_ids[t >> bs_shift]);  // uniform
     if (blk < 0 || blk >= p.N) return -1;
     return (((long)blk * p.Hkv + g) * p.bs + (t & (p.bs - 1))) * D;
+  };
+  // wave-uniform 64-bit value in scalar registers
+  auto uniform = [](long x) -> long {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(x & 0xffffffff));
+    const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+    return (long)(((unsigned long)(unsigned)hi << 32) | lo);
   };
   const int n_tiles = (end + kPfKeys - 1) / kPfKeys;
   struct Stage {
@@ -175,60 +182,87 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   // Every stage issues the same loads on every path (clamped addresses), so
   // the compiler waits for one stage at a time.  A 32-key tile is two 16-key
   // halves, each inside one block (block sizes are multiples of 16).
+  // this thread's chunks of a tile: row, element offset within the row, LDS
+  // offset; with head 128 chunk u of every thread lies in 16-key half u
+  __builtin_assume(tid < kPfThreads);
+  int frow[PER], fchk[PER], lofs[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = min(u * kPfThreads + tid, TCH - 1);  // extra threads repeat the last chunk
+    frow[u] = idx / CPR;
+    fchk[u] = (idx % CPR) * 8;
+    lofs[u] = frow[u] * ROWB + fchk[u] * 2;
+  }
   auto fetch = [&](Stage& s, int n) {
     const int t = n * kPfKeys;
     const bool in = t < end;
-    const long b0 = key_base(in ? t : 0);
-    const long b1 = key_base(in && t + 16 < end ? t + 16 : (in ? t : 0));
+    const long b0 = uniform(key_base(in ? t : 0));
+    const long b1 = uniform(key_base(in && t + 16 < end ? t + 16 : (in ? t : 0)));
     s.ok = in && b0 >= 0 && b1 >= 0;
-    const int last = in ? min(kPfKeys, end - t) - 1 : 0;
+    // not loaded: every row clamps to the cache's first row
+    const int last = __builtin_amdgcn_readfirstlane(s.ok ? min(kPfKeys, end - t) - 1 : 0);
+    const long c0 = s.ok ? b0 : 0, c1 = s.ok ? b1 - 16 * D : 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int idx = s.ok ? min(u * kPfThreads + tid, TCH - 1) : 0;
-      const int row = min(idx / CPR, last);
-      const long base = s.ok ? (row < 16 ? b0 : b1 - 16 * D) : 0;
-      const long off = base + (long)row * D + (idx % CPR) * 8;
-      s.k[u] = load_stream((const uint16_t*)p.k + off);
-      s.v[u] = load_stream((const uint16_t*)p.v + off);
+      const int row = min(frow[u], last);
+      const long c = frow[u] >= 16 && last >= 16 ? c1 : c0;
+      const uint32_t lane_off = (uint32_t)(row * D + fchk[u]) * 2;  // bytes
+      s.k[u] = load_stream((const uint8_t*)p.k + c * 2 + lane_off);
+      s.v[u] = load_stream((const uint8_t*)p.v + c * 2 + lane_off);
     }
   };
   auto store = [&](const Stage& s) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int idx = u * kPfThreads + tid;
-      if (idx < TCH) {
-        const int o = (idx / CPR) * ROWB + (idx % CPR) * 16;
-        *reinterpret_cast<uint4*>(k_lds + o) = s.k[u];
-        *reinterpret_cast<uint4*>(v_lds + o) = s.v[u];
+      if (TCH % kPfThreads == 0 || u * kPfThreads + tid < TCH) {
+        *reinterpret_cast<uint4*>(k_lds + lofs[u]) = s.k[u];
+        *reinterpret_cast<uint4*>(v_lds + lofs[u]) = s.v[u];
       }
     }
   };
   constexpr float kLazy = 8.f;
-  auto compute16 = [&](int t16, int half) {  // keys t16 .. t16 + 15 from LDS rows half*16..
-    const uint8_t* ka_ptr = k_lds + (half * 16 + col) * ROWB + grp * 16;
-    const uint8_t* va_ptr = v_lds + (half * 16 + grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
-    bf16x8_t ka[KK];
+  // One 32-key tile: scores of both 16-key halves, one softmax step over the
+  // 32 keys, then the value products.  A lane holds keys grp*4 .. +3 of each
+  // half, so its value operand is the transposed read of those rows of half
+  // 0 followed by the same rows of half 1 -- eight distinct keys -- and the
+  // weights enter as two products, bf16 hi parts then lo parts.
+  auto compute32 = [&](int t) {
+    const uint8_t* ka_ptr = k_lds + col * ROWB + grp * 16;
+    const uint8_t* va_ptr = v_lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+    bf16x8_t ka[2][KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka_ptr + kk * 64));
-    bf16x8_t pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], s, 0, 0, 0);
-      const int key0 = t16 + grp * 4;
-      float sv[4];
+        ka[h][kk] = __builtin_bit_cast(bf16x8_t,
+                                       *reinterpret_cast<const uint4*>(ka_ptr + h * 16 * ROWB + kk * 64));
+    bf16x8_t ph[NT], pl[NT];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sv[v] = s[v] * p.scale_log2;
-      if (t16 + 16 > vis_min) {  // the tile reaches past some row's last key
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? sv[v] : -INFINITY;
+      for (int kk = 0; kk < KK; ++kk) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qf[nt][kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qf[nt][kk], s1, 0, 0, 0);
       }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (t + kPfKeys > vis_min) {  // the tile reaches past some row's last key
+        const int key0 = t + grp * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          s0[v] = key0 + v < lvis[nt] ? s0[v] : -INFINITY;
+          s1[v] = key0 + 16 + v < lvis[nt] ? s1[v] : -INFINITY;
+        }
+      }
+      float sv[8];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = s0[v] * p.scale_log2;
+        sv[4 + v] = s1[v] * p.scale_log2;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) mx = vmax(mx, sv[v]);
+      mx = rows_max(mx);
       const bool move = mx > m[nt] + kLazy;
       if (__any(move)) {
         const float m_new = move ? mx : m[nt];
@@ -239,26 +273,40 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
         m[nt] = m_new;
       }
       const float m_use = m[nt] == -INFINITY ? 0.f : m[nt];
-      const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
-      const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
-      l[nt] += (p01[0] + p01[1]) + (p23[0] + p23[1]);
-      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
-      const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
-      const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
-      const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
-      pb[nt] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
-                                       __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+      f32x2_t pp[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        pp[v] = f32x2_t{fast_exp2(sv[2 * v] - m_use), fast_exp2(sv[2 * v + 1] - m_use)};
+      l[nt] += ((pp[0][0] + pp[0][1]) + (pp[1][0] + pp[1][1])) +
+               ((pp[2][0] + pp[2][1]) + (pp[3][0] + pp[3][1]));
+      bf16x2_t hi[4], lo[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        hi[v] = __builtin_convertvector(pp[v], bf16x2_t);
+        lo[v] = __builtin_convertvector(pp[v] - __builtin_convertvector(hi[v], f32x2_t), bf16x2_t);
+      }
+      ph[nt] = __builtin_shufflevector(__builtin_shufflevector(hi[0], hi[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(hi[2], hi[3], 0, 1, 2, 3),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
+      pl[nt] = __builtin_shufflevector(__builtin_shufflevector(lo[0], lo[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(lo[2], lo[3], 0, 1, 2, 3),
                                        0, 1, 2, 3, 4, 5, 6, 7);
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+      lds_i16x4_t* a0 = reinterpret_cast<lds_i16x4_t*>(
           (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
-      const bf16x4_t va = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
-      const bf16x8_t va2 = __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3);
+      lds_i16x4_t* a1 = reinterpret_cast<lds_i16x4_t*>(
+          (__attribute__((address_space(3))) uint8_t*)(va_ptr + 16 * ROWB + dt * 32));
+      const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0));
+      const bf16x4_t v1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1));
+      const bf16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[nt], oacc[nt][dt], 0, 0, 0);
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[nt], oacc[nt][dt], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[nt], oacc[nt][dt], 0, 0, 0);
     }
   };
 
@@ -277,8 +325,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
         if (!ok) {
           if (tid == 0) report(p.status, KVC_ERR_DATA);
         } else {
-          if (t < wave_vis) compute16(t, 0);       // tiles above the diagonal are skipped
-          if (t + 16 < wave_vis) compute16(t + 16, 1);
+          if (t < wave_vis) compute32(t);  // tiles above the diagonal are skipped
         }
       }
       __syncthreads();

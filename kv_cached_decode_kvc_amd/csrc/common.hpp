@@ -164,6 +164,22 @@ __device__ __forceinline__ float cross_sum(float x) {
   return x;
 }
 
+// Maximum over the four 16-lane rows of a wavefront (lanes i, i ^ 16, i ^ 32
+// and i ^ 48), received by every lane.  gfx950's permlane swaps exchange
+// rows between two registers on the vector ALU, with no LDS round trip: each
+// returns, per lane, itself and its partner across the swap, in some order.
+// The IEEE maximum (v_maximum3_f32) needs no canonicalised inputs and
+// propagates NaN.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float rows_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = vmax(x, vmax(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  const unsigned w = __float_as_uint(x);
+  const auto c = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return vmax(x, vmax(__uint_as_float(c[0]), __uint_as_float(c[1])));
+}
+
 // Orders LDS traffic of one wavefront: LDS instructions of a wave execute in
 // issue order, so a compiler-level barrier at wavefront scope is enough for a
 // wave-private LDS region.
