@@ -15,7 +15,8 @@
 // 4 * 16 * NT rows); a row is (query position, query head of the group), so
 // the grouped heads share every K/V tile ("Efficient Inference", GQA passage).
 // The threads load each 32-key tile of K and V (one contiguous run per
-// tensor) cooperatively into LDS through a two-stage register ring; each
+// tensor) cooperatively into two LDS buffers through a two-stage register
+// ring (one barrier per tile); each
 // wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 (S^T =
 // K.Q^T with Q^T in registers, two 16-key halves; one online-softmax step
 // per 32 keys; O^T += V^T.P^T with V^T via ds_read_b64_tr_b16 and the weights
@@ -82,10 +83,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   constexpr int CPR = D * 2 / 16;              // 16-byte chunks per row
   constexpr int TCH = kPfKeys * CPR;           // chunks per tile and tensor
   constexpr int PER = (TCH + kPfThreads - 1) / kPfThreads;
-  constexpr int ROWB = D * 2 + 16;
+  constexpr int ROWB = D * 2 + 16;   // K rows: 4 banks apart
+  constexpr int VROWB = D * 2 + 32;  // V rows: 8 banks apart, for the transposed reads
   constexpr int PF = 2;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPfKeys * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kPfKeys * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kPfKeys * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][kPfKeys * VROWB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -185,13 +187,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   // this thread's chunks of a tile: row, element offset within the row, LDS
   // offset; with head 128 chunk u of every thread lies in 16-key half u
   __builtin_assume(tid < kPfThreads);
-  int frow[PER], fchk[PER], lofs[PER];
+  int frow[PER], fchk[PER], lofs[PER], vofs[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = min(u * kPfThreads + tid, TCH - 1);  // extra threads repeat the last chunk
     frow[u] = idx / CPR;
     fchk[u] = (idx % CPR) * 8;
     lofs[u] = frow[u] * ROWB + fchk[u] * 2;
+    vofs[u] = frow[u] * VROWB + fchk[u] * 2;
   }
   auto fetch = [&](Stage& s, int n) {
     const int t = n * kPfKeys;
@@ -211,12 +214,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       s.v[u] = load_stream((const uint8_t*)p.v + c * 2 + lane_off);
     }
   };
-  auto store = [&](const Stage& s) {
+  auto store = [&](const Stage& s, int buf) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       if (TCH % kPfThreads == 0 || u * kPfThreads + tid < TCH) {
-        *reinterpret_cast<uint4*>(k_lds + lofs[u]) = s.k[u];
-        *reinterpret_cast<uint4*>(v_lds + lofs[u]) = s.v[u];
+        *reinterpret_cast<uint4*>(k_lds[buf] + lofs[u]) = s.k[u];
+        *reinterpret_cast<uint4*>(v_lds[buf] + vofs[u]) = s.v[u];
       }
     }
   };
@@ -226,9 +229,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   // half, so its value operand is the transposed read of those rows of half
   // 0 followed by the same rows of half 1 -- eight distinct keys -- and the
   // weights enter as two products, bf16 hi parts then lo parts.
-  auto compute32 = [&](int t) {
-    const uint8_t* ka_ptr = k_lds + col * ROWB + grp * 16;
-    const uint8_t* va_ptr = v_lds + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8;
+  auto compute32 = [&](int t, int buf) {
+    const uint8_t* ka_ptr = k_lds[buf] + col * ROWB + grp * 16;
+    const uint8_t* va_ptr = v_lds[buf] + (grp * 4 + (col >> 2)) * VROWB + (col & 3) * 8;
     bf16x8_t ka[2][KK];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       lds_i16x4_t* a0 = reinterpret_cast<lds_i16x4_t*>(
           (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
       lds_i16x4_t* a1 = reinterpret_cast<lds_i16x4_t*>(
-          (__attribute__((address_space(3))) uint8_t*)(va_ptr + 16 * ROWB + dt * 32));
+          (__attribute__((address_space(3))) uint8_t*)(va_ptr + 16 * VROWB + dt * 32));
       const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0));
       const bf16x4_t v1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1));
       const bf16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -310,26 +313,34 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
     }
   };
 
-#pragma unroll
-  for (int j = 0; j < PF; ++j) fetch(st[j], j);
-  store(st[0]);
+  // Tile k lives in register stage k % 2 and then LDS buffer k % 2.  Step n
+  // stores tile n + 1 into its buffer (last read in step n - 1, which ended
+  // with a barrier), issues the loads of tile n + 3 into the freed stage and
+  // computes tile n: one barrier per tile, and each tile's loads have two
+  // steps to arrive.
+  fetch(st[0], 0);
+  fetch(st[1], 1);
+  store(st[0], 0);
+  bool bok[2] = {st[0].ok, false};
+  fetch(st[0], 2);
   __syncthreads();
-  for (int n0 = 0; n0 < n_tiles; n0 += PF) {
+  for (int n0 = 0; n0 < n_tiles; n0 += 2) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
+    for (int j = 0; j < 2; ++j) {
+      // straight-line steps (a tile past the end is loaded clamped and not
+      // computed), so the compiler waits for one stage's loads at a time
       const int n = n0 + j;
-      const bool ok = st[j].ok;
-      fetch(st[j], n + PF);
+      store(st[1 - j], 1 - j);  // tile n + 1
+      bok[1 - j] = st[1 - j].ok;
+      fetch(st[1 - j], n + 3);
       const int t = n * kPfKeys;
       if (n < n_tiles) {
-        if (!ok) {
+        if (!bok[j]) {
           if (tid == 0) report(p.status, KVC_ERR_DATA);
-        } else {
-          if (t < wave_vis) compute32(t);  // tiles above the diagonal are skipped
+        } else if (t < wave_vis) {
+          compute32(t, j);  // tiles above the diagonal are skipped
         }
       }
-      __syncthreads();
-      store(st[(j + 1) % PF]);
       __syncthreads();
     }
   }
