@@ -219,7 +219,12 @@ int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_len
 size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
 
 /* Partition length in tokens the attention calls use for this desc and n_q
- * (negative kvc_status on a bad desc). */
+ * (negative kvc_status on a bad desc).  With the library default and an FP8
+ * cache on the grouped-query / verify path, near one round of resident
+ * wavefronts, this is an upper bound: each launch then picks a length between
+ * half of it and it from the actual sequence lengths (the workspace is sized
+ * for the shorter bound).  An explicit desc.partition_tokens is always used
+ * as given. */
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
 
 /* Static text for a kvc_status value. */

@@ -73,7 +73,9 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
     if (part == 0 && g == 0 && rb == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
     return;
   }
-  const int nparts = (L + p.P - 1) / p.P;
+  if (part >= (L + p.P_lo - 1) / p.P_lo) return;  // beyond any length's partitions
+  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+  const int nparts = (L + P - 1) / P;
   if (part >= nparts) return;
   const int start = part * kTile;     // first tile of this partition
   const int stride = nparts * kTile;  // distance to its next tile

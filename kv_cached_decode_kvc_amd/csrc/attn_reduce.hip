@@ -40,12 +40,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   float2 mine_raw = make_float2(-INFINITY, 0.f);
   if (lane < p.max_parts) mine_raw = ml[lane];
   const int L = p.seq_lens[b];
+  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
   float acc[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
   float den = 0.f;
   if (L >= p.n_q && L <= p.cap) {
-    const int nparts = (L + p.P - 1) / p.P;
+    const int nparts = (L + P - 1) / P;
 #pragma unroll
     for (int j = 0; j < kEarly; ++j)
 #pragma unroll

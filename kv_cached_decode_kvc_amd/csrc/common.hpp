@@ -30,6 +30,8 @@ struct AttnParams {
   int B, n_q, Hq, Hkv, G, D;
   int bs, S_max, max_blocks, N;
   int P, max_parts;
+  int slots_u;           // > 0: partition length chosen per launch (part_tokens)
+  int P_lo;              //   between P_lo and P
   int cap;               // tokens a sequence may hold
   float scale_log2;      // scale * log2(e): scores go straight into exp2
 };
@@ -54,7 +56,30 @@ struct ReduceParams {
   void* out;
   int32_t* status;
   int B, n_q, Hq, D, P, max_parts, cap;
+  int slots_u, P_lo;  // as in AttnParams
 };
+
+// Partition length of a launch, in tokens.  With slots_u = 0 it is the
+// planned P.  Otherwise (the matrix-core decode and verify kernels) it is
+// chosen from the actual lengths so that the partitions of the whole batch
+// just fit one round of resident wavefronts: with T the 16-key tiles of all
+// sequences (lengths clamped to [0, cap]) and slots_u the resident slots per
+// unit of a sequence, 16 * ceil(T / (slots_u - B)) tokens, kept within
+// [P_lo, P].  Since a sequence of t tiles has ceil(t / tau) <= t / tau + 1
+// partitions, the batch then has at most slots_u wavefronts per unit, and
+// none streams more than tau tiles.  Every lane of the wavefront must call
+// it; the result is wave-uniform.
+__device__ __forceinline__ int part_tokens(const int32_t* seq_lens, int B, int cap, int slots_u,
+                                           int P_lo, int P) {
+  if (slots_u <= 0) return P;
+  int t = 0;
+  for (int i = (int)(threadIdx.x & (kWave - 1)); i < B; i += kWave)
+    t += (min(max(seq_lens[i], 0), cap) + kTile - 1) / kTile;
+  for (int m = 1; m < kWave; m <<= 1) t += __shfl_xor(t, m);
+  const int denom = slots_u - B;
+  const int tau = denom > 0 ? (t + denom - 1) / denom : P / kTile;
+  return __builtin_amdgcn_readfirstlane(min(max(tau * kTile, P_lo), P));
+}
 
 // Work items of the split-KV partition kernels: (sequence b, partition part,
 // unit u), one wavefront each, one wavefront per workgroup.  The hardware

@@ -3,6 +3,8 @@
 // synchronisation, no global state.
 #include <math.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace {
@@ -57,7 +59,9 @@ size_t cache_rows(const kvc_cache_desc* d) {
 struct Plan {
   bool mfma;          // grouped rows on the matrix cores
   int rows_per_item;  // mfma: 16 or 32 rows per wavefront
-  int P;              // partition length in tokens
+  int P;              // partition length in tokens (an upper bound when slots_u > 0)
+  int P_lo;           // slots_u > 0: the shortest partition a launch may choose
+  int slots_u;        // > 0: resident wavefront slots per unit of a sequence
   int max_parts;      // partitions of a full-capacity sequence
   int units;          // work units of a sequence per partition (rows, or row blocks per KV head)
   long grid;          // workgroups of the partition launch
@@ -78,6 +82,17 @@ struct Plan {
 // per key.  It is halved (down to 64) while a full-capacity batch would give
 // fewer than 1024 wavefronts, and doubled (up to 8192) while it would give
 // more than 65536.
+// SIMDs of the current device (4 per compute unit), for the launch-time
+// partition length; 1024 on MI355X.
+int resident_simds() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return 4 * cus;
+}
+
 Plan make_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -101,7 +116,24 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < 1024) pl.P >>= 1;
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 65536) pl.P <<= 1;
   }
-  pl.max_parts = (cap + pl.P - 1) / pl.P;
+  pl.P_lo = pl.P;
+  if (pl.mfma && fp8_format(d) && d->partition_tokens == 0 && pl.P >= 2 * kTile) {
+    // FP8 wavefronts move half the bytes per tile, so they need about twice
+    // as many in flight as bf16 ones to keep HBM busy.  Near one round of
+    // resident wavefronts at full capacity, the matrix-core kernels then
+    // choose the length per launch from the actual lengths (part_tokens),
+    // between half the planned length and the planned length, so that the
+    // batch fills the resident slots.  Well beyond one round the dispatcher
+    // balances the rounds and the planned length stays; bf16 verify measured
+    // no better with the launch-time length (its wavefronts already hold
+    // about the bytes in flight that HBM needs).
+    const long slots = (long)resident_simds() * (pl.rows_per_item == 32 ? 2 : 3);
+    if (units * ((cap + pl.P - 1) / pl.P) <= 2 * slots) {
+      pl.P_lo = pl.P / 2;
+      pl.slots_u = (int)std::min(slots / pl.units, 1L << 30);
+    }
+  }
+  pl.max_parts = (cap + pl.P_lo - 1) / pl.P_lo;
   pl.grid = xcd_grid(d->batch, pl.units, pl.max_parts);
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * d->head_dim * sizeof(float);
@@ -146,6 +178,7 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > one_round) pl.P += 256;
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
   }
+  pl.P_lo = pl.P;
   pl.max_parts = (cap + pl.P - 1) / pl.P;
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * kMlaValueDim * sizeof(float);
@@ -195,6 +228,8 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
   p.max_blocks = d->max_blocks_per_seq;
   p.N = d->num_blocks;
   p.P = pl.P;
+  p.P_lo = pl.P_lo;
+  p.slots_u = pl.slots_u;
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
@@ -314,6 +349,8 @@ int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_len
   p.Hq = d->num_q_heads;
   p.D = d->head_dim;
   p.P = pl.P;
+  p.P_lo = pl.P_lo;
+  p.slots_u = pl.slots_u;
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
   return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));

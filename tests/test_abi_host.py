@@ -123,6 +123,30 @@ def test_workspace_and_partition_sizes(lib):
         assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) > 0
 
 
+def _ws_bytes(rows, parts, d):
+    o = rows * parts * d * 4
+    return ((o + 255) // 256) * 256 + rows * parts * 2 * 4
+
+
+def test_fp8_verify_workspace_covers_launch_time_partitions(lib):
+    # FP8 verify near one round: launches may use partitions down to half the
+    # planned length, so the workspace holds twice the partitions; bf16 and an
+    # explicit partition length keep the planned count
+    w = synth.get("C5")
+    cap = synth.capacity_tokens(w)
+    rows = w.B * w.Hq * w.n_q
+    for dtype, explicit, factor in (("fp8_e4m3", 0, 2), ("bf16", 0, 1), ("fp8_e4m3", 512, 1)):
+        dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                  dtype=kvc.DTYPE_CODES[dtype],
+                  block_size=w.block_size, max_seq_len=cap,
+                  max_blocks_per_seq=synth.max_blocks_per_seq(w),
+                  num_blocks=synth.pool_blocks(w), partition_tokens=explicit)
+        P = kvc.kvc_attn_partition_tokens(dd, w.n_q)
+        assert P == 512, (dtype, P)
+        parts = -(-cap // (P // factor))
+        assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _ws_bytes(rows, parts, w.D), dtype
+
+
 def test_status_strings(lib):
     for code, name in kvc.STATUS_NAMES.items():
         s = kvc.kvc_status_string(code)
