@@ -99,6 +99,9 @@ ATTN_CASES = [
     ("verify5-gqa4-e4m3-d128-paged", "e4m3", 128, 8, 2, 16, 5, 5, 900, 5, 0, None),
     ("verify5-gqa4-e5m2-d64-paged-P16", "e5m2", 64, 8, 2, 16, 5, 5, 300, 4, 16, None),
     ("verify3-mha-e4m3-d128-contig-cap301", "e4m3", 128, 2, 2, 0, 3, 3, 300, 3, 0, 301),
+    # enough sequences that the launch-time partition length lands strictly
+    # between its bounds (planned 256 keys, about 208 chosen from these lengths)
+    ("verify5-gqa4-e4m3-d128-paged-B40", "e4m3", 128, 32, 8, 16, 5, 5, 2000, 40, 0, None),
 ]
 
 
