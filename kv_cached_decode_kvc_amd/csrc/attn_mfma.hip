@@ -234,12 +234,20 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
         float sl[4];       // score factor of each of this lane's four keys
 #pragma unroll
         for (int v = 0; v < 4; ++v) sl[v] = F ? ks_cur[v] * p.scale_log2 : p.scale_log2;
+        // two accumulation chains per row block (even and odd steps along D),
+        // interleaved across the row blocks, so no product waits on the one
+        // just issued
+        f32x4_t sc[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            sc[nt][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], sc[nt][kk & 1], 0, 0, 0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[nt][kk], s, 0, 0, 0);
+          const f32x4_t s = sc[nt][0] + sc[nt][1];
           const int key0 = tile + grp * 4;
           float sv[4];
 #pragma unroll

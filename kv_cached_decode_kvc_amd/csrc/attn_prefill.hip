@@ -240,14 +240,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
         ka[h][kk] = __builtin_bit_cast(bf16x8_t,
                                        *reinterpret_cast<const uint4*>(ka_ptr + h * 16 * ROWB + kk * 64));
     bf16x8_t ph[NT], pl[NT];
+    f32x4_t sa[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sa[nt][0] = sa[nt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        sa[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qf[nt][kk], sa[nt][0], 0, 0, 0);
+        sa[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qf[nt][kk], sa[nt][1], 0, 0, 0);
+      }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qf[nt][kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qf[nt][kk], s1, 0, 0, 0);
-      }
+      f32x4_t s0 = sa[nt][0], s1 = sa[nt][1];
       if (t + kPfKeys > vis_min) {  // the tile reaches past some row's last key
         const int key0 = t + grp * 4;
 #pragma unroll
@@ -295,6 +300,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
                                        __builtin_shufflevector(lo[2], lo[3], 0, 1, 2, 3),
                                        0, 1, 2, 3, 4, 5, 6, 7);
     }
+    bf16x8_t vas[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       lds_i16x4_t* a0 = reinterpret_cast<lds_i16x4_t*>(
@@ -304,13 +310,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0));
       const bf16x4_t v1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1));
       const bf16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      vas[dt] = va;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[nt], oacc[nt][dt], 0, 0, 0);
+    }
+    // the lo products a full pass later: no accumulator is used twice in a row
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[nt], oacc[nt][dt], 0, 0, 0);
-    }
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vas[dt], pl[nt], oacc[nt][dt], 0, 0, 0);
   };
 
   // Tile k lives in register stage k % 2 and then LDS buffer k % 2.  Step n
