@@ -36,6 +36,10 @@ CASES = [
     ("verify16-mha-bf16-d64-paged", "bf16", 64, 2, 2, 16, 16, 16, 300, 2, 0),
     ("verify5-f32-d64-paged", "f32", 64, 4, 2, 16, 5, 5, 300, 3, 0),
     ("verify3-gqa4-bf16-d128-P32", "bf16", 128, 8, 2, 16, 3, 3, 200, 4, 32),
+    # up to 94 partitions a row: the combine's eight-at-a-time loads and its
+    # second pass over partitions beyond 64
+    ("mha-bf16-d128-contig-P16-long", "bf16", 128, 4, 4, 0, 1, 1000, 1500, 3, 16),
+    ("verify4-gqa4-bf16-d64-paged-P16-long", "bf16", 64, 8, 2, 16, 4, 1000, 1500, 3, 16),
 ]
 
 

@@ -23,6 +23,8 @@ CASES = [
     ("verify2-h128-paged16-four-row-groups", 128, 2, 16, 2, 400, 0, None),
     ("verify5-h16-paged16-P32", 16, 5, 16, 3, 300, 32, None),
     ("h8-half-wave-P16", 8, 1, 64, 3, 200, 16, None),
+    # up to 75 partitions a row: the 512-wide combine past its first 64
+    ("h16-paged64-P16-long", 16, 1, 64, 3, 3000, 16, None),
 ]
 
 
