@@ -129,3 +129,38 @@ def test_prefill_refusals():
     with pytest.raises(kvc.KvcError):  # fp32 caches: not supported by the prefill kernel
         kvc.kvc_prefill_attn(gc.desc, out, i32([0, 4]), 4, 4, gc.k, gc.v, gc.seq_lens, gc.table,
                              0.125, out, gc.status)
+
+
+def _small_prefill(seed):
+    w = synth.custom(name="e", seed=seed, B=2, Hq=8, Hkv=2, D=128, dtype="bf16", block_size=16,
+                     n_q=1, len_lo=1, len_hi=200, prefill=True)
+    cached = np.array([40, 60])
+    chunk = np.array([70, 50])
+    gc = GpuCache(w, block_size=16, capacity=int((cached + chunk).max()) + 3)
+    gc.prefill(cached)
+    total = int(chunk.sum())
+    kr = synth.normal(w, (total, 2, 128), synth.S_KNEW, 56, seed)
+    vr = synth.normal(w, (total, 2, 128), synth.S_VNEW, 56, seed)
+    q = to_dev(synth.normal(w, (total, 8, 128), synth.S_Q, 56, seed), "bf16")
+    gc.add_tokens(kr, vr, chunk)
+    assert gc.dev_status() == 0
+    out = torch.zeros((total, 8, 128), device="cuda")
+    return gc, q, i32(synth.cu_from_counts(chunk)), total, out
+
+
+def test_prefill_bad_block_id_reports_and_does_not_fault():
+    gc, q, cu, total, out = _small_prefill(61)
+    gc.table[1, 2] = gc.N + 5  # inside sequence 1's visible keys, outside the pool
+    kvc.kvc_prefill_attn(gc.desc, q, cu, total, 70, gc.k, gc.v, gc.seq_lens, gc.table, 0.088, out,
+                         gc.status)
+    assert gc.dev_status() == -8
+    assert bool(torch.isfinite(out).all())
+
+
+def test_prefill_chunk_longer_than_max_q_reports():
+    gc, q, cu, total, out = _small_prefill(62)
+    # max_q below the first sequence's 70 rows: its last rows are not computed
+    kvc.kvc_prefill_attn(gc.desc, q, cu, total, 40, gc.k, gc.v, gc.seq_lens, gc.table, 0.088, out,
+                         gc.status)
+    assert gc.dev_status() == -8
+    assert bool(torch.isfinite(out).all())
