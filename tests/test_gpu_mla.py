@@ -73,6 +73,20 @@ def test_mla_bf16_output_and_refusals(ref):
                          out, ws)
 
 
+@pytest.mark.parametrize("Hq", [16, 128])
+def test_mla_bad_block_id_reports_and_does_not_fault(Hq):
+    w = synth.custom(name="bad", seed=3300 + Hq, B=2, Hq=Hq, Hkv=1, D=576, dtype="bf16",
+                     block_size=64, n_q=1, len_lo=200, len_hi=300, dv=512)
+    lengths = synth.final_lengths(w)
+    gc = GpuCache(w, block_size=64)
+    gc.prefill(lengths - 1)
+    gc.step_rows(0)
+    gc.table[1, 1] = gc.N + 5  # inside sequence 1's keys, outside the pool
+    out = gc.attend(queries_dev(w), 1, scale=SCALE)
+    assert gc.dev_status() == -8
+    assert bool(torch.isfinite(out).all())
+
+
 @pytest.mark.parametrize("name", ["M1", "M2"])
 def test_mla_full_size_sampled(ref, name):
     w = synth.get(name)
