@@ -24,23 +24,36 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const int b = (int)(bh / p.Hq);
   const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + lane * CPL;
 
-  // One round trip: the length, the first kEarly partitions' outputs for this
-  // lane's columns and one partition's (m, l) per lane are all requested
-  // together, for every partition slot the workspace has (slots beyond the
-  // sequence's partitions hold stale bytes and are discarded by selection,
-  // never multiplied, once the length is known).
+  // With few partition slots, one round trip: the length, the first kEarly
+  // partitions' outputs for this lane's columns and one partition's (m, l)
+  // per lane are all requested together, for every slot the workspace has
+  // (slots beyond the sequence's partitions hold stale bytes and are
+  // discarded by selection, never multiplied, once the length is known).
+  // With more slots than that, fetching every slot's outputs would move
+  // several times the bytes the sequence has, so the outputs wait for the
+  // length (a second round trip) and only its partitions are read.
   constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
+  const bool speculate = p.max_parts <= (kEarly > 8 ? 8 : kEarly);
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
   const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
   float early[kEarly][CPL];
+  if (speculate) {
 #pragma unroll
-  for (int j = 0; j < kEarly; ++j)
+    for (int j = 0; j < kEarly; ++j)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) early[j][c] = j < p.max_parts ? po[(long)j * D + c] : 0.f;
+      for (int c = 0; c < CPL; ++c) early[j][c] = j < p.max_parts ? po[(long)j * D + c] : 0.f;
+  }
   float2 mine_raw = make_float2(-INFINITY, 0.f);
   if (lane < p.max_parts) mine_raw = ml[lane];
   const int L = p.seq_lens[b];
   const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+  if (!speculate) {
+    const int n = L >= p.n_q && L <= p.cap ? (L + P - 1) / P : 0;
+#pragma unroll
+    for (int j = 0; j < kEarly; ++j)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) early[j][c] = j < n ? po[(long)j * D + c] : 0.f;
+  }
   float acc[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
