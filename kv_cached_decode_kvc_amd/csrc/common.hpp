@@ -91,6 +91,13 @@ __device__ __forceinline__ int part_tokens(const int32_t* seq_lens, int B, int c
 // innermost would hand the high partitions, which only long sequences have,
 // to a fixed subset of XCDs), and an XCD's items of one sequence are
 // dispatched together, so they stream neighbouring tiles at the same time.
+// Within an XCD the hardware passes workgroups to its four shader engines in
+// strict rotation, whatever their load, so with m in order the engine of an
+// item would follow m mod 4, i.e. its partition: one engine would get
+// partitions 0, 4, 8, ... and another 3, 7, 11, ..., which only long
+// sequences have.  Each full block of 8 consecutive m is therefore walked as
+// a snake (0 1 2 3 7 6 5 4): the two positions that share an engine hold
+// offsets j and 7 - j, and every engine's partitions have the same mean.
 constexpr int kXcds = 8;
 
 struct WorkItem {
@@ -105,7 +112,10 @@ __device__ __forceinline__ WorkItem xcd_item(long wg, int U, int max_parts) {
   const int M = (K + kXcds - 1) / kXcds;
   WorkItem w;
   w.b = (int)(t / M);
-  const int m = (int)(t % M);
+  int m = (int)(t % M);
+  // snake within each full block of 8: positions j and j + 4 hold offsets j
+  // and 7 - j
+  if ((m | 7) < M && (m & 4)) m ^= 3;
   const int xr = (x + kXcds - (w.b % kXcds)) % kXcds;
   const int k = m * kXcds + xr;
   w.live = k < K;
