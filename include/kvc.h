@@ -333,6 +333,12 @@ int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* 
  *                latent rows (apply the absorbed value up-projection after)
  * Verify rows (n_q > 1) see keys 0 .. L - n_q + r.  Other geometries return
  * KVC_ERR_UNSUPPORTED.  The workspace is sized by kvc_mla_workspace_bytes.
+ * kvc_mla_partition_tokens returns the planned partition length; when the
+ * descriptor's partition_tokens is 0 and a full-capacity batch fits one round
+ * of resident workgroups, it is an upper bound: each launch then picks a
+ * length between half of it and it from the lengths in device memory, the
+ * same in the partition and reduce calls, and the workspace covers the
+ * shortest.  An explicit partition_tokens is used as given.
  */
 size_t kvc_mla_workspace_bytes(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);
 int32_t kvc_mla_partition_tokens(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);

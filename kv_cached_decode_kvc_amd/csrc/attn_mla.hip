@@ -50,6 +50,42 @@ constexpr int kMlaThreads = kMlaWaves * kWave;
 
 }  // namespace
 
+// The k-th (sequence, partition) pair in sequence order, where sequence b
+// has ceil(L_b / P) partitions, or one if L_b lies outside [n_q, cap] (that
+// pair reports the error).  Numbering only the pairs that exist packs the
+// live workgroups at the front of the grid: each XCD passes its workgroups
+// to its shader engines in turn whatever their load, so live pairs spread
+// among dead ones could queue behind each other on one engine while CUs of
+// another sat idle.  Computed by every wavefront alike (one pass over the
+// lengths, 64 at a time, with a wavefront prefix sum); returns (-1, 0) when
+// k is past the last pair.
+__device__ __forceinline__ int2 nth_pair(const int32_t* seq_lens, int B, int n_q, int cap, int P,
+                                         int k) {
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  int before = 0;  // pairs of the chunks already passed
+  for (int c = 0; c < B; c += kWave) {
+    const int i = c + lane;
+    int n = 0;
+    if (i < B) {
+      const int L = seq_lens[i];
+      n = (L < n_q || L > cap) ? 1 : (L + P - 1) / P;
+    }
+    int incl = n;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const unsigned long long hit = __ballot(k < before + incl);
+    if (hit != 0) {
+      const int j = __ffsll((long long)hit) - 1;
+      const int excl = before + __shfl(incl - n, j);
+      return make_int2(__builtin_amdgcn_readfirstlane(c + j), __builtin_amdgcn_readfirstlane(k - excl));
+    }
+    before += __shfl(incl, kWave - 1);
+  }
+  return make_int2(-1, 0);
+}
+
 template <int PF, int C>
 __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(AttnParams p) {
   constexpr int NT = 1;
@@ -78,17 +114,18 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
   // = chunk * 8 + j, so its row groups sit 8 ids apart on one XCD
   const long wg = blockIdx.x;
   const int rg = (int)((wg / 8) % n_rg);
-  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);  // b * max_parts + part
+  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);  // the unit-th live pair
   if (unit >= (long)p.B * p.max_parts) return;
-  const int part = (int)(unit % p.max_parts);
-  const int b = (int)(unit / p.max_parts);
-  const int L = p.seq_lens[b];
+  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+  const int2 bp = nth_pair(p.seq_lens, p.B, p.n_q, p.cap, P, (int)unit);
+  if (bp.x < 0) return;  // past the last live pair: whole workgroup
+  const int b = bp.x, part = bp.y;
+  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
   if (L < p.n_q || L > p.cap) {
-    if (part == 0 && rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+    if (rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
     return;  // whole workgroup
   }
-  const int nparts = (L + p.P - 1) / p.P;
-  if (part >= nparts) return;  // whole workgroup
+  const int nparts = (L + P - 1) / P;
   const int start = part * kTile, stride = nparts * kTile, end = L;
 
   // this wavefront's rows: i = r * Hq + h

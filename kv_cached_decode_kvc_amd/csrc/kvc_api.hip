@@ -170,16 +170,25 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   const long n_rg = (R + rows_wg - 1) / rows_wg;
   const long units = (long)d->batch * n_rg;
   const int cap = capacity(d);
+  const long one_round = C == 1 ? 256 : 512;  // workgroups resident at once
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
-    const long one_round = C == 1 ? 256 : 512;  // workgroups resident at once
     pl.P = 256;
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > one_round) pl.P += 256;
     while (pl.P > 64 && units * ((cap + pl.P - 1) / pl.P) < one_round) pl.P >>= 1;
   }
   pl.P_lo = pl.P;
-  pl.max_parts = (cap + pl.P - 1) / pl.P;
+  if (d->partition_tokens == 0 && pl.P >= 2 * kTile &&
+      units * ((cap + pl.P - 1) / pl.P) <= one_round) {
+    // The planned length fits a full-capacity batch in one round; with the
+    // actual lengths the kernel shortens it (down to half) so that the live
+    // (sequence, partition) pairs fill the round, and packs them at the
+    // front of the grid (nth_pair in the kernel).
+    pl.P_lo = pl.P / 2;
+    pl.slots_u = (int)(one_round / n_rg);
+  }
+  pl.max_parts = (cap + pl.P_lo - 1) / pl.P_lo;
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * kMlaValueDim * sizeof(float);
   pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
@@ -540,6 +549,8 @@ int kvc_mla_attn_reduce(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim,
   p.Hq = d->num_q_heads;
   p.D = kMlaValueDim;
   p.P = pl.P;
+  p.P_lo = pl.P_lo;
+  p.slots_u = pl.slots_u;
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
   return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));

@@ -147,6 +147,25 @@ def test_fp8_verify_workspace_covers_launch_time_partitions(lib):
         assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _ws_bytes(rows, parts, w.D), dtype
 
 
+def test_mla_workspace_covers_launch_time_partitions(lib):
+    # MLA whose full-capacity batch fits one round of resident workgroups:
+    # launches may use partitions down to half the planned length, so the
+    # workspace holds twice the partitions; an explicit length keeps the count
+    for alias, planned in (("M1", 1024), ("M2", 2048)):
+        w = synth.get(alias)
+        cap = synth.capacity_tokens(w)
+        rows = w.B * w.Hq * w.n_q
+        for explicit, factor in ((0, 2), (planned, 1)):
+            dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                      dtype=kvc.DTYPE_CODES[w.dtype], block_size=w.block_size, max_seq_len=cap,
+                      max_blocks_per_seq=synth.max_blocks_per_seq(w),
+                      num_blocks=synth.pool_blocks(w), partition_tokens=explicit)
+            P = kvc.kvc_mla_partition_tokens(dd, w.n_q, w.dv)
+            assert P == planned, (alias, P)
+            parts = -(-cap // (P // factor))
+            assert kvc.kvc_mla_workspace_bytes(dd, w.n_q, w.dv) == _ws_bytes(rows, parts, w.dv), alias
+
+
 def test_status_strings(lib):
     for code, name in kvc.STATUS_NAMES.items():
         s = kvc.kvc_status_string(code)

@@ -25,6 +25,10 @@ CASES = [
     ("h8-half-wave-P16", 8, 1, 64, 3, 200, 16, None),
     # up to 75 partitions a row: the 512-wide combine past its first 64
     ("h16-paged64-P16-long", 16, 1, 64, 3, 3000, 16, None),
+    # launch-time lengths with the live pairs packed: 24 sequences, and 70 (two
+    # chunks of 64 lengths in the numbering)
+    ("h16-paged16-b24-packed", 16, 1, 16, 24, 900, 0, None),
+    ("h128-paged64-b70-packed", 128, 1, 64, 70, 260, 0, None),
 ]
 
 
@@ -85,6 +89,25 @@ def test_mla_bad_block_id_reports_and_does_not_fault(Hq):
     out = gc.attend(queries_dev(w), 1, scale=SCALE)
     assert gc.dev_status() == -8
     assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("bad_len", [0, 10_000])
+def test_mla_bad_length_reports_and_others_unchanged(ref, bad_len):
+    # a length outside [n_q, capacity] takes one pair of the packed numbering,
+    # which reports; the other sequences' pairs still follow it
+    w = synth.custom(name="badlen", seed=3400, B=3, Hq=16, Hkv=1, D=576, dtype="bf16",
+                     block_size=64, n_q=1, len_lo=200, len_hi=900, dv=512)
+    lengths = synth.final_lengths(w)
+    gc = GpuCache(w, block_size=64)
+    gc.prefill(lengths - 1)
+    gc.step_rows(0)
+    gc.seq_lens[1] = bad_len
+    out = gc.attend(queries_dev(w), 1, scale=SCALE)
+    assert gc.dev_status() == -8  # data error
+    want = oracle_outputs(ref, w, [0, 2], lengths - 1, scale=SCALE)
+    got = out.cpu().numpy()
+    for b in [0, 2]:
+        assert_close(got[b], want[b], "b=%d" % b)
 
 
 @pytest.mark.parametrize("name", ["M1", "M2"])
