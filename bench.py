@@ -8,10 +8,16 @@ kvc_attn_reduce.  The prepared step reads its lengths and free-list head from
 buffers it never writes, so replaying it K times does identical work each
 time; the cache and all inputs are resident in HBM before the timed region.
 
-Printed: one JSON line.  value = KV bytes attended per step / time per step
-(GB/s); roofline.achieved = the same bytes / the partition kernel's average
-duration, measured with HIP events around K back-to-back launches of it on
-the stream the kernels run on.
+Printed: one JSON line.  value = KV bytes attended per step / the median time
+of a step timed alone behind a 1 GiB write (no KV row comes from the
+last-level caches), over --flush-iters steps; roofline.achieved = the same
+bytes / the median of those steps' partition launches, HIP events on the
+stream the kernels run on.  The K steps of the timed region (back to back,
+between two synchronisations) are reported as 'steady'.  The same protocol
+is applied to the other target workloads ('configs'), the paged and
+contiguous forms of the 16 x 2048 layer are compared, a streaming-read probe
+gives the device's read ceiling, and the oracle is timed on the host (one
+thread, and every core).
 """
 from __future__ import annotations
 
@@ -22,6 +28,7 @@ import math
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -71,52 +78,112 @@ def stored_traffic(workload: str, kernel: str, src_hash: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rows(w, b):
+    """Sequence b's attended rows as the oracle takes them, from the generator:
+    (k, v) [Hkv, L, D] (MLA: the latent rows [L, Dk], None); an FP8 workload
+    gets the oracle's own quantization of the rows, dequantized exactly."""
+    import numpy as np
+
+    import oracle
+    from kv_cached_decode_kvc_amd import synth
+
+    ref = oracle.get()
+    cached = synth.cached_lengths(w)
+    kv = []
+    for x in (("k",) if w.dv else ("k", "v")):
+        rows = np.concatenate([synth.cache_rows(w, x, b, int(cached[b])),
+                               synth.new_rows(w, x, b)]).transpose(1, 0, 2).copy()
+        if w.kv:
+            rows = ref.dequantize_rows(*ref.quantize_rows(rows, w.kv), w.kv)
+        kv.append(rows)
+    if w.dv:
+        return kv[0][0], None
+    return kv[0], kv[1]
+
+
 def cpu_baseline(w, seconds: float, gpu_out=None):
-    """The oracle (single thread, float64) on a bounded sample of the same
-    workload: whole sequences, cycled until `seconds` of oracle time."""
+    """The oracle (float64) timed on this host, on a bounded sample of the same
+    workload: the batch's whole sequences, cycled until `seconds` of oracle
+    time per leg.  Two legs on the same rows: the single-threaded definition,
+    and the many-sequence function (OpenMP over (sequence, query head) on every
+    host core, the same arithmetic).  Row generation is not timed."""
     import numpy as np
 
     import oracle
     from kv_cached_decode_kvc_amd import metrics, synth
 
     ref = oracle.get()
-    cached = synth.cached_lengths(w)
     lens = synth.final_lengths(w)
     scale = 1.0 / math.sqrt(w.D)
+    dt = "f64" if w.kv else w.dtype
+    with ThreadPoolExecutor(max_workers=16) as ex:  # row generation, not timed
+        rows = list(ex.map(lambda b: oracle_rows(w, b), range(w.B)))
+    qs = [synth.queries(w, b) for b in range(w.B)]
+    if w.kv:
+        qs = [oracle.widen(q, "bf16") for q in qs]
+    seq_bytes = [metrics.attended_cache_bytes([lens[b]], w.Hkv, w.kv_row_bytes, w.kv_tensors)
+                 for b in range(w.B)]
+
+    # single thread: one sequence per call, batch order, cycled
     spent, nbytes, nseq, worst = 0.0, 0, 0, 0.0
-    rows = {}  # generated once per sequence; only the oracle call is timed
     b = 0
     while spent < seconds:
-        if b not in rows:
-            rows[b] = tuple(
-                np.concatenate([synth.cache_rows(w, x, b, int(cached[b])),
-                                synth.new_rows(w, x, b)]).transpose(1, 0, 2).copy()
-                for x in (("k",) if w.dv else ("k", "v")))
-        k, v = rows[b] if not w.dv else (rows[b][0], None)
-        q = synth.queries(w, b)
+        k, v = rows[b]
         t0 = time.perf_counter()
-        if w.dv:  # MLA: the latent rows are keys and, in their first dv dims, values
-            want = ref.mla_attention(q, k[0], scale, w.dv)
-        elif w.kv:  # the oracle's own quantization of the rows, dequantized exactly
-            kd = ref.dequantize_rows(*ref.quantize_rows(k, w.kv), w.kv)
-            vd = ref.dequantize_rows(*ref.quantize_rows(v, w.kv), w.kv)
-            want = ref.attention(oracle.widen(q, "bf16"), kd, vd, scale, "f64")
+        if w.dv:
+            want = ref.mla_attention(qs[b], k, scale, w.dv)
         else:
-            want = ref.attention(q, k, v, scale, w.dtype)
+            want = ref.attention(qs[b], k, v, scale, dt)
         spent += time.perf_counter() - t0
-        nbytes += metrics.attended_cache_bytes([lens[b]], w.Hkv, w.kv_row_bytes, w.kv_tensors)
+        nbytes += seq_bytes[b]
         nseq += 1
         if gpu_out is not None and nseq <= w.B:
             worst = max(worst, float(np.abs(gpu_out[b] - want).max()))
         b = (b + 1) % w.B
+    single = {
+        "value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+        "seq_steps_per_s": round(nseq / spent, 3),
+        "sample": "%d whole sequences (batch order, cycled), %.1f s of oracle time" % (
+            nseq, spent),
+        "sample_max_abs_err_vs_gpu": worst if gpu_out is not None else None,
+    }
+
+    # every host core: the whole batch per call, cycled
+    spent, nbytes, nseq, threads = 0.0, 0, 0, 0
+    ks = [r[0] for r in rows]
+    vs = None if w.dv else [r[1] for r in rows]
+    while spent < seconds:
+        t0 = time.perf_counter()
+        _, threads = ref.attention_many(qs, ks, vs, scale, dt, dv=w.dv)
+        spent += time.perf_counter() - t0
+        nbytes += sum(seq_bytes)
+        nseq += w.B
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
     return {
         "value": round(nbytes / spent / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%d whole sequences of the workload (batch order, cycled), float64, one thread; "
-                  "%.1f s of oracle time; %.4g sequence-steps/s" % (nseq, spent, nseq / spent),
-        "sample_max_abs_err_vs_gpu": worst if gpu_out is not None else None,
+        "sample": "the batch's %d whole sequences per call, cycled %d times; float64; OpenMP over "
+                  "(sequence, query head) on %d threads; %.1f s of oracle time; %.4g "
+                  "sequence-steps/s" % (w.B, nseq // max(w.B, 1), threads, spent, nseq / spent),
+        "seq_steps_per_s": round(nseq / spent, 3),
+        "cpu_model": cpu_model(),
+        "nproc": nproc,
+        "single_thread": single,
     }
 
 
@@ -408,18 +475,177 @@ def calibrate_copy(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+def stats(xs) -> dict:
+    return {"p10": pct(xs, 10), "median": pct(xs, 50), "p90": pct(xs, 90)}
+
+
+def flushed_partitions(call, iters: int, flush_bytes: int = 1 << 30):
+    """One launch of `call` (a partition launch) timed at a time behind a
+    >= 1 GiB write, HIP events on torch's current stream.  Returns us list."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    out = []
+    for i in range(iters):
+        buf.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    del buf
+    return out
+
+
+def steady_partition_us(lc, n: int) -> float:
+    """Average of n back-to-back partition launches (HIP events)."""
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(n):
+        lc.step_partition()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n * 1e3
+
+
+def kv_bytes_of(w) -> int:
+    from kv_cached_decode_kvc_amd import metrics, synth
+    return metrics.attended_cache_bytes(synth.final_lengths(w), w.Hkv, w.kv_row_bytes,
+                                        w.kv_tensors)
+
+
+def config_result(name: str, warmup: int, iters: int, steady: int) -> dict:
+    """One of the other target workloads: flushed step and partition times
+    (median, p10, p90 over `iters` iterations behind a 1 GiB write), steady
+    back-to-back partition time, and for multi-step workloads the HIP-graph
+    replay of the whole loop."""
+    import torch
+
+    from kv_cached_decode_kvc_amd import runner, synth
+
+    w = synth.get(name)
+    print("# config %s (%s): building" % (name, w.name), file=sys.stderr, flush=True)
+    lc = runner.build(w)
+    for _ in range(warmup):
+        lc.step()
+    torch.cuda.synchronize()
+    assert lc.dev_status() == 0
+    kvb = kv_bytes_of(w)
+    st_us, pt_us = flushed_steps(lc, iters)
+    sp = steady_partition_us(lc, steady)
+    assert lc.dev_status() == 0
+    step_med, part_med = pct(st_us, 50), pct(pt_us, 50)
+    res = {
+        "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+        "query_rows": w.n_q, "cache": w.cache_dtype, "block_size": w.block_size,
+        "kv_bytes_per_step": kvb, "flushed_iters": iters,
+        "flushed_step_us": stats(st_us), "flushed_partition_us": stats(pt_us),
+        "gbs_step": round(kvb / (step_med * 1e-6) / 1e9, 2),
+        "hbm_frac_step": round(kvb / (step_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "gbs_partition": round(kvb / (part_med * 1e-6) / 1e9, 2),
+        "hbm_frac_partition": round(kvb / (part_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "seq_steps_per_s": round(w.B / (step_med * 1e-6), 1),
+        "query_rows_per_s": round(w.B * w.n_q / (step_med * 1e-6), 1),
+        "steady_partition_us": round(sp, 3),
+        "steady_hbm_frac_partition": round(kvb / (sp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if w.steps > 1:
+        res["graph_replay"] = graph_replay(w, lc)
+    del lc
+    torch.cuda.empty_cache()
+    return res
+
+
+def paged_vs_contiguous(iters: int) -> dict:
+    """The 16 x 2048 Llama-2-13B-shaped layer as a paged cache (block 16, the
+    seeded permuted pool, the same seed and rows) against the contiguous one:
+    flushed partition times at the same partition length (1024 keys) isolate
+    the block-table indirection; the paged cache's own default length is shown
+    too."""
+    import torch
+
+    from kv_cached_decode_kvc_amd import kvc, runner, synth
+
+    wc = synth.get("C2")
+    wp = synth.custom(name="llama2-13b-layer-paged16-b16-ctx2048", seed=wc.seed, B=wc.B,
+                      Hq=wc.Hq, Hkv=wc.Hkv, D=wc.D, dtype=wc.dtype, block_size=16, n_q=1,
+                      len_lo=wc.len_lo, len_hi=wc.len_hi)
+    kvb = kv_bytes_of(wc)
+    res = {"workload": wp.name, "kv_bytes_per_step": kvb, "flushed_iters": iters}
+    print("# paged vs contiguous: building", file=sys.stderr, flush=True)
+    for label, w, P in (("contiguous_p1024", wc, 0), ("paged_p1024", wp, 1024),
+                        ("paged_default", wp, 0)):
+        lc = runner.build(w, partition_tokens=P)
+        lc.step()
+        torch.cuda.synchronize()
+        us = flushed_partitions(lc.step_partition, iters)
+        assert lc.dev_status() == 0
+        res[label] = {"partition_tokens": kvc.kvc_attn_partition_tokens(lc.desc, 1),
+                      "flushed_partition_us": stats(us),
+                      "hbm_frac": round(kvb / (pct(us, 50) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del lc
+        torch.cuda.empty_cache()
+    c, p = res["contiguous_p1024"]["flushed_partition_us"]["median"], \
+        res["paged_p1024"]["flushed_partition_us"]["median"]
+    res["paged_over_contiguous_same_partition"] = round(p / c, 4)
+    res["paged_default_over_contiguous"] = round(
+        res["paged_default"]["flushed_partition_us"]["median"] / c, 4)
+    return res
+
+
+def probe(iters: int = 20, nbytes: int = 2 << 30) -> dict:
+    """Plain streaming-read probe (libkvc_probe.so): a 2 GiB buffer read once
+    per launch (8x the last-level cache), ordinary and non-temporal 16-byte
+    loads, three grid sizes; average of `iters` back-to-back launches."""
+    import torch
+
+    from kv_cached_decode_kvc_amd import probe as pr
+
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"bytes_per_launch": nbytes, "launches": iters}
+    best = 0.0
+    for nt in (False, True):
+        for wg in (1024, 2048, 4096):
+            for _ in range(3):
+                pr.stream_read(buf, nt, wg, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                pr.stream_read(buf, nt, wg, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / iters * 1e3
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res["%s_wg%d_gbs" % ("nontemporal" if nt else "ordinary", wg)] = round(gbs, 1)
+            best = max(best, gbs)
+    res["best_gbs"] = round(best, 1)
+    res["best_frac"] = round(best / HBM_PEAK_GBS, 4)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="steady-state steps timed back to back between two synchronisations")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time of each CPU-baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
-    ap.add_argument("--flush-iters", type=int, default=30,
-                    help="extra steps timed singly after a 1 GiB cache flush (0: skip)")
+    ap.add_argument("--flush-iters", type=int, default=100,
+                    help="steps timed one at a time behind a 1 GiB write (the headline)")
+    ap.add_argument("--configs", default="C1,C3,C4,C5",
+                    help="other workloads measured with the same protocol ('none': skip)")
+    ap.add_argument("--no-paged-compare", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="run the streaming-read probe only")
     ap.add_argument("--lifecycle", action="store_true",
                     help="time the block-lifecycle calls instead (speculative rollback, "
                          "parallel sampling, block copies)")
@@ -431,13 +657,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from kv_cached_decode_kvc_amd import kvc, metrics, runner, synth
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    if args.probe:
+        print(json.dumps({"probe": probe()}), flush=True)
         return
 
     if args.lifecycle:
@@ -457,6 +686,7 @@ def main():
     torch.cuda.synchronize()
     assert lc.dev_status() == 0, "device status %d" % lc.dev_status()
 
+    # the timed region: K steady steps back to back, between synchronisations
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -465,47 +695,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert lc.dev_status() == 0
-    # the dominant kernel alone: K back-to-back launches on the stream the
-    # library launches on (torch's current stream), between two HIP events
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(K):
-        lc.step_partition()
-    ev1.record()
-    torch.cuda.synchronize()
-    part_ms = ev0.elapsed_time(ev1) / K
+    print("# %d steady steps: %.2f us/step" % (K, wall / K * 1e6), file=sys.stderr, flush=True)
+
+    # the headline: steps timed one at a time behind a 1 GiB write, so that no
+    # KV row comes from the last-level caches
+    F = max(1, args.flush_iters)
+    st_us, pt_us = flushed_steps(lc, F)
     assert lc.dev_status() == 0
+    print("# %d flushed steps: median %.2f us" % (F, pct(st_us, 50)), file=sys.stderr, flush=True)
 
     lens = synth.final_lengths(w)
     kv_bytes = metrics.attended_cache_bytes(lens, w.Hkv, w.kv_row_bytes, w.kv_tensors)
     # score and value products, 2 FLOP per multiply-add, over every visible (row, key)
     flops = metrics.attention_flops(lens, w.n_q, w.Hq, w.D) // 2 + \
         metrics.attention_flops(lens, w.n_q, w.Hq, w.out_dim) // 2
-    ms_per_step = wall / K * 1e3
-    value = kv_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = kv_bytes / (part_ms / 1e3) / 1e9
+    step_us, part_us = pct(st_us, 50), pct(pt_us, 50)
+    value = kv_bytes / (step_us * 1e-6) / 1e9
+    achieved = kv_bytes / (part_us * 1e-6) / 1e9
+    steady_ms = wall / K * 1e3
     kname, ksrc = kernel_of(w, mfma)
     shash = source_hash(ksrc)
     traffic = stored_traffic(w.name, kname, shash)
 
-    flushed = None
-    if args.flush_iters > 0:
-        st_us, pt_us = flushed_steps(lc, args.flush_iters)
-        assert lc.dev_status() == 0
-        flushed = {
-            "iters": args.flush_iters, "flush_bytes": 1 << 30,
-            "step_us": {"p10": pct(st_us, 10), "median": pct(st_us, 50), "p90": pct(st_us, 90)},
-            "partition_us": {"p10": pct(pt_us, 10), "median": pct(pt_us, 50),
-                             "p90": pct(pt_us, 90)},
-            "gbs_step_median": round(kv_bytes / (pct(st_us, 50) * 1e-6) / 1e9, 2),
-            "gbs_partition_median": round(kv_bytes / (pct(pt_us, 50) * 1e-6) / 1e9, 2),
-        }
-
-    graph = None
-    if w.steps > 1:
-        graph = graph_replay(w, lc)
-
+    graph = graph_replay(w, lc) if w.steps > 1 else None
     gpu_out = lc.s_out.cpu().numpy()
+    del lc
+    torch.cuda.empty_cache()
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -513,7 +729,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(step_us / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -526,10 +742,20 @@ def main():
             "accumulate": "f32", "cache": w.cache_dtype, "cache_row_bytes": w.kv_row_bytes,
             "cache_tensors": w.kv_tensors, "out_dim": w.out_dim,
         },
+        "timing": "value, ms_per_step and roofline use the median of %d steps (roofline: of their "
+                  "partition launches), each timed alone with HIP events behind a 1 GiB write "
+                  "that evicts the last-level caches; 'steady' is the timed region of %d "
+                  "back-to-back steps between two synchronisations" % (F, K),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
-        "seq_steps_per_s": round(w.B / (ms_per_step / 1e3), 1),
-        "query_rows_per_s": round(w.B * w.n_q / (ms_per_step / 1e3), 1),
+        "seq_steps_per_s": round(w.B / (step_us * 1e-6), 1),
+        "query_rows_per_s": round(w.B * w.n_q / (step_us * 1e-6), 1),
         "kv_bytes_per_step": kv_bytes,
+        "flushed": {"iters": F, "flush_bytes": 1 << 30, "step_us": stats(st_us),
+                    "partition_us": stats(pt_us)},
+        "steady": {"steps": K, "ms_per_step": round(steady_ms, 5),
+                   "gbs": round(kv_bytes / (steady_ms * 1e-3) / 1e9, 2),
+                   "hbm_frac_step": round(kv_bytes / (steady_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "seq_steps_per_s": round(w.B / (steady_ms * 1e-3), 1)},
         "roofline": {
             "bound": "hbm",
             "kernel": kname,
@@ -538,20 +764,20 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_kernel_us": round(part_ms * 1e3, 3),
+            "avg_kernel_us": round(part_us, 3),
+            "kernel_us": stats(pt_us),
             "algorithmic_bytes_per_launch": kv_bytes,
             "source_sha256": shash,
             "flops_per_launch": flops,
-            "achieved_tflops": round(flops / (part_ms / 1e3) / 1e12, 2),
-            "mfma_bf16_peak_tflops": 2500.0,
+            "achieved_tflops": round(flops / (part_us * 1e-6) / 1e12, 2),
+            "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
         },
-        "cache_flushed": flushed,
     }
     if w.prefill:  # compute-bound: the line reports FLOP/s against the matrix-core peak
         line["metric"] = PREFILL_METRIC
-        line["value"] = round(flops / (ms_per_step / 1e3) / 1e12, 2)
+        line["value"] = round(flops / (step_us * 1e-6) / 1e12, 2)
         line["unit"] = "TFLOP/s"
-        line["tokens_per_s"] = round(w.B * w.n_q / (ms_per_step / 1e3), 1)
+        line["tokens_per_s"] = round(w.B * w.n_q / (step_us * 1e-6), 1)
         rf = line["roofline"]
         rf.update({"bound": "mfma", "achieved": rf["achieved_tflops"],
                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -559,9 +785,20 @@ def main():
                    "hbm_gbs": round(achieved, 2)})
     if graph is not None:
         line["graph_replay"] = graph
+
+    configs = [c for c in args.configs.split(",") if c and c != "none"]
+    if configs:
+        line["configs"] = {c: config_result(c, min(args.warmup, 5), F, min(K, 50))
+                           for c in configs}
+    if not args.no_paged_compare and synth.get(args.workload).name == synth.get("C2").name:
+        line["paged_vs_contiguous"] = paged_vs_contiguous(F)
+    if not args.no_probe:
+        print("# streaming-read probe", file=sys.stderr, flush=True)
+        line["probe"] = probe()
     if args.no_cpu_baseline or w.prefill:  # prefill: the oracle takes minutes per sequence
         line["cpu_baseline"] = None
     else:
+        print("# oracle timing on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, gpu_out)
     print(json.dumps(line), flush=True)
 

@@ -227,7 +227,6 @@ size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
  * as given. */
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
 
-/* Static text for a kvc_status value. */
 /*
  * Block lifecycle (paged caches only): sharing, copy-on-write and rollback.
  *
@@ -385,6 +384,8 @@ int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q
  * codes and scales, or the plain elements.  0 on an invalid description. */
 size_t kvc_cache_bytes(const kvc_cache_desc* d);
 
+/* Static text for a kvc_status value (never NULL; "unknown status" for any
+ * other integer).  The string is owned by the library. */
 const char* kvc_status_string(int32_t status);
 
 #ifdef __cplusplus

@@ -1,4 +1,5 @@
-"""Compile the HIP sources in ``csrc/`` into ``libkvc.so`` next to this file.
+"""Compile the HIP sources in ``csrc/`` into ``libkvc.so`` next to this file,
+and the streaming-read probe in ``probe/`` into ``probe/libkvc_probe.so``.
 
 gfx950 only.  Every source is built with the packed-fp32 target feature
 switched off (the compiler would otherwise fuse pairs of fp32 operations into
@@ -20,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "kvc")
 LIB = os.path.join(PKG, "libkvc.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PROBE_DIR, "libkvc_probe.so")
 ARCH = "gfx950"
 
 CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -33,13 +36,13 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d: str = CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, include: str = "") -> str:
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *(["-I" + include] if include else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -49,17 +52,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, lib: str):
+    tmp = lib + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs,
+                           "-o", tmp])
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    probe_srcs = sources(PROBE_DIR)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs,
-                           "-o", tmp])
-    os.replace(tmp, LIB)
+        probe_objs = list(ex.map(lambda f: _compile(f, PROBE_DIR), probe_srcs))
+    _link(objs, LIB)
+    _link(probe_objs, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -99,14 +99,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   const int q0 = p.cu_q[b], n_b = p.cu_q[b + 1] - q0;
   const int R = n_b * p.G;                      // rows of this (sequence, KV head)
   const int row0 = it.rt * rows_wg;
-  if (it.rt == 0 && g == 0 && tid == 0 && (long)R > (long)n_rt * rows_wg)
-    report(p.status, KVC_ERR_DATA);  // a chunk longer than max_q: its last rows are not computed
-  if (row0 >= R) return;  // whole workgroup
+  // Offsets and length are checked before anything else, so that a
+  // decreasing cu_q (a negative chunk) is reported rather than skipped.
   const int L = p.seq_lens[b];
   if (n_b < 0 || L < n_b || L > p.cap || q0 < 0 || q0 + n_b > p.total_q) {
     if (it.rt == 0 && g == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
-    return;
+    return;  // whole workgroup
   }
+  if (it.rt == 0 && g == 0 && tid == 0 && (long)R > (long)n_rt * rows_wg)
+    report(p.status, KVC_ERR_DATA);  // a chunk longer than max_q: its last rows are not computed
+  if (row0 >= R) return;  // whole workgroup
   const int cached = L - n_b;
 
   int lvis[NT];

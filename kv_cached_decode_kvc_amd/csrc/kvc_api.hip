@@ -196,9 +196,11 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   return pl;
 }
 
+// Host checks of an attention call; on success *pl holds the call's plan
+// (computed once per entry-point call and handed to both stages).
 int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, const void* v,
                const int32_t* seq_lens, const int32_t* table, float scale, const void* ws,
-               size_t ws_bytes) {
+               size_t ws_bytes, Plan* pl) {
   int st = check_desc(d);
   if (st != KVC_OK) return st;
   if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
@@ -208,9 +210,23 @@ int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, c
   if ((d->block_size > 0) != (table != nullptr)) return KVC_ERR_ARG;
   if (!isfinite(scale)) return KVC_ERR_ARG;
   if (((uintptr_t)ws & 15) != 0) return KVC_ERR_ARG;
-  const Plan pl = make_plan(d, n_q);
-  if (pl.grid > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;  // one workgroup per work item
-  if (ws_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
+  *pl = make_plan(d, n_q);
+  if (pl->grid > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;  // one workgroup per work item
+  if (ws_bytes < pl->bytes) return KVC_ERR_WORKSPACE;
+  return KVC_OK;
+}
+
+// Host checks of a reduce call that are not covered by check_attn.
+int check_reduce(const kvc_cache_desc* d, int n_q, const int32_t* seq_lens, const void* ws,
+                 const void* out, int32_t out_dtype) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // kvc_mla_attn_reduce
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!seq_lens || !ws || !out) return KVC_ERR_ARG;
+  if (((uintptr_t)ws & 15) != 0) return KVC_ERR_ARG;
   return KVC_OK;
 }
 
@@ -244,6 +260,46 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   if (fp8_format(d) && d->block_size == 0) p.S_max = (int)fp8_padded_rows(d->max_seq_len);
   return p;
+}
+
+ReduceParams reduce_params(const kvc_cache_desc* d, const Plan& pl, int n_q, int D,
+                           const int32_t* seq_lens, const void* ws, void* out,
+                           int32_t* status) {
+  ReduceParams p{};
+  p.ws_o = (const float*)ws;
+  p.ws_ml = (const float*)((const char*)ws + pl.ml_offset);
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.status = status;
+  p.B = d->batch;
+  p.n_q = n_q;
+  p.Hq = d->num_q_heads;
+  p.D = D;
+  p.P = pl.P;
+  p.P_lo = pl.P_lo;
+  p.slots_u = pl.slots_u;
+  p.max_parts = pl.max_parts;
+  p.cap = capacity(d);
+  return p;
+}
+
+// The two stages of decode / verify attention with a plan already checked.
+int run_partition(const kvc_cache_desc* d, const Plan& pl, const void* q, int n_q,
+                  const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                  const int32_t* block_table, float scale, void* ws, int32_t* status,
+                  void* stream) {
+  const AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
+                                   ws, status);
+  hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, fp8_format(d),
+                                                 (hipStream_t)stream)
+                         : launch_partition_valu(p, d->dtype, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+int run_reduce(const kvc_cache_desc* d, const Plan& pl, int n_q, int D, const int32_t* seq_lens,
+               const void* ws, void* out, int32_t out_dtype, int32_t* status, void* stream) {
+  const ReduceParams p = reduce_params(d, pl, n_q, D, seq_lens, ws, out, status);
+  return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -322,64 +378,41 @@ int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, cons
                        const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
                        float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,
                        void* stream) {
+  Plan pl{};
   int st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
-                      workspace_bytes);
+                      workspace_bytes, &pl);
   if (st != KVC_OK || d->batch == 0) return st;
-  const Plan pl = make_plan(d, n_q);
-  const AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
-                                   workspace, dev_status);
-  hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, fp8_format(d),
-                                                 (hipStream_t)stream)
-                         : launch_partition_valu(p, d->dtype, (hipStream_t)stream);
-  return hip_status(e);
+  return run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
+                       dev_status, stream);
 }
 
 int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_lens,
                     const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                     int32_t* dev_status, void* stream) {
-  int st = check_desc(d);
-  if (st != KVC_OK) return st;
-  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
-  if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // kvc_mla_attn_reduce
-  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
-  if (d->batch == 0) return KVC_OK;
-  if (!seq_lens || !workspace || !out) return KVC_ERR_ARG;
-  if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
+  int st = check_reduce(d, n_q, seq_lens, workspace, out, out_dtype);
+  if (st != KVC_OK || d->batch == 0) return st;
   const Plan pl = make_plan(d, n_q);
   if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
-  ReduceParams p{};
-  p.ws_o = (const float*)workspace;
-  p.ws_ml = (const float*)((const char*)workspace + pl.ml_offset);
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.status = dev_status;
-  p.B = d->batch;
-  p.n_q = n_q;
-  p.Hq = d->num_q_heads;
-  p.D = d->head_dim;
-  p.P = pl.P;
-  p.P_lo = pl.P_lo;
-  p.slots_u = pl.slots_u;
-  p.max_parts = pl.max_parts;
-  p.cap = capacity(d);
-  return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
+  return run_reduce(d, pl, n_q, d->head_dim, seq_lens, workspace, out, out_dtype, dev_status,
+                    stream);
 }
 
 int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
                     const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
                     float scale, void* out, int32_t out_dtype, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  Plan pl{};
   int st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
-                      workspace_bytes);
+                      workspace_bytes, &pl);
   if (st != KVC_OK) return st;
   if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (d->batch == 0) return KVC_OK;
   if (!out) return KVC_ERR_ARG;
-  st = kvc_attn_partition(d, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
-                          workspace_bytes, dev_status, stream);
+  st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
+                     dev_status, stream);
   if (st != KVC_OK) return st;
-  return kvc_attn_reduce(d, n_q, seq_lens, workspace, workspace_bytes, out, out_dtype, dev_status,
-                         stream);
+  return run_reduce(d, pl, n_q, d->head_dim, seq_lens, workspace, out, out_dtype, dev_status,
+                    stream);
 }
 
 int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
@@ -524,7 +557,9 @@ int kvc_mla_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q,
   if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
   const AttnParams p = attn_params(d, pl, n_q, q, latent_cache, latent_cache, seq_lens,
                                    block_table, scale, workspace, dev_status);
-  return hip_status(launch_partition_mla(p, (hipStream_t)stream));
+  st = hip_status(launch_partition_mla(p, (hipStream_t)stream));
+  if (st != KVC_OK) return st;
+  return KVC_OK;
 }
 
 int kvc_mla_attn_reduce(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim,
@@ -538,22 +573,8 @@ int kvc_mla_attn_reduce(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim,
   if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
   const Plan pl = make_mla_plan(d, n_q);
   if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
-  ReduceParams p{};
-  p.ws_o = (const float*)workspace;
-  p.ws_ml = (const float*)((const char*)workspace + pl.ml_offset);
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.status = dev_status;
-  p.B = d->batch;
-  p.n_q = n_q;
-  p.Hq = d->num_q_heads;
-  p.D = kMlaValueDim;
-  p.P = pl.P;
-  p.P_lo = pl.P_lo;
-  p.slots_u = pl.slots_u;
-  p.max_parts = pl.max_parts;
-  p.cap = capacity(d);
-  return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
+  return run_reduce(d, pl, n_q, kMlaValueDim, seq_lens, workspace, out, out_dtype, dev_status,
+                    stream);
 }
 
 int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* latent_cache,
@@ -564,12 +585,18 @@ int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void
   if (st != KVC_OK) return st;
   if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
   if (d->batch == 0) return KVC_OK;
-  if (!out) return KVC_ERR_ARG;
-  st = kvc_mla_attn_partition(d, q, n_q, latent_cache, seq_lens, block_table, value_dim, scale,
-                              workspace, workspace_bytes, dev_status, stream);
+  if (!q || !latent_cache || !seq_lens || !workspace || !out) return KVC_ERR_ARG;
+  if ((d->block_size > 0) != (block_table != nullptr)) return KVC_ERR_ARG;
+  if (!isfinite(scale)) return KVC_ERR_ARG;
+  if (((uintptr_t)workspace & 15) != 0) return KVC_ERR_ARG;
+  const Plan pl = make_mla_plan(d, n_q);
+  if (workspace_bytes < pl.bytes) return KVC_ERR_WORKSPACE;
+  const AttnParams p = attn_params(d, pl, n_q, q, latent_cache, latent_cache, seq_lens,
+                                   block_table, scale, workspace, dev_status);
+  st = hip_status(launch_partition_mla(p, (hipStream_t)stream));
   if (st != KVC_OK) return st;
-  return kvc_mla_attn_reduce(d, n_q, value_dim, seq_lens, workspace, workspace_bytes, out,
-                             out_dtype, dev_status, stream);
+  return run_reduce(d, pl, n_q, kMlaValueDim, seq_lens, workspace, out, out_dtype, dev_status,
+                    stream);
 }
 
 int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q, int32_t total_q,

@@ -69,7 +69,7 @@ class LayerCache:
             self.free_list = i32(self.free_host, dev)
             self.head = torch.zeros(1, dtype=torch.int32, device=dev)
         self.shape = shape
-        if w.kv:  # FP8: codes, then (at a 256-byte boundary) one float32 scale per row
+        if w.kv:  # FP8: tiles of 16 rows, each the rows' codes followed by their 16 float32 scales
             nbytes = kvc.kvc_cache_bytes(self.desc)
             self.k = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
             self.v = torch.zeros(nbytes, dtype=torch.uint8, device=dev)

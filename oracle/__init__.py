@@ -30,11 +30,12 @@ FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle with gcc into ``out`` (plain -O2, no fast-math)."""
+    """Compile the oracle with gcc into ``out`` (plain -O2, no fast-math;
+    OpenMP only for the many-sequence timing function)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+            ["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-fPIC", "-shared", "-fopenmp",
              "-Wall", "-Werror", src, "-o", tmp, "-lm"])
         os.replace(tmp, out)
     return out
@@ -74,7 +75,9 @@ class Oracle:
         lib.kvc_ref_dequantize_rows.argtypes = [P, P, ctypes.c_long, I, I, P]
         lib.kvc_ref_dequantize_rows.restype = None
         lib.kvc_ref_mla_attention.argtypes = [I, I, I, I, I, P, P, ctypes.c_double, P]
-        for name in ("kvc_ref_mla_attention", "kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
+        lib.kvc_ref_attention_many.argtypes = [I, I, I, I, I, I, I, P, P, P, P, ctypes.c_double,
+                                               P, P]
+        for name in ("kvc_ref_attention_many", "kvc_ref_mla_attention", "kvc_ref_fork", "kvc_ref_truncate", "kvc_ref_cow",
                      "kvc_ref_block_table", "kvc_ref_append", "kvc_ref_gather",
                      "kvc_ref_attention", "kvc_ref_cache_attention",
                      "kvc_ref_attention_split"):
@@ -272,6 +275,32 @@ class Oracle:
         if st != 0:
             raise ValueError("attention failed: %d" % st)
         return out
+
+    # -- kvc_ref_attention_many ---------------------------------------------
+    def attention_many(self, qs, ks, vs, scale, dtype, dv=0):
+        """Several sequences at once on all host cores (one OpenMP iteration per
+        (sequence, query head)): qs[s] [n_q, Hq, Dk], ks[s]/vs[s] [Hkv, L_s, Dk]
+        (MLA, dv > 0: ks[s] = latent rows [L_s, Dk], vs ignored) -> (list of
+        out [n_q, Hq, Dout] float64, threads used)."""
+        nd = NP_DTYPES[dtype]
+        qs = [self._c(q, nd) for q in qs]
+        ks = [self._c(k, nd) for k in ks]
+        vs = [self._c(v, nd) for v in vs] if not dv else ks
+        n = len(qs)
+        if n == 0:
+            return [], 0
+        n_q, Hq, Dk = qs[0].shape
+        Hkv = 1 if dv else ks[0].shape[0]
+        L = np.array([k.shape[0] if dv else k.shape[1] for k in ks], dtype=np.int32)
+        outs = [np.zeros((n_q, Hq, dv or Dk), dtype=np.float64) for _ in range(n)]
+        arr = lambda xs: (ctypes.c_void_p * n)(*[x.ctypes.data for x in xs])
+        threads = ctypes.c_int(0)
+        st = self.lib.kvc_ref_attention_many(n, n_q, Hq, Hkv, Dk, dv, DTYPES[dtype], self._p(L),
+                                             arr(qs), arr(ks), arr(vs), float(scale), arr(outs),
+                                             ctypes.byref(threads))
+        if st != 0:
+            raise ValueError("attention_many failed: %d" % st)
+        return outs, threads.value
 
     # -- kvc_ref_attention_split --------------------------------------------
     def attention_split(self, q, k, v, scale, dtype, P):

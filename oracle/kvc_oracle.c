@@ -31,6 +31,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* status codes (the same integers the library returns; values restated here) */
 #define REF_OK 0
@@ -705,4 +708,70 @@ int kvc_ref_mla_attention(int n_q, int Hq, int Dk, int Dv, int L, const uint16_t
     }
   free(p);
   return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Many sequences at once on all host cores -- a timing aid for the CPU
+ * baseline, not a different computation.  Every (sequence, query head) pair
+ * is one OpenMP iteration that evaluates the definition above for that head
+ * alone: kvc_ref_attention (dv == 0) or kvc_ref_mla_attention (dv > 0, one
+ * latent head, bf16).  The head's query rows are copied out, its KV head's
+ * rows are passed in place, and the head's result is copied back, so every
+ * number is the one the single-threaded definition gives.
+ *   q[s]   [n_q][Hq][Dk] (dtype)
+ *   k[s], v[s] [Hkv][L[s]][Dk] (dtype); dv > 0: k[s] = [L[s]][Dk] latent rows, v unused
+ *   out[s] [n_q][Hq][Dout] double, Dout = dv > 0 ? dv : Dk
+ * Returns the first failing status (REF_OK when all succeed); *threads
+ * receives the number of threads that ran. */
+int kvc_ref_attention_many(int nseq, int n_q, int Hq, int Hkv, int Dk, int dv, int dtype,
+                           const int32_t* L, const void* const* q, const void* const* k,
+                           const void* const* v, double scale, double* const* out,
+                           int* threads) {
+  if (nseq < 0 || n_q <= 0 || Hq <= 0 || Hkv <= 0 || Dk <= 0 || Hq % Hkv != 0) return REF_ERR_ARG;
+  if (dv > 0 && (Hkv != 1 || dtype != REF_BF16 || dv > Dk)) return REF_ERR_ARG;
+  const size_t es = dtype == REF_BF16 ? 2 : dtype == REF_F32 ? 4 : 8;
+  const int G = Hq / Hkv, Dout = dv > 0 ? dv : Dk;
+  const long pairs = (long)nseq * Hq;
+  int status = REF_OK, team = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    {
+#ifdef _OPENMP
+      team = omp_get_num_threads();
+#endif
+    }
+    char* qh = (char*)malloc(es * (size_t)n_q * Dk);
+    double* oh = (double*)malloc(sizeof(double) * (size_t)n_q * Dout);
+#pragma omp for schedule(dynamic, 1)
+    for (long i = 0; i < pairs; ++i) {
+      const int s = (int)(i / Hq), h = (int)(i % Hq), g = h / G;
+      int st = REF_ERR_ARG;
+      if (qh && oh) {
+        for (int r = 0; r < n_q; ++r)
+          memcpy(qh + es * (size_t)r * Dk, (const char*)q[s] + es * ((size_t)r * Hq + h) * Dk,
+                 es * (size_t)Dk);
+        if (dv > 0) {
+          st = kvc_ref_mla_attention(n_q, 1, Dk, dv, L[s], (const uint16_t*)qh,
+                                     (const uint16_t*)k[s], scale, oh);
+        } else {
+          const size_t kv_off = es * (size_t)g * L[s] * Dk;
+          st = kvc_ref_attention(n_q, 1, 1, Dk, L[s], dtype, qh, (const char*)k[s] + kv_off,
+                                 (const char*)v[s] + kv_off, scale, oh);
+        }
+        if (st == REF_OK)
+          for (int r = 0; r < n_q; ++r)
+            memcpy(out[s] + ((size_t)r * Hq + h) * Dout, oh + (size_t)r * Dout,
+                   sizeof(double) * (size_t)Dout);
+      }
+      if (st != REF_OK) {
+#pragma omp critical
+        if (status == REF_OK) status = st;
+      }
+    }
+    free(qh);
+    free(oh);
+  }
+  if (threads) *threads = team;
+  return status;
 }

@@ -64,8 +64,7 @@ def test_mla_bf16_output_and_refusals(ref):
     want = oracle_outputs(ref, w, range(2), lengths - 1, scale=SCALE)
     got = out.float().cpu().numpy()
     for b in range(2):
-        err = np.abs(got[b] - want[b])
-        assert np.all(err <= 2e-3 + 1e-2 * np.abs(want[b]) + np.abs(want[b]) * 2.0 ** -8)
+        assert_close(got[b], want[b], "bf16 out b=%d" % b, bf16_out=True)
     # the ordinary attention calls refuse the latent geometry, MLA refuses others
     ws = gc.workspace(1)
     o2 = torch.empty((2, 1, 16, 576), dtype=torch.float32, device="cuda")
@@ -108,26 +107,6 @@ def test_mla_bad_length_reports_and_others_unchanged(ref, bad_len):
     got = out.cpu().numpy()
     for b in [0, 2]:
         assert_close(got[b], want[b], "b=%d" % b)
-
-
-@pytest.mark.parametrize("name", ["M1", "M2"])
-def test_mla_full_size_sampled(ref, name):
-    w = synth.get(name)
-    print("full-size MLA workload", w.name, flush=True)
-    lc = runner.build(w)
-    out1 = lc.step().clone()
-    out2 = lc.step().clone()
-    assert lc.dev_status() == 0
-    assert torch.equal(out1, out2)
-    lens = synth.final_lengths(w)
-    cached = synth.cached_lengths(w)
-    sample = sorted({0, w.B - 1, int(np.argmax(lens)), int(np.argmin(lens))})
-    want = oracle_outputs(ref, w, sample, cached)
-    got = out1.cpu().numpy()
-    for b in sample:
-        assert_close(got[b], want[b], "%s b=%d L=%d" % (name, b, lens[b]))
-    del lc
-    torch.cuda.empty_cache()
 
 
 def test_mla_graph_replay_and_key_only_copies(ref):
