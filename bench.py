@@ -193,27 +193,29 @@ def pct(xs, q):
 
 
 def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
-    """Steps timed one at a time with a >= 1 GiB write between them, so that no
+    """Steps timed one at a time with a >= 1 GiB write before each, so that no
     KV row is served from the last-level caches; HIP events on the library's
-    stream.  Returns (step us list, partition us list)."""
+    stream.  Returns (step us list, partition us list).
+
+    A step's events bracket the whole step only: an event recorded between
+    two kernels of the step adds its own dispatch gap (about 5.6 us in the
+    kernel trace, against none between two kernels without one), so the
+    partition launches are timed in a second flushed loop of their own."""
     import torch
     buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
-    step_us, part_us = [], []
+    step_us = []
     for i in range(iters):
         buf.fill_(float(i))
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        e[0].record()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         lc.step_front()
-        e[1].record()
         lc.step_partition()
-        e[2].record()
         lc.step_reduce()
-        e[3].record()
+        e1.record()
         torch.cuda.synchronize()
-        step_us.append(e[0].elapsed_time(e[3]) * 1e3)
-        part_us.append(e[1].elapsed_time(e[2]) * 1e3)
+        step_us.append(e0.elapsed_time(e1) * 1e3)
     del buf
-    return step_us, part_us
+    return step_us, flushed_partitions(lc.step_partition, iters, flush_bytes)
 
 
 class CallTimer:
@@ -742,10 +744,11 @@ def main():
             "accumulate": "f32", "cache": w.cache_dtype, "cache_row_bytes": w.kv_row_bytes,
             "cache_tensors": w.kv_tensors, "out_dim": w.out_dim,
         },
-        "timing": "value, ms_per_step and roofline use the median of %d steps (roofline: of their "
-                  "partition launches), each timed alone with HIP events behind a 1 GiB write "
-                  "that evicts the last-level caches; 'steady' is the timed region of %d "
-                  "back-to-back steps between two synchronisations" % (F, K),
+        "timing": "value and ms_per_step use the median of %d steps, each timed alone with HIP "
+                  "events at its two ends behind a 1 GiB write that evicts the last-level caches; "
+                  "roofline uses the median of %d partition launches timed the same way; 'steady' "
+                  "is the timed region of %d back-to-back steps between two synchronisations"
+                  % (F, F, K),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.B / (step_us * 1e-6), 1),
         "query_rows_per_s": round(w.B * w.n_q / (step_us * 1e-6), 1),

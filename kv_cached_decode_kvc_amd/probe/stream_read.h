@@ -15,9 +15,9 @@ extern "C" {
 #endif
 
 /* Read `bytes` (a multiple of 16) of device memory at `src` (16-byte
- * aligned) once, with `workgroups` workgroups of 256 threads striding over
- * it, four 16-byte loads in flight per thread; ordinary loads, or
- * non-temporal ones when `nontemporal` != 0.  `sink` (device, 4 bytes) is
+ * aligned) once, with `workgroups` workgroups of 256 threads, each streaming
+ * one contiguous share 16 KiB at a time with four 16-byte loads in flight
+ * per thread; ordinary loads, or non-temporal ones when `nontemporal` != 0.  `sink` (device, 4 bytes) is
  * written only in the improbable case that the combined data equals a fixed
  * constant.  Asynchronous on `stream` (a hipStream_t, NULL = default).
  * Returns 0, -1 for a bad argument, -7 for a failed launch. */

@@ -2,13 +2,14 @@
 //
 // Not part of the decode path: it gives the read rate a kernel can reach on
 // this device, the ceiling next to which the attention kernels' achieved
-// bandwidth is read.  Every thread reads 16-byte pieces of one buffer, four
-// in flight, consecutive lanes on consecutive pieces (a wavefront instruction
-// covers 1 KiB), the grid striding over the whole buffer.  Loads are either
-// ordinary or non-temporal (the form the partition kernels use for KV rows
-// that are read once).  The loaded words are combined and compared with a
-// constant, so the loads cannot be dropped; nothing is stored unless the
-// combination happens to equal it.
+// bandwidth is read.  Each workgroup of 256 threads streams one contiguous
+// share of the buffer, 16 KiB per step (a wavefront instruction covers 1 KiB
+// of consecutive 16-byte pieces), with `UNROLL` steps' loads in flight per
+// thread -- the access pattern of a partition kernel reading its keys.
+// Loads are either ordinary or non-temporal (the form the partition kernels
+// use for KV rows that are read once).  The loaded words are combined and
+// compared with a constant, so the loads cannot be dropped; nothing is
+// stored unless the combination happens to equal it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,6 +19,10 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr long kStep16 = (long)kThreads * kUnroll;  // 16-byte pieces per workgroup step
+
 template <bool NT>
 __device__ __forceinline__ u32x4_t load16(const u32x4_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -25,22 +30,23 @@ __device__ __forceinline__ u32x4_t load16(const u32x4_t* p) {
 }
 
 template <bool NT>
-__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src,
-                                                          long n16, uint32_t* sink) {
-  const long stride = (long)gridDim.x * blockDim.x;
-  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4_t* __restrict__ src,
+                                                               long n16, long share16,
+                                                               uint32_t* sink) {
+  const long lo = (long)blockIdx.x * share16;
+  const long hi = lo + share16 < n16 ? lo + share16 : n16;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4_t a = load16<NT>(src + i);
-    const u32x4_t b = load16<NT>(src + i + stride);
-    const u32x4_t c = load16<NT>(src + i + 2 * stride);
-    const u32x4_t d = load16<NT>(src + i + 3 * stride);
-    acc ^= (a.x ^ a.y ^ a.z ^ a.w) + (b.x ^ b.y ^ b.z ^ b.w) + (c.x ^ c.y ^ c.z ^ c.w) +
-           (d.x ^ d.y ^ d.z ^ d.w);
+  long i = lo + threadIdx.x;
+  for (; i + (kUnroll - 1) * kThreads < hi; i += kStep16) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load16<NT>(src + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < hi; i += kThreads) {
     const u32x4_t a = load16<NT>(src + i);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    acc += a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == 0x9e3779b9u) sink[0] = (uint32_t)i;
 }
@@ -52,12 +58,15 @@ extern "C" int kvc_probe_stream_read(const void* src, size_t bytes, int nontempo
   if (!src || !sink || bytes % 16 != 0 || workgroups <= 0) return -1;
   if (((uintptr_t)src & 15) != 0) return -1;
   const long n16 = (long)(bytes / 16);
-  const dim3 grid(workgroups), block(256);
+  // each workgroup's share: whole steps of 16 KiB (the last share may be short)
+  const long steps = (n16 + kStep16 - 1) / kStep16;
+  const long share16 = (steps + workgroups - 1) / workgroups * kStep16;
+  const dim3 grid(workgroups), block(kThreads);
   if (nontemporal)
     hipLaunchKernelGGL(stream_read_kernel<true>, grid, block, 0, (hipStream_t)stream,
-                       (const u32x4_t*)src, n16, sink);
+                       (const u32x4_t*)src, n16, share16, sink);
   else
     hipLaunchKernelGGL(stream_read_kernel<false>, grid, block, 0, (hipStream_t)stream,
-                       (const u32x4_t*)src, n16, sink);
+                       (const u32x4_t*)src, n16, share16, sink);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
