@@ -199,6 +199,26 @@ int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const v
                     float scale, void* out, int32_t out_dtype, void* workspace,
                     size_t workspace_bytes, int32_t* dev_status, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kvc_verify_attn (n_q = 1: kvc_decode_attn) without the workspace
+ * arguments.  The split-KV partials go to a static device array of
+ * KVC_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one copy per
+ * device, held until the process ends; nothing is allocated, freed or
+ * synchronised.  A call whose kvc_attn_workspace_bytes exceeds that size
+ * returns KVC_ERR_WORKSPACE before any launch.  `stream` must belong to the
+ * current device (else KVC_ERR_ARG); a failed lookup of the array's
+ * address returns KVC_ERR_HIP.  Every call on one device shares its array,
+ * which keeps the last call's partials (nothing in it needs to start at
+ * zero): calls that overlap on one device -- on different streams, or from
+ * different host threads without ordering -- race and give undefined
+ * results.  Other arguments, checks and results as kvc_verify_attn. */
+#define KVC_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kvc_verify_attn_noalloc(const kvc_cache_desc* d, const void* q, int32_t n_q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, float scale, void* out,
+                            int32_t out_dtype, int32_t* dev_status, void* stream);
+
 /*
  * The two stages kvc_verify_attn runs, exported so that each can be timed on
  * its own: kvc_attn_partition writes every (row, partition) partial -- running

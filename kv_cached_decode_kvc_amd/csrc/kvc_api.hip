@@ -1,9 +1,11 @@
 // kvc_api.hip -- the C ABI of libkvc.so: argument checks, work planning and
-// kernel launches on the caller's stream.  Host code only; no allocation, no
-// synchronisation, no global state.
+// kernel launches on the caller's stream.  Host code; no allocation, no
+// synchronisation.  The only global state is the static scratch array of
+// kvc_verify_attn_noalloc (one copy per device) and its per-device address.
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -196,19 +198,28 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   return pl;
 }
 
-// Host checks of an attention call; on success *pl holds the call's plan
-// (computed once per entry-point call and handed to both stages).
-int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, const void* v,
-               const int32_t* seq_lens, const int32_t* table, float scale, const void* ws,
-               size_t ws_bytes, Plan* pl) {
+// Host checks of an attention call's arguments, workspace aside.
+int check_attn_args(const kvc_cache_desc* d, int n_q, const void* q, const void* k,
+                    const void* v, const int32_t* seq_lens, const int32_t* table, float scale) {
   int st = check_desc(d);
   if (st != KVC_OK) return st;
   if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
   if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // the kvc_mla_* calls
   if (d->batch == 0) return KVC_OK;
-  if (!q || !k || !v || !seq_lens || !ws) return KVC_ERR_ARG;
+  if (!q || !k || !v || !seq_lens) return KVC_ERR_ARG;
   if ((d->block_size > 0) != (table != nullptr)) return KVC_ERR_ARG;
   if (!isfinite(scale)) return KVC_ERR_ARG;
+  return KVC_OK;
+}
+
+// Host checks of an attention call; on success *pl holds the call's plan
+// (computed once per entry-point call and handed to both stages).
+int check_attn(const kvc_cache_desc* d, int n_q, const void* q, const void* k, const void* v,
+               const int32_t* seq_lens, const int32_t* table, float scale, const void* ws,
+               size_t ws_bytes, Plan* pl) {
+  int st = check_attn_args(d, n_q, q, k, v, seq_lens, table, scale);
+  if (st != KVC_OK || d->batch == 0) return st;
+  if (!ws) return KVC_ERR_ARG;
   if (((uintptr_t)ws & 15) != 0) return KVC_ERR_ARG;
   *pl = make_plan(d, n_q);
   if (pl->grid > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;  // one workgroup per work item
@@ -300,6 +311,32 @@ int run_reduce(const kvc_cache_desc* d, const Plan& pl, int n_q, int D, const in
                const void* ws, void* out, int32_t out_dtype, int32_t* status, void* stream) {
   const ReduceParams p = reduce_params(d, pl, n_q, D, seq_lens, ws, out, status);
   return hip_status(launch_reduce(p, out_dtype, (hipStream_t)stream));
+}
+
+// Scratch of kvc_verify_attn_noalloc: the split-KV partials (partial outputs
+// and their (m, l) statistics) live in this file-scope device array instead
+// of a caller-provided workspace.  Every device the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host
+// stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in `g_scratch_dev`.
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device (null: not yet)
+
+// Device address of `scratch` on the current device, or null on a HIP error.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
 }
 
 }  // namespace
@@ -421,6 +458,37 @@ int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
                     size_t workspace_bytes, int32_t* dev_status, void* stream) {
   return kvc_verify_attn(d, q, 1, k_cache, v_cache, seq_lens, block_table, scale, out, out_dtype,
                          workspace, workspace_bytes, dev_status, stream);
+}
+
+int kvc_verify_attn_noalloc(const kvc_cache_desc* d, const void* q, int32_t n_q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            const int32_t* block_table, float scale, void* out,
+                            int32_t out_dtype, int32_t* dev_status, void* stream) {
+  // Every host check first, the scratch size included, so that a refused
+  // call makes no device call; the scratch address is looked up only for a
+  // call that runs.
+  int st = check_attn_args(d, n_q, q, k_cache, v_cache, seq_lens, block_table, scale);
+  if (st != KVC_OK) return st;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return KVC_OK;
+  if (!out) return KVC_ERR_ARG;
+  const Plan pl = make_plan(d, n_q);
+  if (pl.grid > 0x7fffffffL) return KVC_ERR_UNSUPPORTED;
+  if (pl.bytes > (size_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_ERR_WORKSPACE;
+  if (stream) {  // the kernels run on the stream's device: it must be the current one
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess ||
+        hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+      return KVC_ERR_HIP;
+    if (sdev != cur) return KVC_ERR_ARG;
+  }
+  void* ws = scratch_ptr();
+  if (!ws) return KVC_ERR_HIP;
+  st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, ws,
+                     dev_status, stream);
+  if (st != KVC_OK) return st;
+  return run_reduce(d, pl, n_q, d->head_dim, seq_lens, ws, out, out_dtype, dev_status, stream);
 }
 
 int kvc_fork(const kvc_cache_desc* d, const int32_t* parents, const int32_t* children,

@@ -28,7 +28,8 @@ EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn"
            "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
            "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_mla_workspace_bytes",
            "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
-           "kvc_mla_attn", "kvc_prefill_attn", "kvc_status_string")
+           "kvc_mla_attn", "kvc_prefill_attn", "kvc_status_string", "kvc_verify_attn_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KVC_NOALLOC_SCRATCH_BYTES
 
 
 class KvcError(RuntimeError):
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_size_t, P, P]
         L.kvc_attn_partition.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t,
                                          P, P]
+        L.kvc_verify_attn_noalloc.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, I, P, P]
+        L.kvc_verify_attn_noalloc.restype = ctypes.c_int
         L.kvc_attn_reduce.argtypes = [D, I, P, P, ctypes.c_size_t, P, I, P, P]
         L.kvc_fork.argtypes = [D, P, P, I, P, P, P, P, P]
         L.kvc_truncate.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
@@ -179,6 +182,15 @@ def kvc_verify_attn(desc, q, n_q, k_cache, v_cache, seq_lens, block_table, scale
         _out_dtype(out, out_dtype), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(dev_status, "dev_status", I32),
         _stream(stream)))
+
+
+def kvc_verify_attn_noalloc(desc, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, out,
+                            dev_status=None, stream=None, out_dtype=None):
+    _check("kvc_verify_attn_noalloc", lib().kvc_verify_attn_noalloc(
+        ctypes.byref(desc), _ptr(q, "q"), int(n_q), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(seq_lens, "seq_lens", I32),
+        _ptr(block_table, "block_table", I32), float(scale), _ptr(out, "out"),
+        _out_dtype(out, out_dtype), _ptr(dev_status, "dev_status", I32), _stream(stream)))
 
 
 def kvc_attn_partition(desc, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,

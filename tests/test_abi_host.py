@@ -179,3 +179,23 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(16)
     with pytest.raises(ValueError):
         kvc.kvc_decode_attn(d, t, t, t, t.int(), None, 0.1, t, t)
+
+
+def test_noalloc_refusals_before_any_device_call(lib):
+    """The allocation-free attention call refuses on the host: a batch whose
+    partials exceed the static scratch, bad row counts, a missing output."""
+    big = desc(batch=128, num_q_heads=32, num_kv_heads=8, dtype=0, block_size=16,
+               max_seq_len=0, max_blocks_per_seq=4096, num_blocks=600000)
+    need = lib.kvc_attn_workspace_bytes(ctypes.byref(big), 16)
+    assert need > kvc.NOALLOC_SCRATCH_BYTES
+    call = lambda d, n_q=1, out=FAKE: lib.kvc_verify_attn_noalloc(
+        ctypes.byref(d), FAKE, n_q, FAKE, FAKE, FAKE, FAKE if d.block_size else None, 0.1, out,
+        1, None, None)
+    assert call(big, 16) == -4  # KVC_ERR_WORKSPACE
+    assert call(desc(), 0) == -3
+    assert call(desc(), 17) == -3
+    assert call(desc(), 1, None) == -1
+    assert lib.kvc_verify_attn_noalloc(ctypes.byref(desc()), FAKE, 1, FAKE, FAKE, FAKE, None,
+                                       0.1, FAKE, 5, None, None) == -3  # output type
+    assert lib.kvc_verify_attn_noalloc(ctypes.byref(desc(batch=0)), None, 1, None, None, None,
+                                       None, 0.1, None, 1, None, None) == 0

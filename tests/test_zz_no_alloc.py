@@ -1,0 +1,56 @@
+"""The allocation-free attention entry point (static device scratch instead
+of a caller workspace) gives the same outputs as kvc_verify_attn with a
+workspace, bit for bit, on two calls in a row -- the second on a smaller
+batch, so it runs over the first call's leftover partials."""
+import math
+
+import pytest
+import torch
+
+from kv_cached_decode_kvc_amd import kvc, synth
+from gpu_harness import GpuCache, assert_close, oracle_outputs, queries_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # the first is the larger
+    synth.custom(name="na-gqa-verify-paged", seed=4100, B=6, Hq=8, Hkv=2, D=128, dtype="bf16",
+                 block_size=16, n_q=5, len_lo=5, len_hi=900),
+    synth.custom(name="na-mha-decode-contig", seed=4101, B=3, Hq=4, Hkv=4, D=64, dtype="bf16",
+                 block_size=0, n_q=1, len_lo=1, len_hi=300),
+]
+
+
+def _case(ref, w):
+    print("no-alloc case", w.name, flush=True)
+    gc = GpuCache(w)
+    gc.prefill(synth.cached_lengths(w))
+    gc.step_rows(0)
+    q = queries_dev(w)
+    scale = 1.0 / math.sqrt(w.D)
+    want = gc.attend(q, w.n_q)  # kvc_verify_attn / kvc_decode_attn with a workspace
+    got = torch.full_like(want, float("nan"))
+    kvc.kvc_verify_attn_noalloc(gc.desc, q, w.n_q, gc.k, gc.v, gc.seq_lens, gc.table, scale, got,
+                                gc.status)
+    assert gc.dev_status() == 0
+    assert torch.equal(got, want), float((got - want).abs().max())
+    oracle = oracle_outputs(ref, w, range(w.B), synth.cached_lengths(w))
+    g = got.cpu().numpy()
+    for b in range(w.B):
+        assert_close(g[b], oracle[b], "%s b=%d" % (w.name, b))
+
+
+def test_noalloc_matches_workspace_call_twice(ref):
+    for w in CASES:
+        _case(ref, w)
+
+
+def test_noalloc_refuses_oversized_batch():
+    w = synth.custom(name="na-big", seed=4102, B=128, Hq=32, Hkv=8, D=128, dtype="bf16",
+                     block_size=16, n_q=16, len_lo=16, len_hi=16)
+    gc = GpuCache(w, block_size=16, capacity=65536, pool_blocks=256)
+    out = torch.empty((w.B, 16, w.Hq, w.D), device="cuda")
+    q = torch.empty((w.B, 16, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_verify_attn_noalloc(gc.desc, q, 16, gc.k, gc.v, gc.seq_lens, gc.table, 0.1, out,
+                                    gc.status)
+    assert e.value.status == -4
