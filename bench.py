@@ -208,9 +208,7 @@ def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
         buf.fill_(float(i))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        lc.step_front()
-        lc.step_partition()
-        lc.step_reduce()
+        lc.step()
         e1.record()
         torch.cuda.synchronize()
         step_us.append(e0.elapsed_time(e1) * 1e3)

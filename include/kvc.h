@@ -96,7 +96,8 @@ typedef struct {
                                  max_blocks_per_seq * block_size tokens                 */
   int32_t num_blocks;         /* paged: pool size N                                     */
   int32_t partition_tokens;   /* split-KV partition length in tokens: 0 = library
-                                 default, else a multiple of 16                         */
+                                 default (stream-K for grouped rows), else a multiple
+                                 of 16                                                  */
 } kvc_cache_desc;
 
 /*
@@ -157,6 +158,57 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
                const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new, int32_t max_new,
                const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t* seq_lens_out,
                int32_t* dev_status, void* stream);
+
+/*
+ * kvc_block_table_append -- kvc_block_table followed by kvc_append, in one
+ * launch (paged caches only).
+ *
+ * The same operations as the two calls ([I1] "PagedAttention", [VN] 05
+ * "Block table": blocks on demand from the free pool; [EI] KV-cache passage:
+ * rows written in place at the current length), with one launch instead of
+ * two: a decode step's bookkeeping costs launches, not bytes ([I2] "CUDA
+ * graphs": per-kernel launch overhead dominates small steps).  Arguments as the
+ * two calls take them (block_table, free_list, free_head_in, free_head_out
+ * and slot_mapping of kvc_block_table; k_new, v_new, max_new, k_cache,
+ * v_cache and seq_lens_out of kvc_append).  On success the table, the head,
+ * the slots, the cache bytes and the lengths are exactly those of the two
+ * calls in order.  An allocation error (a negative length or count:
+ * KVC_ERR_DATA; a sequence beyond max_blocks_per_seq: KVC_ERR_CAPACITY; too
+ * few free blocks: KVC_ERR_NO_BLOCKS) writes nothing but free_head_out =
+ * free_head_in, seq_lens_out = seq_lens and the status; a token whose slot
+ * lies outside the pool is not written (KVC_ERR_DATA), as in kvc_append.
+ * Every workgroup reads the whole batch's lengths, so B is limited to 8192
+ * (KVC_ERR_UNSUPPORTED beyond: use the two calls).
+ */
+int kvc_block_table_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                           const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                           int32_t max_new, int32_t* block_table, const int32_t* free_list,
+                           const int32_t* free_head_in, int32_t* free_head_out,
+                           int32_t* slot_mapping, void* k_cache, void* v_cache,
+                           int32_t* seq_lens_out, int32_t* dev_status, void* stream);
+
+/*
+ * kvc_append_attn -- kvc_append followed by kvc_verify_attn (n_q = 1:
+ * kvc_decode_attn) over the new lengths, for a contiguous cache.
+ *
+ * [EI] names "KV cache write + attention" among the fused kernels serving
+ * systems ship.  With one query row per KV row (MHA, and every fp32 cache)
+ * the append happens inside the attention's partition launch: the tiles that
+ * reach a sequence's new rows read them from k_new / v_new, and the work item
+ * of the last query row of each KV head writes them into the cache (a decode
+ * step is then two launches instead of three).  Grouped rows and FP8 caches
+ * run the append kernel first.  Arguments as kvc_append (contiguous: no slot
+ * mapping) and kvc_verify_attn (its seq_lens are seq_lens_out, the lengths
+ * after the append; the workspace is sized by kvc_attn_workspace_bytes).
+ * Outputs, cache bytes and seq_lens_out are those of the two calls in order.
+ * A sequence the append refuses (it would pass max_seq_len:
+ * KVC_ERR_CAPACITY) keeps its length; its attention output is unspecified.
+ */
+int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                    const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                    int32_t max_new, void* k_cache, void* v_cache, int32_t* seq_lens_out,
+                    const void* q, int32_t n_q, float scale, void* out, int32_t out_dtype,
+                    void* workspace, size_t workspace_bytes, int32_t* dev_status, void* stream);
 
 /*
  * kvc_decode_attn -- one new query row per sequence attends over all of its
@@ -235,16 +287,21 @@ int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_len
                     const void* workspace, size_t workspace_bytes, void* out, int32_t out_dtype,
                     int32_t* dev_status, void* stream);
 
-/* Workspace bytes the attention calls need for this desc and n_q (0 on a bad desc). */
+/* Workspace bytes the attention calls need for this desc and n_q (0 on a bad
+ * desc).  With the stream-K split (below) it depends on the current
+ * device's compute-unit count, not on the capacity. */
 size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
 
 /* Partition length in tokens the attention calls use for this desc and n_q
- * (negative kvc_status on a bad desc).  With the library default and an FP8
- * cache on the grouped-query / verify path, near one round of resident
- * wavefronts, this is an upper bound: each launch then picks a length between
- * half of it and it from the actual sequence lengths (the workspace is sized
- * for the shorter bound).  An explicit desc.partition_tokens is always used
- * as given. */
+ * (negative kvc_status on a bad desc).  0: the call has no fixed length --
+ * with desc.partition_tokens = 0, rows that share a KV head (G * n_q >= 2,
+ * bf16 and FP8 caches) use the stream-K split ([I1] "FlashDecoding": any
+ * split of the keys combines exactly): the batch's 16-key tiles, taken
+ * sequence by sequence and KV head by KV head, are shared out evenly over a
+ * fixed set of workers (one per SIMD of the device for bf16 caches, one
+ * round of resident wavefronts for FP8), so every worker streams the same
+ * number of tiles whatever the lengths.  An explicit desc.partition_tokens
+ * is always used as given (fixed partitions). */
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
 
 /*

@@ -8,7 +8,10 @@
 // out = sum_p w_p O_p / sum_p w_p l_p, then one rounding to the output type.
 //
 // One wavefront per output row (sequence, query head, query row); each lane
-// owns D/64 consecutive columns and, for the statistics, one partition.
+// owns D/64 consecutive columns and, for the statistics, one partition.  The
+// partials are either a row's fixed partitions or, for the matrix-core
+// kernel's stream-K split, the pieces of the workers that covered the row's
+// segment.
 #include "launch.hpp"
 
 namespace kvc {
@@ -24,42 +27,77 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   const int b = (int)(bh / p.Hq);
   const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + lane * CPL;
 
-  // With few partition slots, one round trip: the length, the first kEarly
-  // partitions' outputs for this lane's columns and one partition's (m, l)
-  // per lane are all requested together, for every slot the workspace has
-  // (slots beyond the sequence's partitions hold stale bytes and are
-  // discarded by selection, never multiplied, once the length is known).
-  // With more slots than that, fetching every slot's outputs would move
-  // several times the bytes the sequence has, so the outputs wait for the
-  // length (a second round trip) and only its partitions are read.
+  // Where this row's partials are: partial j's statistics at ml[j * ml_step]
+  // and its outputs at po[j * o_step] (this lane's columns).  Fixed
+  // partitions: the row's max_parts slots, in order.  Stream-K: the pieces
+  // (segment + worker) of the workers sk_meta names for the row's segment.
   constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
-  const bool speculate = p.max_parts <= (kEarly > 8 ? 8 : kEarly);
-  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
-  const float* po = p.ws_o + row * p.max_parts * D + lane * CPL;
+  const float2* ml;
+  const float* po;
+  long ml_step, o_step;
   float early[kEarly][CPL];
-  if (speculate) {
-#pragma unroll
-    for (int j = 0; j < kEarly; ++j)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) early[j][c] = j < p.max_parts ? po[(long)j * D + c] : 0.f;
-  }
   float2 mine_raw = make_float2(-INFINITY, 0.f);
-  if (lane < p.max_parts) mine_raw = ml[lane];
-  const int L = p.seq_lens[b];
-  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
-  if (!speculate) {
-    const int n = L >= p.n_q && L <= p.cap ? (L + P - 1) / P : 0;
+  int code;
+  const int L = attended_len(p.seq_lens, p.cu_new, p.total_new, b, p.n_q, p.cap, &code);
+  const bool valid = L >= 0;
+  int n = 0;  // partials of the row
+  if (p.sk_meta == nullptr) {
+    ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
+    po = p.ws_o + row * p.max_parts * D + lane * CPL;
+    ml_step = 1;
+    o_step = D;
+    // With few partition slots, one round trip: the length, the first kEarly
+    // partitions' outputs for this lane's columns and one partition's (m, l)
+    // per lane are all requested together, for every slot the workspace has
+    // (slots beyond the sequence's partitions hold stale bytes and are
+    // discarded by selection, never multiplied, once the length is known).
+    // With more slots than that, fetching every slot's outputs would move
+    // several times the bytes the sequence has, so the outputs wait for the
+    // length (a second round trip) and only its partitions are read.
+    const bool speculate = p.max_parts <= (kEarly > 8 ? 8 : kEarly);
+    if (speculate) {
+#pragma unroll
+      for (int j = 0; j < kEarly; ++j)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) early[j][c] = j < p.max_parts ? po[(long)j * D + c] : 0.f;
+    }
+    if (lane < p.max_parts) mine_raw = ml[lane];
+    const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+    n = valid ? (L + P - 1) / P : 0;
+    if (!speculate) {
+#pragma unroll
+      for (int j = 0; j < kEarly; ++j)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) early[j][c] = j < n ? po[(long)j * D + c] : 0.f;
+    }
+  } else {
+    const int g = h / p.G;
+    const int i = r * p.G + h % p.G;  // row of the KV head's rows
+    const int n_rb = (p.G * p.n_q + p.rows_item - 1) / p.rows_item;
+    const long seg = ((long)b * p.Hkv + g) * n_rb + i / p.rows_item;
+    int2 wr = make_int2(0, -1);
+    if (valid) wr = p.sk_meta[seg];
+    // a record that names workers outside the launch (a workspace the
+    // partition kernel did not fill) is not followed
+    if (wr.x < 0 || wr.y < wr.x || wr.y >= p.sk_workers) wr = make_int2(0, -1);
+    n = valid ? wr.y - wr.x + 1 : 0;
+    const long first = (seg + wr.x) * p.sk_rows + i % p.rows_item;  // workspace row of piece 0
+    ml = reinterpret_cast<const float2*>(p.ws_ml) + first;
+    po = p.ws_o + first * D + lane * CPL;
+    ml_step = p.sk_rows;
+    o_step = (long)p.sk_rows * D;
+    if (lane < n) mine_raw = ml[lane * ml_step];
 #pragma unroll
     for (int j = 0; j < kEarly; ++j)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) early[j][c] = j < n ? po[(long)j * D + c] : 0.f;
+      for (int c = 0; c < CPL; ++c) early[j][c] = j < n ? po[j * o_step + c] : 0.f;
   }
   float acc[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
   float den = 0.f;
-  if (L >= p.n_q && L <= p.cap) {
-    const int nparts = (L + P - 1) / P;
+  if (valid) {
+    const int nparts = n;
 #pragma unroll
     for (int j = 0; j < kEarly; ++j)
 #pragma unroll
@@ -67,11 +105,11 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     const float2 mine = lane < nparts ? mine_raw : make_float2(-INFINITY, 0.f);
     float mstar = mine.x;
     for (int q0 = kWave; q0 < nparts; q0 += kWave)  // more than 64 partitions
-      if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[q0 + lane].x);
+      if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[(q0 + lane) * ml_step].x);
     for (int m = 1; m < kWave; m <<= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, m));
     for (int q0 = 0; q0 < nparts; q0 += kWave) {
       float2 mq = q0 == 0 ? mine : make_float2(-INFINITY, 0.f);
-      if (q0 > 0 && q0 + lane < nparts) mq = ml[q0 + lane];
+      if (q0 > 0 && q0 + lane < nparts) mq = ml[(q0 + lane) * ml_step];
       const float wq = mq.x == -INFINITY ? 0.f : fast_exp2(mq.x - mstar);  // empty: 0
       den += wq * mq.y;
       const int cnt = min(kWave, nparts - q0);
@@ -90,7 +128,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) o[u][c] = po[(long)(q0 + j + u) * D + c];
+          for (int c = 0; c < CPL; ++c) o[u][c] = po[(q0 + j + u) * o_step + c];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const float wj = __shfl(wq, j + u);
@@ -101,13 +139,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
       for (; j < cnt; ++j) {
         const float wj = __shfl(wq, j);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += wj * po[(long)(q0 + j) * D + c];
+        for (int c = 0; c < CPL; ++c) acc[c] += wj * po[(q0 + j) * o_step + c];
       }
     }
     for (int m = 1; m < kWave; m <<= 1) den += __shfl_xor(den, m);
-  } else if (lane == 0 && h == 0 && r == 0) {
-    report(p.status, KVC_ERR_DATA);
   }
+  if (!valid && lane == 0 && h == 0 && r == 0) report(p.status, code);
+  if (valid && n == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
   const float inv = den > 0.f ? 1.f / den : 0.f;  // invalid data: zeros
   if constexpr (BF16_OUT) {
     uint16_t* out = (uint16_t*)p.out + ooff;

@@ -146,7 +146,10 @@ struct Elem<Fp8<F>> {  // FP8 codes: a 16-byte load holds 16 elements; q is 16 b
   }
 };
 
-template <typename T, int D>
+// AP: an append fused into the launch (contiguous caches, not FP8): the new
+// rows of a sequence come from k_new / v_new and are written into the cache
+// (AttnParams::cu_new).
+template <typename T, int D, bool AP>
 __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
@@ -157,11 +160,21 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
   if (!wi.live) return;
   const int b = wi.b, part = wi.part, r = wi.u % p.n_q, h = wi.u / p.n_q;
 
-  const int L = p.seq_lens[b];
-  if (L < p.n_q || L > p.cap) {
-    if (part == 0 && h == 0 && r == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
+  int code;
+  const int L = attended_len(p.seq_lens, p.cu_new, p.total_new, b, p.n_q, p.cap, &code);
+  const bool writer = AP && part == 0 && h == 0 && r == p.n_q - 1 && lane == 0;
+  if (L < 0) {
+    if (part == 0 && h == 0 && r == 0 && lane == 0) report(p.status, code);
+    if (writer) p.seq_lens_out[b] = p.seq_lens[b];  // a refused append keeps the length
     return;
   }
+  if (writer) p.seq_lens_out[b] = L;
+  // fused append: keys len0 .. L-1 are the new rows, read from k_new / v_new
+  // (row c0 + key - len0) and written into the cache by the work item of the
+  // last query row of the KV head's first query head, which sees them all
+  const int len0 = AP ? p.seq_lens[b] : L;
+  const int c0 = AP ? p.cu_new[b] : 0;
+  const bool app_writer = AP && r == p.n_q - 1 && h % p.G == 0;
   const int nparts = (L + p.P - 1) / p.P;
   if (part >= nparts) return;
   const int start = part * kTile;              // first tile of this partition
@@ -243,13 +256,32 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
             vsc[i][u] = __builtin_nontemporal_load(
                 reinterpret_cast<const float*>((const uint8_t*)p.v + so));
           } else {
-            const long off = (row0 + tt) * D + c * VE;
-            kr[i][u] = load_stream(kbase + off);
-            vr[i][u] = load_stream(vbase + off);
+            const T* ks = kbase + (row0 + tt) * D + c * VE;
+            const T* vs = vbase + (row0 + tt) * D + c * VE;
+            if (AP && ti + kTile > len0 && ti + tt >= len0) {  // a new row: from k_new / v_new
+              const long nr = ((long)(c0 + ti + tt - len0) * p.Hkv + g) * D + c * VE;
+              ks = (const T*)p.k_new + nr;
+              vs = (const T*)p.v_new + nr;
+            }
+            kr[i][u] = load_stream(ks);
+            vr[i][u] = load_stream(vs);
           }
         }
       }
       idx += TPI;
+      if constexpr (AP && !kF8) {
+        if (app_writer && tile + kTile > len0 && nvalid[0] > 0) {  // store this tile's new rows
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int tt = u * RPL + r0;
+            if (tt < nvalid[0] && tile + tt >= len0) {
+              const long off = (((long)b * p.Hkv + g) * p.S_max + tile + tt) * D + c * VE;
+              *reinterpret_cast<uint4*>((T*)p.k_out + off) = kr[0][u];
+              *reinterpret_cast<uint4*>((T*)p.v_out + off) = vr[0][u];
+            }
+          }
+        }
+      }
       float s[TPI][U];
       float mx = -INFINITY;
 #pragma unroll
@@ -305,18 +337,30 @@ hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) 
   if (n_wg == 0) return hipSuccess;
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_wg), block(64);
+  if (p.cu_new) {  // fused append: bf16 and fp32 contiguous caches
+    if (dtype == KVC_BF16) {
+      if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((partition_valu<uint16_t, 64, true>), grid, block, 0, s, p);
+    } else if (dtype == KVC_F32) {
+      if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((partition_valu<float, 64, true>), grid, block, 0, s, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (dtype == KVC_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<uint16_t, 64>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<uint16_t, 64, false>), grid, block, 0, s, p);
   } else if (dtype == KVC_FP8_E4M3) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 64>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 128, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 64, false>), grid, block, 0, s, p);
   } else if (dtype == KVC_FP8_E5M2) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 64>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 128, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 64, false>), grid, block, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<float, 64>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<float, 64, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

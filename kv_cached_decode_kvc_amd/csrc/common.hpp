@@ -34,7 +34,48 @@ struct AttnParams {
   int P_lo;              //   between P_lo and P
   int cap;               // tokens a sequence may hold
   float scale_log2;      // scale * log2(e): scores go straight into exp2
+  // Stream-K split (matrix-core kernel; sk_meta == NULL: fixed partitions).
+  // Segment s = (b * Hkv + g) * n_rb + rb; piece (s, worker w) keeps its rows'
+  // partials at workspace rows (s + w) * sk_rows + i, and sk_meta[s] = (first,
+  // last) worker of segment s, written by the first.
+  int2* sk_meta;
+  int sk_workers;        // workers launched (one workgroup each)
+  int sk_rows;           // rows a piece holds: min(16 * NT, G * n_q)
+  int sk_min_tiles;      // fewest tiles a worker takes (fewer workers for small batches)
+  // Append fused into the partition launch (contiguous cache, vector-ALU
+  // kernel; cu_new == NULL: none).  seq_lens then holds the lengths before
+  // the append; sequence b's new rows are rows cu_new[b] .. cu_new[b+1] of
+  // k_new / v_new, read from there by the tiles that reach them and written
+  // into the cache by one work item per KV head, which also writes
+  // seq_lens_out.
+  const int32_t* cu_new;
+  const void* k_new;
+  const void* v_new;
+  void* k_out;           // the cache buffers (the same memory as k, v)
+  void* v_out;
+  int32_t* seq_lens_out;
+  int total_new;
 };
+
+// Attended length of sequence b and whether it is usable: seq_lens[b], or,
+// with an append fused in, seq_lens[b] plus its new rows.  *code receives the
+// status an unusable sequence reports (a capacity overflow of the append, or
+// bad data).
+__device__ __forceinline__ int attended_len(const int32_t* seq_lens, const int32_t* cu_new,
+                                            int total_new, int b, int n_q, int cap, int* code) {
+  int L = seq_lens[b];
+  *code = KVC_ERR_DATA;
+  if (cu_new) {
+    const int c0 = cu_new[b], n = cu_new[b + 1] - c0;
+    if (L < 0 || n < 0 || c0 < 0 || c0 + n > total_new) return -1;
+    if ((long)L + n > cap) {
+      *code = KVC_ERR_CAPACITY;
+      return -1;
+    }
+    L += n;
+  }
+  return (L >= n_q && L <= cap) ? L : -1;
+}
 
 struct PrefillParams {
   const void* q;            // [total_q][Hq][D] bf16, sequence b's rows at cu_q[b] ..
@@ -57,6 +98,10 @@ struct ReduceParams {
   int32_t* status;
   int B, n_q, Hq, D, P, max_parts, cap;
   int slots_u, P_lo;  // as in AttnParams
+  const int2* sk_meta;  // stream-K partials (as in AttnParams); NULL: fixed partitions
+  int sk_rows, sk_workers, G, Hkv, rows_item;
+  const int32_t* cu_new;  // append fused into the partition launch (as in AttnParams)
+  int total_new;
 };
 
 // Partition length of a launch, in tokens.  With slots_u = 0 it is the

@@ -60,16 +60,24 @@ size_t cache_rows(const kvc_cache_desc* d) {
 
 struct Plan {
   bool mfma;          // grouped rows on the matrix cores
+  bool sk;            // mfma: the stream-K split (no fixed partition length)
   int rows_per_item;  // mfma: 16 or 32 rows per wavefront
-  int P;              // partition length in tokens (an upper bound when slots_u > 0)
+  int P;              // partition length in tokens (an upper bound when slots_u > 0; 0: stream-K)
   int P_lo;           // slots_u > 0: the shortest partition a launch may choose
   int slots_u;        // > 0: resident wavefront slots per unit of a sequence
   int max_parts;      // partitions of a full-capacity sequence
   int units;          // work units of a sequence per partition (rows, or row blocks per KV head)
+  int sk_workers;     // stream-K: workers launched (one round of resident wavefronts)
+  int sk_rows;        // stream-K: rows one piece holds
   long grid;          // workgroups of the partition launch
   size_t ml_offset;   // byte offset of the (m, l) array inside the workspace
+  size_t meta_offset; // stream-K: byte offset of the per-segment worker records
   size_t bytes;       // workspace size
 };
+
+constexpr int kSkMinTiles = 8;  // stream-K: fewest 16-key tiles a worker streams
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Work is one wavefront per (rows, partition).  A wavefront pays a few
 // dependent memory latencies (length, block ids, first tile) before it
@@ -84,8 +92,15 @@ struct Plan {
 // per key.  It is halved (down to 64) while a full-capacity batch would give
 // fewer than 1024 wavefronts, and doubled (up to 8192) while it would give
 // more than 65536.
-// SIMDs of the current device (4 per compute unit), for the launch-time
-// partition length; 1024 on MI355X.
+//
+// The matrix-core path (grouped rows) uses no partition length by default:
+// the stream-K split shares the batch's tiles out evenly over a fixed number
+// of workers (one per SIMD for bf16 caches; for FP8 caches one round of
+// resident wavefronts, 2 per SIMD with 32-row blocks, 3 with 16-row blocks),
+// each taking at least kSkMinTiles tiles.  Its workspace holds one partial
+// per row of every piece: at most segments + workers pieces (a piece starts
+// at a segment start or a worker start), sk_rows rows each.
+// SIMDs of the current device (4 per compute unit); 1024 on MI355X.
 int resident_simds() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -105,6 +120,23 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
                      : d->num_q_heads * n_q;
   const long units = (long)d->batch * pl.units;
   const int cap = capacity(d);
+  const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
+  if (pl.mfma && d->partition_tokens == 0) {
+    pl.sk = true;
+    // bf16 tiles: one worker per SIMD; FP8 tiles carry half the bytes, so a
+    // full round of resident wavefronts keeps enough of them in flight
+    // (measured on the full-size GQA and verify workloads: bf16 GQA 372 us
+    // at 1024 workers against 380 at 3072, FP8 GQA 208 us at 3072 against
+    // 345 at 1024)
+    pl.sk_workers = resident_simds() * (!fp8_format(d) ? 1 : pl.rows_per_item == 32 ? 2 : 3);
+    pl.sk_rows = std::min(pl.rows_per_item, R);
+    pl.grid = pl.sk_workers;
+    const size_t pieces = (size_t)units + pl.sk_workers;
+    pl.ml_offset = align256(pieces * pl.sk_rows * d->head_dim * sizeof(float));
+    pl.meta_offset = align256(pl.ml_offset + pieces * pl.sk_rows * 2 * sizeof(float));
+    pl.bytes = pl.meta_offset + (size_t)units * 2 * sizeof(int32_t);
+    return pl;
+  }
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {
@@ -119,27 +151,10 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
     while (pl.P < 8192 && units * ((cap + pl.P - 1) / pl.P) > 65536) pl.P <<= 1;
   }
   pl.P_lo = pl.P;
-  if (pl.mfma && fp8_format(d) && d->partition_tokens == 0 && pl.P >= 2 * kTile) {
-    // FP8 wavefronts move half the bytes per tile, so they need about twice
-    // as many in flight as bf16 ones to keep HBM busy.  Near one round of
-    // resident wavefronts at full capacity, the matrix-core kernels then
-    // choose the length per launch from the actual lengths (part_tokens),
-    // between half the planned length and the planned length, so that the
-    // batch fills the resident slots.  Well beyond one round the dispatcher
-    // balances the rounds and the planned length stays; bf16 verify measured
-    // no better with the launch-time length (its wavefronts already hold
-    // about the bytes in flight that HBM needs).
-    const long slots = (long)resident_simds() * (pl.rows_per_item == 32 ? 2 : 3);
-    if (units * ((cap + pl.P - 1) / pl.P) <= 2 * slots) {
-      pl.P_lo = pl.P / 2;
-      pl.slots_u = (int)std::min(slots / pl.units, 1L << 30);
-    }
-  }
   pl.max_parts = (cap + pl.P_lo - 1) / pl.P_lo;
   pl.grid = xcd_grid(d->batch, pl.units, pl.max_parts);
-  const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * d->head_dim * sizeof(float);
-  pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
+  pl.ml_offset = align256(o_bytes);
   pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
   return pl;
 }
@@ -270,6 +285,12 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
   p.cap = capacity(d);
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   if (fp8_format(d) && d->block_size == 0) p.S_max = (int)fp8_padded_rows(d->max_seq_len);
+  if (pl.sk) {
+    p.sk_meta = (int2*)((char*)ws + pl.meta_offset);
+    p.sk_workers = pl.sk_workers;
+    p.sk_rows = pl.sk_rows;
+    p.sk_min_tiles = kSkMinTiles;
+  }
   return p;
 }
 
@@ -291,6 +312,14 @@ ReduceParams reduce_params(const kvc_cache_desc* d, const Plan& pl, int n_q, int
   p.slots_u = pl.slots_u;
   p.max_parts = pl.max_parts;
   p.cap = capacity(d);
+  if (pl.sk) {
+    p.sk_meta = (const int2*)((const char*)ws + pl.meta_offset);
+    p.sk_rows = pl.sk_rows;
+    p.sk_workers = pl.sk_workers;
+    p.G = d->num_q_heads / d->num_kv_heads;
+    p.Hkv = d->num_kv_heads;
+    p.rows_item = pl.rows_per_item;
+  }
   return p;
 }
 
@@ -409,6 +438,109 @@ int kvc_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
   a.total_new = total_new;
   if (d->block_size > 0 && total_new == 0) a.slots = nullptr, a.S_max = 0x7fffffff;
   return hip_status(launch_append(a, (hipStream_t)stream));
+}
+
+int kvc_block_table_append(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                           const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                           int32_t max_new, int32_t* block_table, const int32_t* free_list,
+                           const int32_t* free_head_in, int32_t* free_head_out,
+                           int32_t* slot_mapping, void* k_cache, void* v_cache,
+                           int32_t* seq_lens_out, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;  // contiguous caches: kvc_append
+  if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
+  if (d->batch > kMaxFusedBatch) return KVC_ERR_UNSUPPORTED;
+  if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !block_table || !free_list || !free_head_in || !free_head_out ||
+      !k_cache || !seq_lens_out)
+    return KVC_ERR_ARG;
+  if (!v_cache && v_new) return KVC_ERR_ARG;
+  if (!v_cache && fp8_format(d)) return KVC_ERR_UNSUPPORTED;
+  if (seq_lens_out == seq_lens) return KVC_ERR_ARG;
+  if (total_new > 0 && (!k_new || (v_cache && !v_new) || !slot_mapping)) return KVC_ERR_ARG;
+  BlockTableArgs bt{};
+  bt.seq_lens = seq_lens;
+  bt.cu_new = cu_new;
+  bt.table = block_table;
+  bt.free_list = free_list;
+  bt.head_in = free_head_in;
+  bt.head_out = free_head_out;
+  bt.slots = slot_mapping;
+  bt.status = dev_status;
+  bt.B = d->batch;
+  bt.bs = d->block_size;
+  bt.max_blocks = d->max_blocks_per_seq;
+  bt.N = d->num_blocks;
+  bt.total_new = total_new;
+  AppendArgs a{};
+  a.k_new = (const uint8_t*)k_new;
+  a.v_new = (const uint8_t*)v_new;
+  a.seq_lens = seq_lens;
+  a.cu_new = cu_new;
+  a.slots = slot_mapping;
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.seq_lens_out = seq_lens_out;
+  a.status = dev_status;
+  a.B = d->batch;
+  a.Hkv = d->num_kv_heads;
+  a.head_bytes = (int)(d->head_dim * input_bytes(d));
+  a.fp8 = fp8_format(d);
+  a.D = d->head_dim;
+  a.bs = d->block_size;
+  a.N = d->num_blocks;
+  a.max_new = max_new;
+  a.total_new = total_new;
+  return hip_status(launch_block_table_append(bt, a, (hipStream_t)stream));
+}
+
+int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                    const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                    int32_t max_new, void* k_cache, void* v_cache, int32_t* seq_lens_out,
+                    const void* q, int32_t n_q, float scale, void* out, int32_t out_dtype,
+                    void* workspace, size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size != 0) return KVC_ERR_ARG;  // paged caches: kvc_block_table_append
+  if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  Plan pl{};
+  // the attention's checks, on the lengths after the append
+  st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens_out, nullptr, scale, workspace,
+                  workspace_bytes, &pl);
+  if (st != KVC_OK) return st;
+  if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !out || seq_lens_out == seq_lens) return KVC_ERR_ARG;
+  if (total_new > 0 && (!k_new || !v_new)) return KVC_ERR_ARG;
+  if (!pl.mfma && !fp8_format(d)) {
+    // one partition launch appends and attends; the reduce takes the same
+    // lengths (before the append, plus the new rows)
+    AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, nullptr, scale,
+                               workspace, dev_status);
+    p.cu_new = cu_new;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_out = k_cache;
+    p.v_out = v_cache;
+    p.seq_lens_out = seq_lens_out;
+    p.total_new = total_new;
+    st = hip_status(launch_partition_valu(p, d->dtype, (hipStream_t)stream));
+    if (st != KVC_OK) return st;
+    ReduceParams r = reduce_params(d, pl, n_q, d->head_dim, seq_lens, workspace, out, dev_status);
+    r.cu_new = cu_new;
+    r.total_new = total_new;
+    return hip_status(launch_reduce(r, out_dtype, (hipStream_t)stream));
+  }
+  // grouped rows or FP8: the append kernel, then attention over its lengths
+  st = kvc_append(d, k_new, v_new, seq_lens, cu_new, total_new, max_new, nullptr, k_cache, v_cache,
+                  seq_lens_out, dev_status, stream);
+  if (st != KVC_OK) return st;
+  st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens_out, nullptr, scale, workspace,
+                     dev_status, stream);
+  if (st != KVC_OK) return st;
+  return run_reduce(d, pl, n_q, d->head_dim, seq_lens_out, workspace, out, out_dtype, dev_status,
+                    stream);
 }
 
 int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,

@@ -37,7 +37,8 @@ struct AppendArgs {
 };
 
 constexpr int kMaxBatch = 65536;        // sequences per call (one grid row each)
-constexpr int kMaxPoolBlocks = 262144;  // pool size the lifecycle kernels can track in LDS
+constexpr int kMaxPoolBlocks = 262144;
+constexpr int kMaxFusedBatch = 8192;  // kvc_block_table_append: every workgroup reads the batch  // pool size the lifecycle kernels can track in LDS
 
 struct LifecycleArgs {
   const int32_t* seq_lens;
@@ -73,6 +74,7 @@ hipError_t launch_cow(const LifecycleArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, hipStream_t s);
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_block_table_append(const BlockTableArgs& bt, const AppendArgs& a, hipStream_t s);
 // dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)
 constexpr int kMlaKeyDim = 576;    // MLA cache row: latent (512) + decoupled RoPE key (64)
 constexpr int kMlaValueDim = 512;  // the latent part, which also serves as the value

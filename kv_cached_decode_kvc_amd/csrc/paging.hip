@@ -145,6 +145,19 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
 
 constexpr int kAppendThreads = 256;
 
+// One 16-byte piece (number w) of new token src_tok's row of KV head g, K
+// and V, copied bit for bit to byte offset dst of the caches.
+__device__ __forceinline__ void copy_piece(const AppendArgs& a, long src_tok, int g, int w,
+                                           long dst) {
+  const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+  const uint4 kv = *reinterpret_cast<const uint4*>(a.k_new + src);
+  *reinterpret_cast<uint4*>(a.k_cache + dst) = kv;
+  if (a.v_cache) {  // NULL: a key-only cache (MLA latent rows serve as keys and values)
+    const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
+    *reinterpret_cast<uint4*>(a.v_cache + dst) = vv;
+  }
+}
+
 // grid = (vector chunks x token chunks, B): every thread moves one 16-byte
 // piece of one new token's K row and V row (a row of a KV head is head_bytes
 // long), bit for bit.  Decode steps have one token per sequence, so the grid
@@ -191,13 +204,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     } else {
       dst = (((long)b * a.Hkv + g) * a.S_max + len + t) * a.head_bytes + w * 16;
     }
-    const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
-    const uint4 kv = *reinterpret_cast<const uint4*>(a.k_new + src);
-    *reinterpret_cast<uint4*>(a.k_cache + dst) = kv;
-    if (a.v_cache) {  // NULL: a key-only cache (MLA latent rows serve as keys and values)
-      const uint4 vv = *reinterpret_cast<const uint4*>(a.v_new + src);
-      *reinterpret_cast<uint4*>(a.v_cache + dst) = vv;
-    }
+    copy_piece(a, src_tok, g, w, dst);
   }
 }
 
@@ -228,9 +235,34 @@ __device__ __forceinline__ float amax8(const uint4& x) {
   return m;
 }
 
+// Piece w of new token src_tok's bf16 row of KV head g, K and V, quantized
+// into cache row `row`: the row's D/8 lanes (aligned, all active together)
+// reduce its largest magnitude, and the lane of piece 0 stores the scales.
+template <int F>
+__device__ __forceinline__ void quantize_piece(const AppendArgs& a, long src_tok, int g, int w,
+                                               int vec_per_head, long row) {
+  using Fm = Fp8Format<F>;
+  const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+  const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
+  const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
+  float km = amax8(kx), vm = amax8(vx);
+  for (int off = 1; off < vec_per_head; off <<= 1) {
+    km = fmaxf(km, __shfl_xor(km, off));
+    vm = fmaxf(vm, __shfl_xor(vm, off));
+  }
+  const float ks = __fdiv_rn(km, Fm::kMax), vs = __fdiv_rn(vm, Fm::kMax);
+  const long dst = fp8_code_offset(row, a.D) + w * 8;
+  *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8<F>(kx, ks);
+  *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8<F>(vx, vs);
+  if (w == 0) {
+    const long so = fp8_scale_offset(row, a.D);
+    *reinterpret_cast<float*>(a.k_cache + so) = ks;
+    *reinterpret_cast<float*>(a.v_cache + so) = vs;
+  }
+}
+
 template <int F>
 __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a) {
-  using Fm = Fp8Format<F>;
   const int b = blockIdx.y;
   const int vec_per_head = a.head_bytes >> 4;  // lanes per row: D / 8
   const int vec_per_tok = a.Hkv * vec_per_head;
@@ -272,24 +304,147 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
     } else {
       row = ((long)b * a.Hkv + g) * s_row + len + t;
     }
-    const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
-    const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
-    const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
-    float km = amax8(kx), vm = amax8(vx);
-    for (int off = 1; off < vec_per_head; off <<= 1) {
-      km = fmaxf(km, __shfl_xor(km, off));
-      vm = fmaxf(vm, __shfl_xor(vm, off));
+    quantize_piece<F>(a, src_tok, g, w, vec_per_head, row);
+  }
+}
+
+// Block table and append in one launch (paged caches).  Grid = (16-byte
+// chunks of a token's rows x token chunks, B), as for the append.  Every
+// workgroup first reads the whole batch's lengths and counts (one pass, its
+// threads strided over the sequences) to find the blocks each sequence needs,
+// the batch's errors and the free-list index of its own sequence's first new
+// block; then the first workgroup of sequence b writes b's new table entries
+// and length, and every workgroup maps its tokens to slots (an already held
+// block from the table, a new one straight from the free list, so no
+// workgroup waits on another's stores) and copies or quantizes their rows.
+// The results equal those of block_table_kernel followed by the append
+// kernels.  Errors of the allocation (a negative length or count, a sequence
+// beyond its capacity, too few free blocks) are all or nothing, as in the
+// block table: nothing is written but the head, the unchanged lengths and the
+// status.
+template <int F>
+__global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(BlockTableArgs bt,
+                                                                           AppendArgs a) {
+  __shared__ int s_red[kAppendThreads / kWave][3];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int bs = bt.bs;
+  const int head = *bt.head_in;
+  int total = 0, before = 0, bad = 0, over = 0;
+  for (int i = tid; i < bt.B; i += kAppendThreads) {
+    const int len = bt.seq_lens[i];
+    const int n = bt.cu_new[i + 1] - bt.cu_new[i];
+    if (len < 0 || n < 0) {
+      bad = 1;
+      continue;
     }
-    const float ks = __fdiv_rn(km, Fm::kMax), vs = __fdiv_rn(vm, Fm::kMax);
-    const long dst = fp8_code_offset(row, a.D) + w * 8;
-    *reinterpret_cast<uint2*>(a.k_cache + dst) = quantize8<F>(kx, ks);
-    *reinterpret_cast<uint2*>(a.v_cache + dst) = quantize8<F>(vx, vs);
-    if (w == 0) {
-      const long so = fp8_scale_offset(row, a.D);
-      *reinterpret_cast<float*>(a.k_cache + so) = ks;
-      *reinterpret_cast<float*>(a.v_cache + so) = vs;
+    const long have = ((long)len + bs - 1) / bs;
+    const long want = ((long)len + n + bs - 1) / bs;
+    if (want > bt.max_blocks) {
+      over = 1;
+      continue;
+    }
+    total += (int)(want - have);
+    if (i < b) before += (int)(want - have);
+  }
+  for (int m = 1; m < kWave; m <<= 1) {
+    total += __shfl_xor(total, m);
+    before += __shfl_xor(before, m);
+  }
+  bad = __any(bad) ? 1 : 0;
+  over = __any(over) ? 1 : 0;
+  if ((tid & (kWave - 1)) == 0) {
+    s_red[tid / kWave][0] = total;
+    s_red[tid / kWave][1] = before;
+    s_red[tid / kWave][2] = bad | (over << 1);
+  }
+  __syncthreads();
+  total = before = 0;
+  int flags = 0;
+#pragma unroll
+  for (int k = 0; k < kAppendThreads / kWave; ++k) {
+    total += s_red[k][0];
+    before += s_red[k][1];
+    flags |= s_red[k][2];
+  }
+  int err = 0;
+  if (flags & 1) err = KVC_ERR_DATA;
+  else if (flags & 2) err = KVC_ERR_CAPACITY;
+  else if (head < 0 || (long)head + total > bt.N) err = KVC_ERR_NO_BLOCKS;
+  const int len = bt.seq_lens[b];
+  const int c0 = bt.cu_new[b];
+  const int n = bt.cu_new[b + 1] - c0;
+  if (err != 0) {
+    if (blockIdx.x == 0 && tid == 0) {
+      a.seq_lens_out[b] = len;
+      if (b == 0) {
+        report(bt.status, err);
+        *bt.head_out = head;
+      }
+    }
+    return;
+  }
+  const int have = (len + bs - 1) / bs;
+  const int need = (int)(((long)len + n + bs - 1) / bs) - have;
+  const int first = head + before;
+  int32_t* row = bt.table + (long)b * bt.max_blocks;
+  if (blockIdx.x == 0) {
+    for (int j = tid; j < need; j += kAppendThreads) row[have + j] = bt.free_list[first + j];
+    if (tid == 0) {
+      a.seq_lens_out[b] = len + n;
+      if (b == 0) *bt.head_out = head + total;
     }
   }
+  if (n > 0 && c0 + n > bt.total_new) {  // cu_new points past the new-row buffers
+    if (blockIdx.x == 0 && tid == 0) report(bt.status, KVC_ERR_DATA);
+    return;
+  }
+  const int vec_per_head = a.head_bytes >> 4;
+  const int vec_per_tok = a.Hkv * vec_per_head;
+  const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  const int vchunk = blockIdx.x % n_vchunks;
+  const int tchunk = blockIdx.x / n_vchunks;
+  if (blockIdx.x == 0 && tid == 0 && n > (long)(gridDim.x / n_vchunks) * a.tok_per_wg)
+    report(bt.status, KVC_ERR_DATA);  // more new tokens than max_new promised
+  const int idx = vchunk * kAppendThreads + tid;
+  const int g = idx / vec_per_head;
+  const int w = idx - g * vec_per_head;
+  const int t0 = tchunk * a.tok_per_wg;
+  const int t1 = min(t0 + a.tok_per_wg, n);
+  for (int t = t0; t < t1; ++t) {
+    const int pos = len + t;
+    const int lb = pos / bs;
+    const long blk = lb < have ? row[lb] : bt.free_list[first + lb - have];
+    const long slot = blk * bs + pos % bs;
+    if (vchunk == 0 && tid == 0) bt.slots[c0 + t] = (int32_t)slot;
+    if (slot < 0 || slot >= (long)bt.N * bs) {
+      if (idx == 0) report(bt.status, KVC_ERR_DATA);
+      continue;
+    }
+    if (idx >= vec_per_tok) continue;
+    const long prow = ((slot / bs) * a.Hkv + g) * bs + slot % bs;  // cache row of (token, head)
+    if constexpr (F == 0) copy_piece(a, (long)c0 + t, g, w, prow * a.head_bytes + w * 16);
+    else quantize_piece<F>(a, (long)c0 + t, g, w, vec_per_head, prow);
+  }
+}
+
+hipError_t launch_block_table_append(const BlockTableArgs& bt, const AppendArgs& a,
+                                     hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const int vec_per_tok = a.Hkv * (a.head_bytes >> 4);
+  const long n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  AppendArgs b = a;
+  b.tok_per_wg = a.max_new <= 64 ? 1 : 4;
+  const long n_tchunks = a.max_new > 0 ? (a.max_new + b.tok_per_wg - 1) / b.tok_per_wg : 1;
+  if (n_vchunks * n_tchunks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(n_vchunks * n_tchunks), a.B), block(kAppendThreads);
+  if (a.fp8 == kFp8E4M3)
+    hipLaunchKernelGGL(block_table_append_kernel<kFp8E4M3>, grid, block, 0, s, bt, b);
+  else if (a.fp8 == kFp8E5M2)
+    hipLaunchKernelGGL(block_table_append_kernel<kFp8E5M2>, grid, block, 0, s, bt, b);
+  else
+    hipLaunchKernelGGL(block_table_append_kernel<0>, grid, block, 0, s, bt, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_table(const BlockTableArgs& a, hipStream_t s) {

@@ -2,8 +2,9 @@
 
 ``LayerCache`` owns the device buffers of a workload (cache or block pool,
 block table, free list, lengths, workspace) and runs the decode step the way a
-serving loop would: ``kvc_block_table`` (paged caches) -> ``kvc_append`` ->
-``kvc_attn_partition`` -> ``kvc_attn_reduce``.  Every step of the computation
+serving loop would: ``kvc_block_table_append`` (paged caches) ->
+``kvc_attn_partition`` -> ``kvc_attn_reduce``, or, for a contiguous cache,
+``kvc_append_attn`` (append and attention in one call).  Every step of the computation
 runs in the library's kernels; this module only allocates tensors with torch
 and passes their addresses.
 
@@ -196,13 +197,16 @@ class LayerCache:
             self.s_slots = None
 
     def step_front(self):
-        """Block table (paged) and append of the prepared step."""
+        """Block table (paged) and append of the prepared step: one launch
+        (kvc_block_table_append) for a paged cache."""
         if self.bs:
-            kvc.kvc_block_table(self.desc, self.s_len0, self.s_cu, self.s_total, self.table,
-                                self.free_list, self.s_head0, self.s_head1, self.s_slots,
-                                self.status)
-        kvc.kvc_append(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu, self.s_total,
-                       self.w.n_q, self.s_slots, self.k, self.v, self.s_len1, self.status)
+            kvc.kvc_block_table_append(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu,
+                                       self.s_total, self.w.n_q, self.table, self.free_list,
+                                       self.s_head0, self.s_head1, self.s_slots, self.k, self.v,
+                                       self.s_len1, self.status)
+        else:
+            kvc.kvc_append(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu, self.s_total,
+                           self.w.n_q, None, self.k, self.v, self.s_len1, self.status)
 
     def partition(self, q, n_q, lens, ws):
         if self.w.dv:
@@ -233,7 +237,19 @@ class LayerCache:
         if not self.w.prefill:
             self.reduce(self.w.n_q, self.s_len1, self.s_ws, self.s_out)
 
+    @property
+    def fused_step(self) -> bool:
+        """Contiguous decode / verify: the append runs inside the attention call
+        (kvc_append_attn)."""
+        return self.bs == 0 and not self.w.dv and not self.w.prefill
+
     def step(self):
+        if self.fused_step:
+            w = self.w
+            kvc.kvc_append_attn(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu,
+                                self.s_total, w.n_q, self.k, self.v, self.s_len1, self.s_q, w.n_q,
+                                self.scale, self.s_out, self.s_ws, self.status)
+            return self.s_out
         self.step_front()
         self.step_partition()
         self.step_reduce()
@@ -268,14 +284,19 @@ class DecodeLoop:
     def run(self):
         lc, w = self.lc, self.w
         for s in range(self.S):
-            slots = None
             if lc.bs:
-                slots = self.slots[s]
-                kvc.kvc_block_table(lc.desc, self.lens[s], self.cu, self.total, lc.table,
-                                    lc.free_list, self.heads[s], self.heads[s + 1], slots,
-                                    lc.status)
-            kvc.kvc_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total, w.n_q,
-                           slots, lc.k, lc.v, self.lens[s + 1], lc.status)
+                kvc.kvc_block_table_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu,
+                                           self.total, w.n_q, lc.table, lc.free_list,
+                                           self.heads[s], self.heads[s + 1], self.slots[s], lc.k,
+                                           lc.v, self.lens[s + 1], lc.status)
+            elif lc.fused_step:
+                kvc.kvc_append_attn(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu,
+                                    self.total, w.n_q, lc.k, lc.v, self.lens[s + 1], self.q[s],
+                                    w.n_q, lc.scale, self.out[s], self.ws, lc.status)
+                continue
+            else:
+                kvc.kvc_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total,
+                               w.n_q, None, lc.k, lc.v, self.lens[s + 1], lc.status)
             lc.partition(self.q[s], w.n_q, self.lens[s + 1], self.ws)
             lc.reduce(w.n_q, self.lens[s + 1], self.ws, self.out[s])
         return self.out

@@ -111,8 +111,9 @@ def test_workspace_and_partition_sizes(lib):
     assert kvc.kvc_attn_partition_tokens(desc(partition_tokens=48), 1) == 48
     assert kvc.kvc_attn_workspace_bytes(desc(head_dim=80), 1) == 0
     assert kvc.kvc_attn_partition_tokens(desc(head_dim=80), 1) == -3
-    # paged: the power of two nearest an eighth of the capacity (4000, 8176, 4112 tokens)
-    for name, want in (("C2", 1024), ("C3", 512), ("C4", 1024), ("C5", 512)):
+    # paged: the power of two nearest an eighth of the capacity (4000 tokens);
+    # grouped rows (GQA decode, verify) use the stream-K split: no length (0)
+    for name, want in (("C2", 1024), ("C3", 512), ("C4", 0), ("C5", 0)):
         w = synth.get(name)
         dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
                   block_size=w.block_size, max_seq_len=synth.capacity_tokens(w),
@@ -128,23 +129,45 @@ def _ws_bytes(rows, parts, d):
     return ((o + 255) // 256) * 256 + rows * parts * 2 * 4
 
 
-def test_fp8_verify_workspace_covers_launch_time_partitions(lib):
-    # FP8 verify near one round: launches may use partitions down to half the
-    # planned length, so the workspace holds twice the partitions; bf16 and an
-    # explicit partition length keep the planned count
+def _sk_bytes(pieces, rows, d, segs):
+    o = pieces * rows * d * 4
+    ml = ((o + 255) // 256) * 256 + pieces * rows * 2 * 4
+    return ((ml + 255) // 256) * 256 + segs * 2 * 4
+
+
+def test_stream_k_workspace(lib):
+    # grouped rows by default: one partial per row of every piece, at most
+    # segments + workers pieces; workers (1024 SIMDs when no device is
+    # visible): one per SIMD for bf16, for FP8 one round of resident
+    # wavefronts (2 per SIMD with 32-row blocks, 3 with 16-row blocks); an
+    # explicit partition length keeps fixed partitions
     w = synth.get("C5")
     cap = synth.capacity_tokens(w)
-    rows = w.B * w.Hq * w.n_q
-    for dtype, explicit, factor in (("fp8_e4m3", 0, 2), ("bf16", 0, 1), ("fp8_e4m3", 512, 1)):
+    for dtype, workers in (("bf16", 1024), ("fp8_e4m3", 2048)):
         dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
-                  dtype=kvc.DTYPE_CODES[dtype],
-                  block_size=w.block_size, max_seq_len=cap,
+                  dtype=kvc.DTYPE_CODES[dtype], block_size=w.block_size, max_seq_len=cap,
                   max_blocks_per_seq=synth.max_blocks_per_seq(w),
-                  num_blocks=synth.pool_blocks(w), partition_tokens=explicit)
-        P = kvc.kvc_attn_partition_tokens(dd, w.n_q)
-        assert P == 512, (dtype, P)
-        parts = -(-cap // (P // factor))
-        assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _ws_bytes(rows, parts, w.D), dtype
+                  num_blocks=synth.pool_blocks(w))
+        assert kvc.kvc_attn_partition_tokens(dd, w.n_q) == 0
+        segs = w.B * w.Hkv  # 20 rows per KV head: one 32-row block
+        assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _sk_bytes(segs + workers, 20, w.D,
+                                                                    segs)
+    w = synth.get("C4")  # 4 rows per KV head: 16-row blocks
+    dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+              block_size=w.block_size, max_seq_len=synth.capacity_tokens(w),
+              max_blocks_per_seq=synth.max_blocks_per_seq(w), num_blocks=synth.pool_blocks(w))
+    segs = w.B * w.Hkv
+    assert kvc.kvc_attn_workspace_bytes(dd, 1) == _sk_bytes(segs + 1024, 4, w.D, segs)
+    dd.dtype = kvc.DTYPE_CODES["fp8_e4m3"]
+    assert kvc.kvc_attn_workspace_bytes(dd, 1) == _sk_bytes(segs + 3072, 4, w.D, segs)
+    w = synth.get("C5")
+    dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+              dtype=kvc.DTYPE_CODES["fp8_e4m3"], block_size=w.block_size, max_seq_len=cap,
+              max_blocks_per_seq=synth.max_blocks_per_seq(w), num_blocks=synth.pool_blocks(w),
+              partition_tokens=512)
+    assert kvc.kvc_attn_partition_tokens(dd, w.n_q) == 512
+    rows = w.B * w.Hq * w.n_q
+    assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _ws_bytes(rows, -(-cap // 512), w.D)
 
 
 def test_mla_workspace_covers_launch_time_partitions(lib):
@@ -184,7 +207,7 @@ def test_binding_refuses_host_tensors():
 def test_noalloc_refusals_before_any_device_call(lib):
     """The allocation-free attention call refuses on the host: a batch whose
     partials exceed the static scratch, bad row counts, a missing output."""
-    big = desc(batch=128, num_q_heads=32, num_kv_heads=8, dtype=0, block_size=16,
+    big = desc(batch=1024, num_q_heads=32, num_kv_heads=8, dtype=0, block_size=16,
                max_seq_len=0, max_blocks_per_seq=4096, num_blocks=600000)
     need = lib.kvc_attn_workspace_bytes(ctypes.byref(big), 16)
     assert need > kvc.NOALLOC_SCRATCH_BYTES
@@ -199,3 +222,20 @@ def test_noalloc_refusals_before_any_device_call(lib):
                                        0.1, FAKE, 5, None, None) == -3  # output type
     assert lib.kvc_verify_attn_noalloc(ctypes.byref(desc(batch=0)), None, 1, None, None, None,
                                        None, 0.1, None, 1, None, None) == 0
+
+
+def test_block_table_append_refusals(lib):
+    paged = desc(block_size=16, max_seq_len=0, max_blocks_per_seq=8, num_blocks=64)
+    call = lambda d, sl=FAKE, out=ctypes.c_void_p(0x2000), total=1: lib.kvc_block_table_append(
+        ctypes.byref(d), FAKE, FAKE, sl, FAKE, total, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        out, None, None)
+    assert call(desc()) == -1  # a contiguous cache has no table: kvc_append
+    assert call(paged, total=-1) == -1
+    assert call(paged, out=FAKE) == -1  # seq_lens_out aliases seq_lens
+    assert call(paged, out=None) == -1
+    assert call(desc(batch=9000, block_size=16, max_seq_len=0, max_blocks_per_seq=8,
+                     num_blocks=64)) == -3  # every workgroup reads the batch: <= 8192
+    assert lib.kvc_block_table_append(ctypes.byref(desc(batch=0, block_size=16, max_seq_len=0,
+                                                        max_blocks_per_seq=8, num_blocks=64)),
+                                      None, None, None, None, 0, 0, None, None, None, None, None,
+                                      None, None, None, None, None) == 0

@@ -302,3 +302,25 @@ def test_stale_workspace_bytes_do_not_matter(dv):
         assert gc.dev_status() == 0
         assert bool(torch.isfinite(outs[1]).all()), P
         assert torch.equal(outs[0], outs[1]), P
+
+
+@pytest.mark.parametrize("B,n_q,lo,hi,bs", [(300, 1, 1, 40, 16), (1, 5, 5000, 5000, 0),
+                                            (40, 5, 5, 2000, 32)])
+def test_stream_k_split(ref, B, n_q, lo, hi, bs):
+    """The matrix-core path's default (stream-K) split: workers whose runs
+    cross many short segments (300 sequences of 1-40 keys: about 150 workers
+    of 8 tiles, each spanning several sequences), one long sequence shared by
+    many workers, and a mixed verify batch; every row against the oracle."""
+    w = synth.custom(name="sk", seed=900 + B + n_q, B=B, Hq=8, Hkv=2, D=128, dtype="bf16",
+                     block_size=bs, n_q=n_q, len_lo=lo, len_hi=hi)
+    lengths = synth.final_lengths(w)
+    gc = GpuCache(w, block_size=bs if bs else None)
+    assert kvc.kvc_attn_partition_tokens(gc.desc, n_q) == 0
+    gc.prefill(lengths - n_q)
+    gc.step_rows(0)
+    out = gc.attend(queries_dev(w), n_q)
+    assert gc.dev_status() == 0
+    want = oracle_outputs(ref, w, range(B), lengths - n_q)
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert_close(got[b], want[b], "sk B=%d b=%d L=%d" % (B, b, lengths[b]))

@@ -45,9 +45,10 @@ def test_noalloc_matches_workspace_call_twice(ref):
 
 
 def test_noalloc_refuses_oversized_batch():
-    w = synth.custom(name="na-big", seed=4102, B=128, Hq=32, Hkv=8, D=128, dtype="bf16",
+    w = synth.custom(name="na-big", seed=4102, B=1024, Hq=32, Hkv=8, D=128, dtype="bf16",
                      block_size=16, n_q=16, len_lo=16, len_hi=16)
     gc = GpuCache(w, block_size=16, capacity=65536, pool_blocks=256)
+    assert kvc.kvc_attn_workspace_bytes(gc.desc, 16) > kvc.NOALLOC_SCRATCH_BYTES
     out = torch.empty((w.B, 16, w.Hq, w.D), device="cuda")
     q = torch.empty((w.B, 16, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kvc.KvcError) as e:
