@@ -192,28 +192,51 @@ def pct(xs, q):
     return round(float(np.percentile(np.asarray(xs, dtype=np.float64), q)), 3)
 
 
-def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
-    """Steps timed one at a time with a >= 1 GiB write before each, so that no
-    KV row is served from the last-level caches; HIP events on the library's
-    stream.  Returns (step us list, partition us list).
+def flushed_runs(run, iters: int, flush_bytes: int = 1 << 30):
+    """Duration of `run` (launches on torch's current stream, the library's
+    stream) with no KV row in the last-level caches, from HIP events.
 
-    A step's events bracket the whole step only: an event recorded between
-    two kernels of the step adds its own dispatch gap (about 5.6 us in the
-    kernel trace, against none between two kernels without one), so the
-    partition launches are timed in a second flushed loop of their own."""
+    An event recorded just before a kernel adds the dispatch gap that follows
+    it (about 5 us in the kernel trace, against none between two kernels), so
+    a single run's event interval overstates it.  Each iteration therefore
+    times, behind a 1 GiB write each: A = [run, 1 GiB write] and B = [run,
+    1 GiB write, run].  B - A is one run that follows a 1 GiB write with no
+    event before it -- a flushed run without the marker's gap.  Returns
+    (durations B - A, single-run event intervals [run]), microseconds."""
     import torch
     buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
-    step_us = []
+    dur, single = [], []
     for i in range(iters):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         buf.fill_(float(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        lc.step()
-        e1.record()
+        e[0].record()
+        run()
+        e[1].record()
+        buf.fill_(float(i) + 0.25)
+        e[2].record()
+        run()
+        buf.fill_(float(i) + 0.5)
+        e[3].record()
+        buf.fill_(float(i) + 0.75)
+        e[4].record()
+        run()
+        buf.fill_(float(i) + 0.125)
+        run()
+        e[5].record()
         torch.cuda.synchronize()
-        step_us.append(e0.elapsed_time(e1) * 1e3)
+        single.append(e[0].elapsed_time(e[1]) * 1e3)
+        dur.append((e[4].elapsed_time(e[5]) - e[2].elapsed_time(e[3])) * 1e3)
     del buf
-    return step_us, flushed_partitions(lc.step_partition, iters, flush_bytes)
+    return dur, single
+
+
+def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
+    """Whole steps and partition launches, each timed by flushed_runs.
+    Returns (step us, partition us, step event intervals, partition event
+    intervals)."""
+    st, st_ev = flushed_runs(lc.step, iters, flush_bytes)
+    pt, pt_ev = flushed_runs(lc.step_partition, iters, flush_bytes)
+    return st, pt, st_ev, pt_ev
 
 
 class CallTimer:
@@ -479,24 +502,6 @@ def stats(xs) -> dict:
     return {"p10": pct(xs, 10), "median": pct(xs, 50), "p90": pct(xs, 90)}
 
 
-def flushed_partitions(call, iters: int, flush_bytes: int = 1 << 30):
-    """One launch of `call` (a partition launch) timed at a time behind a
-    >= 1 GiB write, HIP events on torch's current stream.  Returns us list."""
-    import torch
-    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
-    out = []
-    for i in range(iters):
-        buf.fill_(float(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) * 1e3)
-    del buf
-    return out
-
-
 def steady_partition_us(lc, n: int) -> float:
     """Average of n back-to-back partition launches (HIP events)."""
     import torch
@@ -532,7 +537,7 @@ def config_result(name: str, warmup: int, iters: int, steady: int) -> dict:
     torch.cuda.synchronize()
     assert lc.dev_status() == 0
     kvb = kv_bytes_of(w)
-    st_us, pt_us = flushed_steps(lc, iters)
+    st_us, pt_us, _, _ = flushed_steps(lc, iters)
     sp = steady_partition_us(lc, steady)
     assert lc.dev_status() == 0
     step_med, part_med = pct(st_us, 50), pct(pt_us, 50)
@@ -579,7 +584,7 @@ def paged_vs_contiguous(iters: int) -> dict:
         lc = runner.build(w, partition_tokens=P)
         lc.step()
         torch.cuda.synchronize()
-        us = flushed_partitions(lc.step_partition, iters)
+        us, _ = flushed_runs(lc.step_partition, iters)
         assert lc.dev_status() == 0
         res[label] = {"partition_tokens": kvc.kvc_attn_partition_tokens(lc.desc, 1),
                       "flushed_partition_us": stats(us),
@@ -700,7 +705,7 @@ def main():
     # the headline: steps timed one at a time behind a 1 GiB write, so that no
     # KV row comes from the last-level caches
     F = max(1, args.flush_iters)
-    st_us, pt_us = flushed_steps(lc, F)
+    st_us, pt_us, st_ev, pt_ev = flushed_steps(lc, F)
     assert lc.dev_status() == 0
     print("# %d flushed steps: median %.2f us" % (F, pct(st_us, 50)), file=sys.stderr, flush=True)
 
@@ -742,17 +747,21 @@ def main():
             "accumulate": "f32", "cache": w.cache_dtype, "cache_row_bytes": w.kv_row_bytes,
             "cache_tensors": w.kv_tensors, "out_dim": w.out_dim,
         },
-        "timing": "value and ms_per_step use the median of %d steps, each timed alone with HIP "
-                  "events at its two ends behind a 1 GiB write that evicts the last-level caches; "
-                  "roofline uses the median of %d partition launches timed the same way; 'steady' "
-                  "is the timed region of %d back-to-back steps between two synchronisations"
-                  % (F, F, K),
+        "timing": "value and ms_per_step use the median of %d flushed step durations, roofline the "
+                  "median of %d flushed partition-launch durations: per iteration, each behind a "
+                  "1 GiB write that leaves no KV row in the last-level caches, HIP events around "
+                  "A = [run, 1 GiB write] and B = [run, 1 GiB write, run]; B - A is one run after a "
+                  "1 GiB write with no event marker (whose dispatch gap the single-run intervals in "
+                  "'flushed' include); 'steady' is the timed region of %d back-to-back steps "
+                  "between two synchronisations" % (F, F, K),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "seq_steps_per_s": round(w.B / (step_us * 1e-6), 1),
         "query_rows_per_s": round(w.B * w.n_q / (step_us * 1e-6), 1),
         "kv_bytes_per_step": kv_bytes,
         "flushed": {"iters": F, "flush_bytes": 1 << 30, "step_us": stats(st_us),
-                    "partition_us": stats(pt_us)},
+                    "partition_us": stats(pt_us),
+                    "event_interval_step_us": stats(st_ev),
+                    "event_interval_partition_us": stats(pt_ev)},
         "steady": {"steps": K, "ms_per_step": round(steady_ms, 5),
                    "gbs": round(kv_bytes / (steady_ms * 1e-3) / 1e9, 2),
                    "hbm_frac_step": round(kv_bytes / (steady_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -12,29 +12,29 @@
 // latent, combined across partitions by the usual reduce.
 //
 // Every query row of a sequence (Hq heads x n_q verify rows) reads the same
-// latent rows, so a workgroup of four wavefronts owns one (sequence, group of
-// rows, partition): its threads load each 16-key tile (16 x 1152 bytes, one
-// contiguous run) cooperatively into one LDS tile, and each wavefront
-// contracts a block of 16 rows against it on the matrix cores:
+// latent rows, so a workgroup owns one (sequence, group of rows, partition):
+// its threads load each 16-key tile (16 x 1152 bytes, one contiguous run)
+// cooperatively into one LDS tile, and its wavefronts contract 16-row blocks
+// against it on the matrix cores:
 //   S^T = K . Q^T   (18 steps of v_mfma_f32_16x16x32_bf16, Q^T in registers)
-//   O^T += V^T . P^T (its column tiles of the 512; V^T via ds_read_b64_tr_b16;
+//   O^T += V^T . P^T (column tiles of the 512; V^T via ds_read_b64_tr_b16;
 //                     the weights as bf16 hi + lo pairs along the reduction
 //                     index, as in the grouped-query kernel).
 // Online softmax per row as in the other partition kernels; verify row r
 // sees keys 0 .. L - n_q + r.
 //
-// C wavefronts share a row block and split its 512 output columns (C = 1, 2
-// or 4): each computes the block's scores and softmax itself (cheap next to
-// the value products) and accumulates 512 / C columns.  With C = 1 a
-// wavefront holds 16 rows of queries (72 VGPRs) and 512-wide fp32
-// accumulators (128) and runs alone on its SIMD; with C >= 2 two fit per
-// SIMD, and a sequence with only 16 rows (16 heads) still keeps all four
-// wavefronts of its workgroup busy.  Two LDS tiles let the score products of
-// tile n + 1 be issued before the softmax of tile n, which does not depend on
-// them; a ring of PF register stages keeps the following tiles in flight.
-// Row groups of the same (sequence, partition) get workgroup ids 8 apart:
-// launches place workgroup i on XCD i mod 8, so they share one XCD's L2 and
-// run at the same time, and the tile comes from HBM once.
+// Two forms.  Up to 16 rows (e.g. 16 heads, partition_mla with C = 4): four
+// wavefronts share the one row block, each computes its scores and softmax
+// itself and accumulates 128 of the 512 columns.  More rows (e.g. 128 heads,
+// partition_mla_pair): eight wavefronts, two per SIMD, cover four row blocks;
+// the two wavefronts of a row block split the columns, and one of them
+// computes the block's scores and softmax and passes the weights to the
+// other through LDS.  Two LDS tiles let the score products of tile n + 1 run
+// beside the value products of tile n; a ring of PF register stages keeps
+// the following tiles in flight.  Row groups of the same (sequence,
+// partition) get workgroup ids 8 apart: launches place workgroup i on XCD i
+// mod 8, so they share one XCD's L2 and run at the same time, and the tile
+// comes from HBM once.
 #include "launch.hpp"
 
 namespace kvc {
@@ -369,10 +369,273 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
   }
 }
 
+// More than 16 rows (e.g. 128 heads): a workgroup of eight wavefronts, two
+// per SIMD, covers 64 rows (four 16-row blocks) and all 512 columns.  Wave w
+// takes row block w % 4 and half w / 4; the two halves of a row block share
+// a SIMD and split the work evenly:
+//   scores: each half multiplies the tile by its half of the absorbed query
+//           (9 of the 18 steps of 32 along the 576 dims, so a wavefront holds
+//           36 query registers), the two 16 x 16 partial sums meet in LDS,
+//           and each half adds them (the same sum in both: a + b = b + a) and
+//           runs the same online softmax, so both hold the weights and the
+//           statistics without sending them;
+//   values: each half accumulates 256 of the 512 output columns.
+// A wavefront's accumulators (64 registers) and its other state then fit the
+// 256 vector registers of two wavefronts per SIMD.  (The one-wavefront form
+// held 16 rows x 512 columns in the accumulation registers, where the
+// compiler moved them on every tile, and left a lone wavefront per SIMD to
+// hide every latency.)  Tile n + 1's partial scores are issued alongside tile
+// n's value products; its softmax follows the barrier that publishes them.
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = kPairWaves * kWave;
+
+template <int PF>
+__global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams p) {
+  static_assert(PF % 2 == 0, "tile n sits in LDS buffer n % 2");
+  constexpr int DK = kMlaKeyDim;          // 576
+  constexpr int DV = kMlaValueDim;        // 512
+  constexpr int KK = DK / 32;             // 18 QK^T steps
+  constexpr int KH = KK / 2;              // 9 steps per half
+  constexpr int DT = DV / 16 / 2;         // 16 output column tiles per half
+  constexpr int CPR = DK * 2 / 16;        // 72 16-byte chunks per row
+  constexpr int TCH = kTile * CPR;        // 1152 chunks per tile
+  constexpr int PER = (TCH + kPairThreads - 1) / kPairThreads;  // chunks per thread
+  constexpr int ROWB = DK * 2 + 16;       // padded LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTile * ROWB];
+  __shared__ __attribute__((aligned(16))) f32x4_t s_ps[2][4][2][kWave];  // partial scores
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int rbw = wave & 3;    // row block of the workgroup
+  const int half = wave >> 2;  // column half, and half of the score reduction
+
+  const int R = p.Hq * p.n_q;
+  constexpr int rows_wg = 64;
+  const int n_rg = (R + rows_wg - 1) / rows_wg;
+  const long wg = blockIdx.x;
+  const int rg = (int)((wg / 8) % n_rg);
+  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);  // the unit-th live pair
+  if (unit >= (long)p.B * p.max_parts) return;
+  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+  const int2 bp = nth_pair(p.seq_lens, p.B, p.n_q, p.cap, P, (int)unit);
+  if (bp.x < 0) return;  // past the last live pair: whole workgroup
+  const int b = bp.x, part = bp.y;
+  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+  if (L < p.n_q || L > p.cap) {
+    if (rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+    return;  // whole workgroup
+  }
+  const int nparts = (L + P - 1) / P;
+  const int start = part * kTile, stride = nparts * kTile, end = L;
+
+  // this wavefront's rows: i = r * Hq + h
+  const int i_row = (rg * 4 + rbw) * 16 + col;
+  const bool rvalid = i_row < R;
+  const int r_q = rvalid ? i_row / p.Hq : 0;
+  const int h_q = rvalid ? i_row % p.Hq : 0;
+  const int lvis = rvalid ? L - p.n_q + r_q + 1 : L;
+  const long wrow = ((long)b * p.Hq + h_q) * p.n_q + r_q;
+  const bool active = __any(rvalid);  // wave-uniform: the row block has rows
+
+  bf16x8_t qf[KH];  // this half's steps of the absorbed queries (B operand of S^T)
+  {
+    const uint16_t* qrow = (const uint16_t*)p.q + (((long)b * p.n_q + r_q) * p.Hq + h_q) * DK;
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (rvalid) w = *reinterpret_cast<const uint4*>(qrow + (half * KH + k) * 32 + grp * 8);
+      qf[k] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  f32x4_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // running statistics of row col (the same in both halves)
+
+  const int n_tiles = (end - start + stride - 1) / stride;  // <= kMlaMaxTiles (plan)
+  const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  __shared__ int s_blk[kMlaMaxTiles];
+  if (p.table != nullptr) {
+    for (int n = tid; n < n_tiles; n += kPairThreads)
+      s_blk[n] = p.table[(long)b * p.max_blocks + ((start + n * stride) >> bs_shift)];
+  }
+  __syncthreads();
+  auto tile_base = [&](int n) -> long {  // element offset of tile n's first key; -1: bad block
+    const int tile = start + n * stride;
+    if (p.table == nullptr) return ((long)b * p.S_max + tile) * DK;
+    const int blk = s_blk[n];
+    if (blk < 0 || blk >= p.N) return -1;
+    return ((long)blk * p.bs + (tile & (p.bs - 1))) * DK;
+  };
+  int frow[PER];
+  uint32_t fchk[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = min(u * kPairThreads + tid, TCH - 1);  // extra threads repeat the last chunk
+    frow[u] = idx / CPR;
+    fchk[u] = (uint32_t)(idx % CPR) * 16;
+  }
+  uint4 stage[PF][PER];
+  long stb[PF];
+  // every stage issues PER loads whatever the tile (clamped rows), so the
+  // compiler can wait for one stage at a time
+  auto fetch = [&](uint4 (&st)[PER], long& tbs, int n) {
+    const int tile = start + n * stride;
+    const bool in = tile < end;
+    const long tb = tile_base(in ? n : 0);
+    tbs = in ? tb : -1;
+    const uint8_t* base = (const uint8_t*)p.k + (tbs >= 0 ? tb : 0) * 2;
+    const int last = tbs >= 0 ? min(kTile, end - tile) - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      st[u] = load_stream(base + ((uint32_t)min(frow[u], last) * (DK * 2) + fchk[u]));
+  };
+  auto store_tile = [&](int buf, const uint4 (&st)[PER]) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = u * kPairThreads + tid;
+      if (idx < TCH)
+        *reinterpret_cast<uint4*>(lds[buf] + (idx / CPR) * ROWB + (idx % CPR) * 16) = st[u];
+    }
+  };
+  constexpr float kLazy = 8.f;
+  // this half's partial S^T of the tile in `buf` (lane: keys grp*4 .. +3 of
+  // row col), published in slot `sl`
+  auto qk_half = [&](int buf, int sl) {
+    const uint8_t* ka = lds[buf] + col * ROWB + grp * 16 + half * KH * 64;
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    bf16x8_t kf[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+      kf[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + k * 64));
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      if (k & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s1, 0, 0, 0);
+      else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s0, 0, 0, 0);
+    }
+    s_ps[sl][rbw][half][lane] = s0 + s1;
+  };
+  // the whole scores of slot `sl` (half 0's part + half 1's part), online
+  // softmax: the weights (bf16 hi + lo) and the factor the accumulators must
+  // be rescaled by; rescale is wave-uniform
+  float alpha = 1.f;
+  bool rescale = false;
+  auto softmax = [&](int sl, int tile, bool ok) -> bf16x8_t {
+    const f32x4_t s = s_ps[sl][rbw][0][lane] + s_ps[sl][rbw][1][lane];
+    const int key0 = tile + grp * 4;
+    float sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = ok && key0 + v < lvis ? s[v] * p.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m + kLazy;
+    rescale = __any(move);
+    const float m_new = move ? mx : m;
+    alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+    m = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
+    const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
+    l = l * alpha + ((p01[0] + p01[1]) + (p23[0] + p23[1]));
+    const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+    const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+    const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+    const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+    return __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                   __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // O^T += V^T . P^T over this half's 256 columns
+  auto pv = [&](int buf, const bf16x8_t& pb) {
+    const uint8_t* va_ptr =
+        lds[buf] + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8 + half * (DV / 2) * 2;
+    constexpr int VG = 8;
+    auto read_v = [&](bf16x4_t (&va)[VG], int g) {
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+            (__attribute__((address_space(3))) uint8_t*)(va_ptr + (g * VG + i) * 32));
+        va[i] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+      }
+    };
+    bf16x4_t vcur[VG], vnext[VG];
+    read_v(vcur, 0);
+#pragma unroll
+    for (int g = 0; g < DT / VG; ++g) {
+      if (g + 1 < DT / VG) read_v(vnext, g + 1);
+#pragma unroll
+      for (int i = 0; i < VG; ++i) {
+        const bf16x8_t va2 = __builtin_shufflevector(vcur[i], vcur[i], 0, 1, 2, 3, 0, 1, 2, 3);
+        oacc[g * VG + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb, oacc[g * VG + i], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VG; ++i) vcur[i] = vnext[i];
+    }
+  };
+
+  // prologue: tiles 0 and 1 in LDS, tiles 2 .. PF + 1 in flight; tile 0's
+  // weights in registers
+#pragma unroll
+  for (int k = 0; k < PF; ++k) fetch(stage[k], stb[k], k);
+  store_tile(0, stage[0]);
+  store_tile(1, stage[1]);
+  bool bok[2] = {stb[0] >= 0, stb[1] >= 0};
+  __syncthreads();
+  fetch(stage[0], stb[0], PF);
+  fetch(stage[1], stb[1], PF + 1);
+  if (active) qk_half(0, 0);
+  __syncthreads();
+  bf16x8_t pb = {};
+  if (active) pb = softmax(0, start, bok[0]);
+  for (int n0 = 0; n0 < n_tiles; n0 += PF) {
+#pragma unroll
+    for (int jj = 0; jj < PF; ++jj) {  // tile n in buffer j, tile n + 1 in buffer 1 - j
+      const int n = n0 + jj;
+      const int j = jj & 1;
+      const int sg = (jj + 2) % PF;  // the stage holding tile n + 2
+      const bool more = n + 1 < n_tiles;
+      if (n < n_tiles) {
+        if (active) {
+          if (more) qk_half(1 - j, 1 - j);  // tile n + 1's partial scores
+          if (rescale) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+          }
+          if (bok[j]) pv(j, pb);  // a bad block's tile holds no usable rows
+        }
+        if (!bok[j] && tid == 0) report(p.status, KVC_ERR_DATA);
+      }
+      __syncthreads();  // partial scores of tile n + 1 published; buffer j read
+      if (n < n_tiles && more && active) pb = softmax(1 - j, start + (n + 1) * stride, bok[1 - j]);
+      store_tile(j, stage[sg]);  // tile n + 2
+      bok[j] = stb[sg] >= 0;
+      fetch(stage[sg], stb[sg], n + 2 + PF);
+      __syncthreads();
+    }
+  }
+
+  if (!rvalid) return;
+  float* wo = p.ws_o + (wrow * p.max_parts + part) * DV + half * (DV / 2);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4_t*>(wo + dt * 16 + grp * 4) = oacc[dt];
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (half == 0 && grp == 0) {
+    float* wml = p.ws_ml + (wrow * p.max_parts + part) * 2;
+    wml[0] = m;
+    wml[1] = lt;
+  }
+}
+
 // Up to 16 rows (one row block): four wavefronts split the columns, so all of
-// them compute.  More rows: each wavefront owns a row block with all 512
-// columns (with two per block the accumulators and stages no longer fit two
-// wavefronts per SIMD without spilling, measured 1.7x slower).
+// them compute (partition_mla<PF, 4>).  More rows: partition_mla_pair, 64 rows
+// per workgroup (returned as 1: one workgroup of rows per 64).
 int mla_col_split(int rows) { return rows <= 16 ? 4 : 1; }
 
 hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s) {
@@ -386,7 +649,7 @@ hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s) {
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_wg), block(kMlaThreads);
   if (C == 4) hipLaunchKernelGGL((partition_mla<2, 4>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((partition_mla<2, 1>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((partition_mla_pair<2>), grid, dim3(kPairThreads), 0, s, p);
   return hipGetLastError();
 }
 

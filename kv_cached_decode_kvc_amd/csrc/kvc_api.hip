@@ -162,10 +162,11 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
 int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
 // MLA latent decode: one bf16 latent head of 576 (512 latent + 64 RoPE key),
-// values = the 512-wide latent.  A workgroup of four wavefronts covers 64 /
-// C query rows (C wavefronts per 16-row block split the output columns); it
-// fills a CU when C = 1 and two fit per CU otherwise, so a round of resident
-// work is 256 or 512 workgroups.  The partition length grows in steps of 256
+// values = the 512-wide latent.  Up to 16 rows, a workgroup of four
+// wavefronts covers the 16 rows (C = 4 wavefronts split the output columns)
+// and two workgroups fit per CU; more rows, a workgroup of eight wavefronts
+// covers 64 rows and fills a CU (C = 1 here); so a round of resident work is
+// 512 or 256 workgroups.  The partition length grows in steps of 256
 // keys until a full-capacity batch fits in one round (a workgroup then
 // streams its partition without a second round behind it; two rounds
 // measured 10-12% slower), and halves (down to 64) while it would not fill
