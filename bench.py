@@ -231,12 +231,23 @@ def flushed_runs(run, iters: int, flush_bytes: int = 1 << 30):
     return dur, single
 
 
+def attn_launch(lc):
+    """The launch the roofline times: the attention call when it is one
+    launch (the partition kernel combining its own partials, as the step
+    runs it), else its partition launch alone (a reduce launch follows; MLA
+    too); the prefill kernel."""
+    from kv_cached_decode_kvc_amd import kvc
+    if lc.w.dv or lc.w.prefill or kvc.kvc_attn_launches(lc.desc, lc.w.n_q) != 1:
+        return lc.step_partition
+    return lc.step_attn
+
+
 def flushed_steps(lc, iters: int, flush_bytes: int = 1 << 30):
     """Whole steps and partition launches, each timed by flushed_runs.
     Returns (step us, partition us, step event intervals, partition event
     intervals)."""
     st, st_ev = flushed_runs(lc.step, iters, flush_bytes)
-    pt, pt_ev = flushed_runs(lc.step_partition, iters, flush_bytes)
+    pt, pt_ev = flushed_runs(attn_launch(lc), iters, flush_bytes)
     return st, pt, st_ev, pt_ev
 
 
@@ -324,10 +335,8 @@ def lifecycle_bench(iters: int, warmup: int):
         kvc.kvc_append(lc.desc, lc.s_k, lc.s_v, lc.s_len0, lc.s_cu, lc.s_total, w.n_q,
                        lc.s_slots, lc.k, lc.v, lc.s_len1, lc.status)
         t.mark("append")
-        lc.step_partition()
-        t.mark("partition")
-        lc.step_reduce()
-        t.mark("reduce")
+        lc.step_attn()
+        t.mark("attention")
         kvc.kvc_truncate(lc.desc, lc.s_len1, accepted[it % 8], lc.table, lc.free_list, h[1],
                          h[2], refs, l_t, lc.status)
         t.mark("truncate")
@@ -388,11 +397,9 @@ def lifecycle_bench(iters: int, warmup: int):
         kvc.kvc_append(lc.desc, lc.s_k, lc.s_v, lens, lc.s_cu, lc.s_total, 1, lc.s_slots, lc.k,
                        lc.v, l_a, lc.status)
         t.mark("append")
-        kvc.kvc_attn_partition(lc.desc, lc.s_q, 1, lc.k, lc.v, l_a, lc.table, lc.scale, lc.s_ws,
-                               lc.status)
-        t.mark("partition")
-        kvc.kvc_attn_reduce(lc.desc, 1, l_a, lc.s_ws, lc.s_out, lc.status)
-        t.mark("reduce")
+        kvc.kvc_decode_attn(lc.desc, lc.s_q, lc.k, lc.v, l_a, lc.table, lc.scale, lc.s_out,
+                            lc.s_ws, lc.status)
+        t.mark("attention")
         kvc.kvc_truncate(lc.desc, l_a, prompt_only, lc.table, lc.free_list, lc.head, lc.head,
                          refs, l_b, lc.status)
         t.mark("truncate")
@@ -413,7 +420,7 @@ def lifecycle_bench(iters: int, warmup: int):
         "workload": ws.name, "prompts": n_prompt, "samples_per_prompt": 4,
         "calls_us": med, "round_us": round(step, 3),
         "lifecycle_share": round((med["fork"] + med["cow"] + med["truncate"]) / step, 4),
-        "attention_gbs": round(att_bytes / ((med["partition"] + med["reduce"]) * 1e-6) / 1e9, 2),
+        "attention_gbs": round(att_bytes / (med["attention"] * 1e-6) / 1e9, 2),
     }
     blk_bytes = ws.Hkv * 16 * ws.D * ws.esize
     del lc
@@ -507,9 +514,10 @@ def steady_partition_us(lc, n: int) -> float:
     """Average of n back-to-back partition launches (HIP events)."""
     import torch
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    run = attn_launch(lc)
     ev0.record()
     for _ in range(n):
-        lc.step_partition()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / n * 1e3

@@ -217,15 +217,20 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
  * [I1] "Why attention matters": softmax(q K^T * scale) V; [I1] "KV cache": a
  * single new row sees every cached key; [I1] "FlashDecoding": split-KV --
  * partitions of the keys processed in parallel, each yielding a partial output
- * with its running maximum and sum ([VN] 07 "Online softmax"), then a separate
- * reduction combines them.  Equivalent to kvc_verify_attn with n_q = 1.
+ * with its running maximum and sum ([VN] 07 "Online softmax"), then a
+ * reduction combines them.  With one query row per KV row (MHA, fp32
+ * caches) and at most one round of resident work items (4096 on MI355X) the
+ * combine runs inside the same launch: the work item that finishes a row's
+ * last partition merges the row's partials and writes it.  Otherwise a
+ * second launch combines.  Equivalent to kvc_verify_attn with n_q = 1.
  *
  *   q            (device) [B][1][Hq][D], dtype d->dtype
  *   seq_lens     (device) [B], 1 <= seq_lens[b] <= capacity
  *   block_table  (device) paged: [B][max_blocks_per_seq]; contiguous: NULL
  *   scale        (host)   score scale, normally 1/sqrt(D)
  *   out          (device) [B][1][Hq][D] of out_dtype (KVC_BF16 rounds to nearest even)
- *   workspace    (device) >= kvc_attn_workspace_bytes(d, 1) bytes, 16-byte aligned
+ *   workspace    (device) >= kvc_attn_workspace_bytes(d, 1) bytes, 16-byte aligned,
+ *                zero-filled before its first use (see kvc_attn_workspace_bytes)
  * A sequence with invalid data produces zeros and reports KVC_ERR_DATA.
  */
 int kvc_decode_attn(const kvc_cache_desc* d, const void* q, const void* k_cache,
@@ -261,10 +266,12 @@ int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const v
  * returns KVC_ERR_WORKSPACE before any launch.  `stream` must belong to the
  * current device (else KVC_ERR_ARG); a failed lookup of the array's
  * address returns KVC_ERR_HIP.  Every call on one device shares its array,
- * which keeps the last call's partials (nothing in it needs to start at
- * zero): calls that overlap on one device -- on different streams, or from
- * different host threads without ordering -- race and give undefined
- * results.  Other arguments, checks and results as kvc_verify_attn. */
+ * which keeps the last call's partials; its counters (see
+ * kvc_attn_workspace_bytes) are zero when the library loads and every call
+ * leaves them at zero.  Calls that overlap on one device -- on different
+ * streams, or from different host threads without ordering -- race and give
+ * undefined results.  Other arguments, checks and results as
+ * kvc_verify_attn. */
 #define KVC_NOALLOC_SCRATCH_BYTES (64u << 20)
 int kvc_verify_attn_noalloc(const kvc_cache_desc* d, const void* q, int32_t n_q,
                             const void* k_cache, const void* v_cache, const int32_t* seq_lens,
@@ -289,7 +296,12 @@ int kvc_attn_reduce(const kvc_cache_desc* d, int32_t n_q, const int32_t* seq_len
 
 /* Workspace bytes the attention calls need for this desc and n_q (0 on a bad
  * desc).  With the stream-K split (below) it depends on the current
- * device's compute-unit count, not on the capacity. */
+ * device's compute-unit count, not on the capacity.  The first 256 KiB of
+ * every attention workspace (MLA's too) hold the counters of the combine
+ * fused into the partition launch: they must be zero before the
+ * workspace's first use (one hipMemset after allocating it) and every call
+ * leaves them at zero; no call writes partials there, so calls of any
+ * shape may share one workspace (one at a time). */
 size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
 
 /* Partition length in tokens the attention calls use for this desc and n_q
@@ -303,6 +315,14 @@ size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
  * number of tiles whatever the lengths.  An explicit desc.partition_tokens
  * is always used as given (fixed partitions). */
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
+
+/* Kernel launches kvc_decode_attn / kvc_verify_attn make for this desc and
+ * n_q (negative kvc_status on a bad desc): 1 when the partition launch also
+ * combines its partials (one query row per KV row, at most one round of
+ * resident work items and 65536 rows), else 2 (a reduce launch follows).
+ * kvc_append_attn adds the append launch in front when its append is not
+ * fused (grouped rows, FP8 caches). */
+int32_t kvc_attn_launches(const kvc_cache_desc* d, int32_t n_q);
 
 /*
  * Block lifecycle (paged caches only): sharing, copy-on-write and rollback.

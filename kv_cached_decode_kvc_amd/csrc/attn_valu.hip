@@ -149,8 +149,13 @@ struct Elem<Fp8<F>> {  // FP8 codes: a 16-byte load holds 16 elements; q is 16 b
 // AP: an append fused into the launch (contiguous caches, not FP8): the new
 // rows of a sequence come from k_new / v_new and are written into the cache
 // (AttnParams::cu_new).
+// Wavefronts per SIMD the FP8 forms keep room for (measured best; the fused
+// combine would otherwise cost them one).
+template <typename T, int D>
+constexpr int valu_min_waves() { return IsFp8<T>::kFormat == 0 ? 1 : D == 128 ? 5 : 6; }
+
 template <typename T, int D, bool AP>
-__global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
+__global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
   constexpr bool kF8 = IsFp8<T>::kFormat != 0;
@@ -166,6 +171,10 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
   if (L < 0) {
     if (part == 0 && h == 0 && r == 0 && lane == 0) report(p.status, code);
     if (writer) p.seq_lens_out[b] = p.seq_lens[b];  // a refused append keeps the length
+    if (p.cnt && part == 0 && lane * 4 < D) {  // combine fused in: the row's output is zeros
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      store_out<4>(p.out, p.out_bf16, (((long)b * p.n_q + r) * p.Hq + h) * D + lane * 4, z);
+    }
     return;
   }
   if (writer) p.seq_lens_out[b] = L;
@@ -181,7 +190,6 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
   const int stride = nparts * kTile;            // distance to its next tile
   const int end = L - p.n_q + r + 1;            // visible keys of row r
   const long row = ((long)b * p.Hq + h) * p.n_q + r;
-  float* wo = p.ws_o + (row * p.max_parts + part) * D;
   float* wml = p.ws_ml + (row * p.max_parts + part) * 2;
   const int c = lane % LPR;   // which 16-byte column chunk of a key row
   const int r0 = lane / LPR;  // which row of a wave load
@@ -321,14 +329,74 @@ __global__ __launch_bounds__(64) void partition_valu(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < VE; ++j) o[j] = cross_sum<LPR>(o[j]);
   }
+  // partials: read by the reduce kernel (a later launch: plain stores) or,
+  // combine fused in, by another work item of this launch (write-through)
+  const __amdgpu_buffer_rsrc_t prow = shared_rsrc(p.ws_o + row * p.max_parts * D);  // the row's partials
   if (r0 == 0) {
 #pragma unroll
-    for (int j = 0; j < VE; j += 4)
-      *reinterpret_cast<float4*>(wo + c * VE + j) = make_float4(o[j], o[j + 1], o[j + 2], o[j + 3]);
+    for (int j = 0; j < VE; j += 4) {
+      const f32x4_t v = {o[j], o[j + 1], o[j + 2], o[j + 3]};
+      if (p.cnt) st_shared4(prow, (uint32_t)((part * D + c * VE + j) * 4), v);
+      else *reinterpret_cast<f32x4_t*>(p.ws_o + (row * p.max_parts + part) * D + c * VE + j) = v;
+    }
   }
   if (lane == 0) {
-    wml[0] = m;
-    wml[1] = l;
+    if (p.cnt) {
+      st_shared(wml, m);
+      st_shared(wml + 1, l);
+    } else {
+      wml[0] = m;
+      wml[1] = l;
+    }
+  }
+
+  // Combine fused in: the row's last partition to finish merges the row's
+  // partials and writes the row.  Lane (r0, c) takes partitions r0, r0 +
+  // RPL, ... for its columns, and the row groups merge by shuffles.  Every
+  // partial, this one's too, is read back from the workspace, so the order
+  // of the sums does not depend on which partition finished last.
+  if (p.cnt && arrive_last(p.cnt, row, nparts)) {
+    float mm = -INFINITY, dd = 0.f, acc[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) acc[j] = 0.f;
+    const float2* mlp = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
+    constexpr int KU = VE >= 16 ? 1 : 2;  // partials per lane in flight
+    for (int j0 = r0; j0 < nparts; j0 += KU * RPL) {
+      float2 mlv[KU];
+      float ov[KU][VE];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int j = j0 + u * RPL;
+        const bool use = j < nparts;
+        mlv[u] = make_float2(-INFINITY, 0.f);
+        if (use) mlv[u] = make_float2(ld_shared(&mlp[j].x), ld_shared(&mlp[j].y));
+#pragma unroll
+        for (int k = 0; k < VE; k += 4) {
+          f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+          if (use) x = ld_shared4(prow, (uint32_t)((j * D + c * VE + k) * 4));
+          ov[u][k] = x[0], ov[u][k + 1] = x[1], ov[u][k + 2] = x[2], ov[u][k + 3] = x[3];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KU; ++u) merge_partial<VE>(mm, dd, acc, mlv[u].x, mlv[u].y, ov[u]);
+    }
+#pragma unroll
+    for (int sh = LPR; sh < kWave; sh <<= 1) {  // one column at a time: no second copy
+      const float m2 = __shfl_xor(mm, sh), d2 = __shfl_xor(dd, sh);
+      const float mn = fmaxf(mm, m2);
+      const float wa = mm == -INFINITY ? 0.f : fast_exp2(mm - mn);
+      const float wb = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+      for (int k = 0; k < VE; ++k) acc[k] = acc[k] * wa + __shfl_xor(acc[k], sh) * wb;
+      dd = dd * wa + d2 * wb;
+      mm = mn;
+    }
+    if (r0 == 0) {
+      const float inv = dd > 0.f ? 1.f / dd : 0.f;
+#pragma unroll
+      for (int k = 0; k < VE; ++k) acc[k] *= inv;
+      store_out<VE>(p.out, p.out_bf16, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE, acc);
+    }
   }
 }
 

@@ -55,7 +55,83 @@ struct AttnParams {
   void* v_out;
   int32_t* seq_lens_out;
   int total_new;
+  // Combine fused into the partition launch of the vector-ALU kernel (cnt ==
+  // NULL: the reduce kernel combines).  cnt[row] counts the row's finished
+  // partitions; the one that completes the row merges all of its partials
+  // and writes the row to `out`, then sets cnt[row] back to zero, so the
+  // counters are zero between launches.
+  uint32_t* cnt;
+  void* out;
+  int out_bf16;          // out: bf16 (1) or fp32 (0), [B][n_q][Hq][D]
 };
+
+// Partials that a launch's own work items combine cross XCDs, whose L2
+// caches are separate.  They are written and read with agent-scope atomic
+// stores and loads (relaxed), which the compiler emits as write-through and
+// coherent accesses (the sc1 cache policy): no device-scope fence, which
+// would write back and invalidate a whole L2, is needed around them.
+__device__ __forceinline__ void st_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_shared(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same cache policy (sc1) on 16-byte buffer accesses, so that a row of
+// partial outputs goes out and comes back in whole lines: `base` is
+// wave-uniform (a buffer resource lives in scalar registers) and the byte
+// offsets stay far below the resource's 2 GiB range.  Word 3 of the
+// resource is gfx950's raw 32-bit buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t shared_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCoherentPolicy = 16;  // the sc1 bit of a buffer access's cache policy
+__device__ __forceinline__ void st_shared4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4_t v) {
+  typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_v, v), r, (int)byte_off, 0,
+                                         kCoherentPolicy);
+}
+__device__ __forceinline__ f32x4_t ld_shared4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCoherentPolicy));
+}
+
+// Arrival of one piece of a unit whose partials it has written with
+// st_shared: true for the piece that completes the unit (the n-th), which may
+// then read every piece's partials with ld_shared.  This wavefront's partial
+// stores are complete (s_waitcnt vmcnt(0): a write-through store counts as
+// done once the coherent level has it) before its count goes in; the
+// completing piece resets the counter.  Called by all lanes; the result is
+// wave-uniform.
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, long unit, int n) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt and lgkmcnt not waited on
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t old = 0;
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    old = __hip_atomic_fetch_add(cnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old + 1 != (uint32_t)n) return false;
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_store(cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Online merge of partial (mj, lj, oj[0..N)) into (m, d, acc): the partials'
+// maxima are in the log2 domain and an empty partial has mj = -inf
+// ("Inference-1", "FlashDecoding": every chunk's output is rescaled by
+// 2^(m_j - m*) before the sum).
+template <int N>
+__device__ __forceinline__ void merge_partial(float& m, float& d, float* acc, float mj, float lj,
+                                              const float* oj) {
+  if (mj == -INFINITY) return;
+  const float mn = fmaxf(m, mj);
+  const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+  const float w = __builtin_amdgcn_exp2f(mj - mn);
+  d = d * a + lj * w;
+#pragma unroll
+  for (int k = 0; k < N; ++k) acc[k] = acc[k] * a + oj[k] * w;
+  m = mn;
+}
 
 // Attended length of sequence b and whether it is usable: seq_lens[b], or,
 // with an append fused in, seq_lens[b] plus its new rows.  *code receives the
@@ -188,6 +264,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// N consecutive outputs (N a multiple of 4, `off` a multiple of 4 elements)
+// as bf16 (round to nearest even) or fp32.
+template <int N>
+__device__ __forceinline__ void store_out(void* out, bool bf16, long off, const float* v) {
+  static_assert(N % 4 == 0, "whole groups of four");
+  if (bf16) {
+    uint2* o = reinterpret_cast<uint2*>((uint16_t*)out + off);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k)
+      o[k] = make_uint2(f32_to_bf16_bits(v[4 * k]) | (f32_to_bf16_bits(v[4 * k + 1]) << 16),
+                        f32_to_bf16_bits(v[4 * k + 2]) | (f32_to_bf16_bits(v[4 * k + 3]) << 16));
+  } else {
+    float4* o = reinterpret_cast<float4*>((float*)out + off);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
 }
 
 // a.x*b.x + a.y*b.y + c over bf16 pairs with an fp32 accumulator (v_dot2_f32_bf16).

@@ -70,12 +70,22 @@ struct Plan {
   int sk_workers;     // stream-K: workers launched (one round of resident wavefronts)
   int sk_rows;        // stream-K: rows one piece holds
   long grid;          // workgroups of the partition launch
+  size_t o_offset;    // byte offset of the partial outputs inside the workspace
   size_t ml_offset;   // byte offset of the (m, l) array inside the workspace
   size_t meta_offset; // stream-K: byte offset of the per-segment worker records
+  bool fused;         // the one-call entry points combine inside the partition launch (vector ALU)
   size_t bytes;       // workspace size
 };
 
 constexpr int kSkMinTiles = 8;  // stream-K: fewest 16-key tiles a worker streams
+
+// Every attention workspace starts with kCntBytes of piece counters for the
+// combine fused into the partition launch (one per output row); the partials
+// of every plan, MLA included, come after them.  The counters must be zero before a workspace's first use and every
+// call leaves them at zero, so calls of any shape may share a workspace.  A
+// call with more units than counters runs the separate reduce kernel.
+constexpr size_t kCntBytes = 256u << 10;
+constexpr long kMaxCounters = (long)(kCntBytes / sizeof(uint32_t));
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -132,7 +142,8 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
     pl.sk_rows = std::min(pl.rows_per_item, R);
     pl.grid = pl.sk_workers;
     const size_t pieces = (size_t)units + pl.sk_workers;
-    pl.ml_offset = align256(pieces * pl.sk_rows * d->head_dim * sizeof(float));
+    pl.o_offset = kCntBytes;
+    pl.ml_offset = align256(pl.o_offset + pieces * pl.sk_rows * d->head_dim * sizeof(float));
     pl.meta_offset = align256(pl.ml_offset + pieces * pl.sk_rows * 2 * sizeof(float));
     pl.bytes = pl.meta_offset + (size_t)units * 2 * sizeof(int32_t);
     return pl;
@@ -154,8 +165,20 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
   pl.max_parts = (cap + pl.P_lo - 1) / pl.P_lo;
   pl.grid = xcd_grid(d->batch, pl.units, pl.max_parts);
   const size_t o_bytes = rows * pl.max_parts * d->head_dim * sizeof(float);
-  pl.ml_offset = align256(o_bytes);
+  pl.o_offset = kCntBytes;
+  pl.ml_offset = align256(pl.o_offset + o_bytes);
   pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
+  // The vector-ALU kernel combines in its own launch (one counter per output
+  // row) when its work items fit one round of resident wavefronts: each item
+  // then waits once for its partial to reach the coherent level and for its
+  // count (a few microseconds, all items at the same time), which is less
+  // than a second launch.  A larger grid pays that wait round after round,
+  // and the separate reduce kernel is cheaper (measured on MI355X: the
+  // 16 x 40-head layer, 1280 items, step 105.9 -> 100.8 us fused; the
+  // 64-sequence paged MHA batch, 20480 items, 425 -> 432 us).  The
+  // matrix-core kernel's stream-K workers would pay the wait on every piece
+  // and keep the separate reduce.
+  pl.fused = !pl.mfma && (long)rows <= kMaxCounters && pl.grid <= 4L * resident_simds();
   return pl;
 }
 
@@ -209,7 +232,8 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   pl.max_parts = (cap + pl.P_lo - 1) / pl.P_lo;
   const size_t rows = (size_t)d->batch * d->num_q_heads * n_q;
   const size_t o_bytes = rows * pl.max_parts * kMlaValueDim * sizeof(float);
-  pl.ml_offset = (o_bytes + 255) & ~(size_t)255;
+  pl.o_offset = kCntBytes;  // the counters of other calls sharing the workspace stay untouched
+  pl.ml_offset = align256(pl.o_offset + o_bytes);
   pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
   return pl;
 }
@@ -257,16 +281,19 @@ int check_reduce(const kvc_cache_desc* d, int n_q, const int32_t* seq_lens, cons
   return KVC_OK;
 }
 
+// out != NULL (and a fused plan): the partition launch also combines and
+// writes `out`.
 AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const void* q,
                        const void* k, const void* v, const int32_t* seq_lens,
-                       const int32_t* table, float scale, void* ws, int32_t* status) {
+                       const int32_t* table, float scale, void* ws, int32_t* status,
+                       void* out = nullptr, int32_t out_dtype = KVC_F32) {
   AttnParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.seq_lens = seq_lens;
   p.table = table;
-  p.ws_o = (float*)ws;
+  p.ws_o = (float*)((char*)ws + pl.o_offset);
   p.ws_ml = (float*)((char*)ws + pl.ml_offset);
   p.status = status;
   p.B = d->batch;
@@ -292,6 +319,11 @@ AttnParams attn_params(const kvc_cache_desc* d, const Plan& pl, int n_q, const v
     p.sk_rows = pl.sk_rows;
     p.sk_min_tiles = kSkMinTiles;
   }
+  if (out && pl.fused) {
+    p.cnt = (uint32_t*)ws;  // the counter region at the workspace's start
+    p.out = out;
+    p.out_bf16 = out_dtype == KVC_BF16;
+  }
   return p;
 }
 
@@ -299,7 +331,7 @@ ReduceParams reduce_params(const kvc_cache_desc* d, const Plan& pl, int n_q, int
                            const int32_t* seq_lens, const void* ws, void* out,
                            int32_t* status) {
   ReduceParams p{};
-  p.ws_o = (const float*)ws;
+  p.ws_o = (const float*)((const char*)ws + pl.o_offset);
   p.ws_ml = (const float*)((const char*)ws + pl.ml_offset);
   p.seq_lens = seq_lens;
   p.out = out;
@@ -325,12 +357,13 @@ ReduceParams reduce_params(const kvc_cache_desc* d, const Plan& pl, int n_q, int
 }
 
 // The two stages of decode / verify attention with a plan already checked.
+// With out != NULL and a fused plan the partition launch is the whole call.
 int run_partition(const kvc_cache_desc* d, const Plan& pl, const void* q, int n_q,
                   const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                   const int32_t* block_table, float scale, void* ws, int32_t* status,
-                  void* stream) {
+                  void* stream, void* out = nullptr, int32_t out_dtype = KVC_F32) {
   const AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
-                                   ws, status);
+                                   ws, status, out, out_dtype);
   hipError_t e = pl.mfma ? launch_partition_mfma(p, pl.rows_per_item, fp8_format(d),
                                                  (hipStream_t)stream)
                          : launch_partition_valu(p, d->dtype, (hipStream_t)stream);
@@ -518,7 +551,7 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
     // one partition launch appends and attends; the reduce takes the same
     // lengths (before the append, plus the new rows)
     AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, nullptr, scale,
-                               workspace, dev_status);
+                               workspace, dev_status, out, out_dtype);
     p.cu_new = cu_new;
     p.k_new = k_new;
     p.v_new = v_new;
@@ -527,7 +560,7 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
     p.seq_lens_out = seq_lens_out;
     p.total_new = total_new;
     st = hip_status(launch_partition_valu(p, d->dtype, (hipStream_t)stream));
-    if (st != KVC_OK) return st;
+    if (st != KVC_OK || p.cnt) return st;  // combined inside the launch
     ReduceParams r = reduce_params(d, pl, n_q, d->head_dim, seq_lens, workspace, out, dev_status);
     r.cu_new = cu_new;
     r.total_new = total_new;
@@ -538,8 +571,8 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
                   seq_lens_out, dev_status, stream);
   if (st != KVC_OK) return st;
   st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens_out, nullptr, scale, workspace,
-                     dev_status, stream);
-  if (st != KVC_OK) return st;
+                     dev_status, stream, out, out_dtype);
+  if (st != KVC_OK || pl.fused) return st;
   return run_reduce(d, pl, n_q, d->head_dim, seq_lens_out, workspace, out, out_dtype, dev_status,
                     stream);
 }
@@ -579,8 +612,8 @@ int kvc_verify_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const v
   if (d->batch == 0) return KVC_OK;
   if (!out) return KVC_ERR_ARG;
   st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, workspace,
-                     dev_status, stream);
-  if (st != KVC_OK) return st;
+                     dev_status, stream, out, out_dtype);
+  if (st != KVC_OK || pl.fused) return st;
   return run_reduce(d, pl, n_q, d->head_dim, seq_lens, workspace, out, out_dtype, dev_status,
                     stream);
 }
@@ -619,8 +652,8 @@ int kvc_verify_attn_noalloc(const kvc_cache_desc* d, const void* q, int32_t n_q,
   void* ws = scratch_ptr();
   if (!ws) return KVC_ERR_HIP;
   st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, ws,
-                     dev_status, stream);
-  if (st != KVC_OK) return st;
+                     dev_status, stream, out, out_dtype);
+  if (st != KVC_OK || pl.fused) return st;
   return run_reduce(d, pl, n_q, d->head_dim, seq_lens, ws, out, out_dtype, dev_status, stream);
 }
 
@@ -855,6 +888,14 @@ int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q) {
   if (st != KVC_OK) return st;
   if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
   return make_plan(d, n_q).P;
+}
+
+int32_t kvc_attn_launches(const kvc_cache_desc* d, int32_t n_q) {
+  const int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (n_q < 1 || n_q > 16) return KVC_ERR_UNSUPPORTED;
+  if (d->head_dim == kMlaKeyDim) return KVC_ERR_UNSUPPORTED;  // the kvc_mla_* calls
+  return make_plan(d, n_q).fused ? 1 : 2;
 }
 
 const char* kvc_status_string(int32_t status) {

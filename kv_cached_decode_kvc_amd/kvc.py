@@ -26,8 +26,8 @@ STATUS_NAMES = {0: "KVC_OK", -1: "KVC_ERR_ARG", -2: "KVC_ERR_SHAPE", -3: "KVC_ER
 EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn",
            "kvc_attn_partition", "kvc_attn_reduce", "kvc_attn_workspace_bytes",
            "kvc_fork", "kvc_truncate", "kvc_cow", "kvc_copy_blocks",
-           "kvc_attn_partition_tokens", "kvc_cache_bytes", "kvc_mla_workspace_bytes",
-           "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
+           "kvc_attn_partition_tokens", "kvc_attn_launches", "kvc_cache_bytes",
+           "kvc_mla_workspace_bytes", "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
            "kvc_mla_attn", "kvc_prefill_attn", "kvc_status_string", "kvc_verify_attn_noalloc",
            "kvc_block_table_append", "kvc_append_attn")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KVC_NOALLOC_SCRATCH_BYTES
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.kvc_cache_bytes.restype = ctypes.c_size_t
         L.kvc_attn_partition_tokens.argtypes = [D, I]
         L.kvc_attn_partition_tokens.restype = ctypes.c_int32
+        L.kvc_attn_launches.argtypes = [D, I]
+        L.kvc_attn_launches.restype = ctypes.c_int32
         L.kvc_status_string.argtypes = [I]
         L.kvc_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -286,6 +288,10 @@ def kvc_attn_workspace_bytes(desc, n_q) -> int:
 
 def kvc_attn_partition_tokens(desc, n_q) -> int:
     return int(lib().kvc_attn_partition_tokens(ctypes.byref(desc), int(n_q)))
+
+
+def kvc_attn_launches(desc, n_q) -> int:
+    return int(lib().kvc_attn_launches(ctypes.byref(desc), int(n_q)))
 
 
 def kvc_mla_workspace_bytes(desc, n_q, value_dim) -> int:

@@ -3,8 +3,10 @@
 ``LayerCache`` owns the device buffers of a workload (cache or block pool,
 block table, free list, lengths, workspace) and runs the decode step the way a
 serving loop would: ``kvc_block_table_append`` (paged caches) ->
-``kvc_attn_partition`` -> ``kvc_attn_reduce``, or, for a contiguous cache,
-``kvc_append_attn`` (append and attention in one call).  Every step of the computation
+``kvc_verify_attn`` (one launch: the partition kernel combines its own
+partials), or, for a contiguous cache, ``kvc_append_attn`` (append and
+attention in one call).  The two-stage calls ``kvc_attn_partition`` ->
+``kvc_attn_reduce`` remain available for timing the stages apart.  Every step of the computation
 runs in the library's kernels; this module only allocates tensors with torch
 and passes their addresses.
 
@@ -149,7 +151,8 @@ class LayerCache:
             nbytes = kvc.kvc_mla_workspace_bytes(self.desc, n_q, self.w.dv)
         else:
             nbytes = kvc.kvc_attn_workspace_bytes(self.desc, n_q)
-        return torch.empty(max((nbytes + 3) // 4, 4), dtype=torch.float32, device=self.dev)
+        # zero-filled: the combine counters at its start must begin at zero
+        return torch.zeros(max((nbytes + 3) // 4, 4), dtype=torch.float32, device=self.dev)
 
     def attend(self, q: torch.Tensor, n_q: int, out_dtype=torch.float32, scale=None,
                seq_lens=None) -> torch.Tensor:
@@ -237,6 +240,23 @@ class LayerCache:
         if not self.w.prefill:
             self.reduce(self.w.n_q, self.s_len1, self.s_ws, self.s_out)
 
+    def attn(self, q, n_q, lens, ws, out):
+        """Attention of n_q rows per sequence through the one-call entry points
+        (decode / verify: one launch that also combines the partials)."""
+        if self.w.dv:
+            kvc.kvc_mla_attn(self.desc, q, n_q, self.k, lens, self.table, self.w.dv, self.scale,
+                             out, ws, self.status)
+        else:
+            kvc.kvc_verify_attn(self.desc, q, n_q, self.k, self.v, lens, self.table, self.scale,
+                                out, ws, self.status)
+
+    def step_attn(self):
+        """The prepared step's attention as a serving loop calls it."""
+        if self.w.prefill:
+            self.step_partition()
+        else:
+            self.attn(self.s_q, self.w.n_q, self.s_len1, self.s_ws, self.s_out)
+
     @property
     def fused_step(self) -> bool:
         """Contiguous decode / verify: the append runs inside the attention call
@@ -251,8 +271,7 @@ class LayerCache:
                                 self.scale, self.s_out, self.s_ws, self.status)
             return self.s_out
         self.step_front()
-        self.step_partition()
-        self.step_reduce()
+        self.step_attn()
         return self.s_out
 
 
@@ -297,8 +316,7 @@ class DecodeLoop:
             else:
                 kvc.kvc_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total,
                                w.n_q, None, lc.k, lc.v, self.lens[s + 1], lc.status)
-            lc.partition(self.q[s], w.n_q, self.lens[s + 1], self.ws)
-            lc.reduce(w.n_q, self.lens[s + 1], self.ws, self.out[s])
+            lc.attn(self.q[s], w.n_q, self.lens[s + 1], self.ws, self.out[s])
         return self.out
 
     def capture(self):

@@ -100,12 +100,26 @@ def test_paging_argument_errors(lib):
                           ctypes.c_void_p(0x2000), None, None) == -1
 
 
+def test_attention_launch_count(lib):
+    """One launch when the vector-ALU partition kernel combines its own
+    partials (one query row per KV row, a grid of at most 4096 items), else
+    two (a reduce launch follows)."""
+    c1 = desc(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=64, max_seq_len=288, dtype=1)
+    assert kvc.kvc_attn_launches(c1, 1) == 1
+    assert kvc.kvc_attn_launches(desc(), 1) == 1  # 16 x 40 heads, 2 partitions: 1280 items
+    assert kvc.kvc_attn_launches(desc(batch=64), 1) == 2  # 5120 items: more than one round
+    assert kvc.kvc_attn_launches(desc(num_kv_heads=8), 1) == 2  # grouped rows: matrix cores
+    assert kvc.kvc_attn_launches(desc(), 5) == 2  # verify rows share a KV row: matrix cores
+    assert kvc.kvc_attn_launches(desc(head_dim=80), 1) == -3
+    assert kvc.kvc_attn_launches(desc(), 17) == -3
+
+
 def test_workspace_and_partition_sizes(lib):
     d = desc()  # 16 x 40 heads, contiguous, 2048 tokens
     assert kvc.kvc_attn_partition_tokens(d, 1) == 1024  # contiguous: long runs
     rows, parts = 16 * 40, 2048 // 1024
     o = rows * parts * 128 * 4
-    assert kvc.kvc_attn_workspace_bytes(d, 1) == ((o + 255) // 256) * 256 + rows * parts * 2 * 4
+    assert kvc.kvc_attn_workspace_bytes(d, 1) == CNT + ((o + 255) // 256) * 256 + rows * parts * 2 * 4
     small = desc(batch=2, num_q_heads=4, num_kv_heads=4, head_dim=64, max_seq_len=288, dtype=1)
     assert kvc.kvc_attn_partition_tokens(small, 1) == 64  # halved while fewer than 1024 items
     assert kvc.kvc_attn_partition_tokens(desc(partition_tokens=48), 1) == 48
@@ -124,15 +138,20 @@ def test_workspace_and_partition_sizes(lib):
         assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) > 0
 
 
+# every attention workspace starts with 256 KiB of combine counters (zero
+# between calls); the partials follow
+CNT = 256 << 10
+
+
 def _ws_bytes(rows, parts, d):
     o = rows * parts * d * 4
-    return ((o + 255) // 256) * 256 + rows * parts * 2 * 4
+    return CNT + ((o + 255) // 256) * 256 + rows * parts * 2 * 4
 
 
 def _sk_bytes(pieces, rows, d, segs):
     o = pieces * rows * d * 4
     ml = ((o + 255) // 256) * 256 + pieces * rows * 2 * 4
-    return ((ml + 255) // 256) * 256 + segs * 2 * 4
+    return CNT + ((ml + 255) // 256) * 256 + segs * 2 * 4
 
 
 def test_stream_k_workspace(lib):

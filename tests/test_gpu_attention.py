@@ -272,9 +272,10 @@ def test_peaked_weights_large_values(ref, n_q):
 def test_stale_workspace_bytes_do_not_matter(dv):
     """The reduce requests every partition slot of a row before it knows the
     row's partition count and discards the extra slots by selection: a
-    workspace full of NaN (stale bytes) gives the same outputs bit for bit.
-    Lengths from 1 to 700 with 32-key partitions give rows with 1 to 22
-    partitions (past the 16 the reduce fetches early) next to unused slots."""
+    workspace full of NaN (stale bytes) past its counter region (which must
+    be zero) gives the same outputs bit for bit.  Lengths from 1 to 700 with
+    32-key partitions give rows with 1 to 22 partitions (past the 16 the
+    reduce fetches early) next to unused slots."""
     if dv:
         w = synth.custom(name="ws-mla", seed=77, B=5, Hq=16, Hkv=1, D=576, dtype="bf16",
                          block_size=64, n_q=1, len_lo=1, len_hi=700, dv=512)
@@ -291,6 +292,7 @@ def test_stale_workspace_bytes_do_not_matter(dv):
         for fill in (0.0, float("nan")):
             ws = gc.workspace(1)
             ws.fill_(fill)
+            ws[:(256 << 10) // 4].zero_()  # the combine counters
             out = torch.empty((w.B, 1, w.Hq, w.out_dim), dtype=torch.float32, device="cuda")
             if dv:
                 kvc.kvc_mla_attn(gc.desc, q, 1, gc.k, gc.seq_lens, gc.table, dv, gc.scale, out, ws,
