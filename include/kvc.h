@@ -211,6 +211,34 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
                     void* workspace, size_t workspace_bytes, int32_t* dev_status, void* stream);
 
 /*
+ * kvc_block_table_append_attn -- kvc_block_table_append followed by
+ * kvc_verify_attn over the lengths after the append, for a paged cache
+ * ([I1] PagedAttention: blocks on demand; [EI] lists "KV cache write +
+ * attention" among the fused kernels serving systems ship).  With one query
+ * row per KV row (MHA, every fp32 cache; not FP8) the partition launch does
+ * it all: its tiles read the new rows from k_new / v_new (never a table
+ * entry this call writes), and one work item per sequence repeats the
+ * batch's block count, takes the sequence's blocks from the free list and
+ * writes the table entries, slots, new rows and length (sequence 0 the
+ * head).  Grouped rows and FP8 caches run kvc_block_table_append first.
+ * Arguments as kvc_block_table_append (B <= 8192) and kvc_verify_attn (its
+ * seq_lens are seq_lens_out and its block_table the updated table; the
+ * workspace is sized by kvc_attn_workspace_bytes).  On success outputs,
+ * table, head, slots, cache bytes and seq_lens_out are those of the two
+ * calls in order.  An allocation error (all or nothing, as in
+ * kvc_block_table_append) writes nothing but the head, the unchanged lengths
+ * and the status; the attention outputs are then unspecified.
+ */
+int kvc_block_table_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                                int32_t max_new, int32_t* block_table, const int32_t* free_list,
+                                const int32_t* free_head_in, int32_t* free_head_out,
+                                int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                int32_t* seq_lens_out, const void* q, int32_t n_q, float scale,
+                                void* out, int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_status, void* stream);
+
+/*
  * kvc_decode_attn -- one new query row per sequence attends over all of its
  * seq_lens[b] cached keys (its own key already appended), no mask.
  *

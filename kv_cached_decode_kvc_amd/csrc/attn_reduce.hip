@@ -37,6 +37,16 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   long ml_step, o_step;
   float early[kEarly][CPL];
   float2 mine_raw = make_float2(-INFINITY, 0.f);
+  // stream-K: the segment's worker record, requested with the length (its
+  // address does not depend on it), so the partials wait one round trip
+  const int g_sk = p.sk_meta ? h / p.G : 0;
+  const int i_sk = p.sk_meta ? r * p.G + h % p.G : 0;  // row of the KV head's rows
+  const long seg_sk = p.sk_meta ? ((long)b * p.Hkv + g_sk) *
+                                      ((p.G * p.n_q + p.rows_item - 1) / p.rows_item) +
+                                      i_sk / p.rows_item
+                                : 0;
+  int2 wr_raw = make_int2(0, -1);
+  if (p.sk_meta) wr_raw = p.sk_meta[seg_sk];
   int code;
   const int L = attended_len(p.seq_lens, p.cu_new, p.total_new, b, p.n_q, p.cap, &code);
   const bool valid = L >= 0;
@@ -71,17 +81,12 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
         for (int c = 0; c < CPL; ++c) early[j][c] = j < n ? po[(long)j * D + c] : 0.f;
     }
   } else {
-    const int g = h / p.G;
-    const int i = r * p.G + h % p.G;  // row of the KV head's rows
-    const int n_rb = (p.G * p.n_q + p.rows_item - 1) / p.rows_item;
-    const long seg = ((long)b * p.Hkv + g) * n_rb + i / p.rows_item;
-    int2 wr = make_int2(0, -1);
-    if (valid) wr = p.sk_meta[seg];
+    int2 wr = valid ? wr_raw : make_int2(0, -1);
     // a record that names workers outside the launch (a workspace the
     // partition kernel did not fill) is not followed
     if (wr.x < 0 || wr.y < wr.x || wr.y >= p.sk_workers) wr = make_int2(0, -1);
     n = valid ? wr.y - wr.x + 1 : 0;
-    const long first = (seg + wr.x) * p.sk_rows + i % p.rows_item;  // workspace row of piece 0
+    const long first = (seg_sk + wr.x) * p.sk_rows + i_sk % p.rows_item;  // workspace row of piece 0
     ml = reinterpret_cast<const float2*>(p.ws_ml) + first;
     po = p.ws_o + first * D + lane * CPL;
     ml_step = p.sk_rows;

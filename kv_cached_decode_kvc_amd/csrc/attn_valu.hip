@@ -146,15 +146,15 @@ struct Elem<Fp8<F>> {  // FP8 codes: a 16-byte load holds 16 elements; q is 16 b
   }
 };
 
-// AP: an append fused into the launch (contiguous caches, not FP8): the new
-// rows of a sequence come from k_new / v_new and are written into the cache
-// (AttnParams::cu_new).
+// AP: an append fused into the launch (not FP8; AttnParams::cu_new): the new
+// rows of a sequence come from k_new / v_new and are written into the cache.
+// 1: a contiguous cache; 2: a paged cache, block table included.
 // Wavefronts per SIMD the FP8 forms keep room for (measured best; the fused
 // combine would otherwise cost them one).
 template <typename T, int D>
 constexpr int valu_min_waves() { return IsFp8<T>::kFormat == 0 ? 1 : D == 128 ? 5 : 6; }
 
-template <typename T, int D, bool AP>
+template <typename T, int D, int AP>
 __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(AttnParams p) {
   using S = ValuShape<T, D>;
   constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
@@ -165,12 +165,77 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
   if (!wi.live) return;
   const int b = wi.b, part = wi.part, r = wi.u % p.n_q, h = wi.u / p.n_q;
 
+  // paged cache with the block table fused in: the work item of the last
+  // query row of the sequence's first head and first partition does the
+  // sequence's bookkeeping (new table entries, slots, new rows, length;
+  // sequence 0 the free-list head) from its own scan of the batch, after
+  // its attention work (nothing in this launch waits for it: the tiles read
+  // new rows from k_new / v_new), where the loop's registers are free
+  constexpr bool paged_ap = AP == 2;
+  auto bookkeeping = [&]() {
+    const AllocScan as = alloc_scan(p.seq_lens, p.cu_new, p.head_in, p.B, p.bs, p.max_blocks,
+                                    p.N, b);
+    const int len = p.seq_lens[b], c0b = p.cu_new[b], n = p.cu_new[b + 1] - c0b;
+    if (as.err != 0) {  // all or nothing: only the head, the lengths and the status
+      if (lane == 0) {
+        p.seq_lens_out[b] = len;
+        if (b == 0) {
+          report(p.status, as.err);
+          *p.head_out = as.head;
+        }
+      }
+    } else {
+      const int have = (len + p.bs - 1) / p.bs;
+      const int need = (int)(((long)len + n + p.bs - 1) / p.bs) - have;
+      const int first = as.head + as.before;
+      int32_t* trow_out = p.table_out + (long)b * p.max_blocks;
+      for (int j = lane; j < need; j += kWave) trow_out[have + j] = p.free_list[first + j];
+      if (n > 0 && c0b + n <= p.total_new) {
+        for (int t = lane; t < n; t += kWave) {
+          const int pos = len + t, lb = pos / p.bs;
+          const long blk = lb < have ? p.table[(long)b * p.max_blocks + lb]
+                                     : p.free_list[first + lb - have];
+          p.slots[c0b + t] = (int32_t)(blk * p.bs + pos % p.bs);
+        }
+        // the sequence's new rows into their slots, token by token (the
+        // block once per token), 16 bytes per lane and four chunks in flight
+        // (the tiles of this launch read the rows from k_new / v_new)
+        constexpr int CH = D * (int)sizeof(T) / 16;  // 16-byte chunks of a row
+        const int per_tok = p.Hkv * CH;
+        for (int t = 0; t < n; ++t) {
+          const int pos = len + t, lb = pos / p.bs;
+          const long blk = __builtin_amdgcn_readfirstlane(
+              lb < have ? p.table[(long)b * p.max_blocks + lb] : p.free_list[first + lb - have]);
+          if (blk < 0 || blk >= p.N) {
+            if (lane == 0) report(p.status, KVC_ERR_DATA);
+            continue;
+          }
+          const uint4* ks = reinterpret_cast<const uint4*>(p.k_new) + (long)(c0b + t) * per_tok;
+          const uint4* vs = reinterpret_cast<const uint4*>(p.v_new) + (long)(c0b + t) * per_tok;
+          uint4* kd = reinterpret_cast<uint4*>(p.k_out) + (blk * p.Hkv * p.bs + pos % p.bs) * CH;
+          uint4* vd = reinterpret_cast<uint4*>(p.v_out) + (blk * p.Hkv * p.bs + pos % p.bs) * CH;
+#pragma unroll 4
+          for (int x = lane; x < per_tok; x += kWave) {  // chunk x: head x / CH, piece x % CH
+            const long dst = (long)(x / CH) * p.bs * CH + x % CH;
+            kd[dst] = ks[x];
+            vd[dst] = vs[x];
+          }
+        }
+      }
+      if (lane == 0) {
+        p.seq_lens_out[b] = len + n;
+        if (b == 0) *p.head_out = as.head + as.total;
+      }
+    }
+    };
+  const bool book = paged_ap && part == 0 && h == 0 && r == p.n_q - 1;
   int code;
   const int L = attended_len(p.seq_lens, p.cu_new, p.total_new, b, p.n_q, p.cap, &code);
-  const bool writer = AP && part == 0 && h == 0 && r == p.n_q - 1 && lane == 0;
+  const bool writer = AP && !paged_ap && part == 0 && h == 0 && r == p.n_q - 1 && lane == 0;
   if (L < 0) {
     if (part == 0 && h == 0 && r == 0 && lane == 0) report(p.status, code);
     if (writer) p.seq_lens_out[b] = p.seq_lens[b];  // a refused append keeps the length
+    if (book) bookkeeping();
     if (p.cnt && part == 0 && lane * 4 < D) {  // combine fused in: the row's output is zeros
       const float z[4] = {0.f, 0.f, 0.f, 0.f};
       store_out<4>(p.out, p.out_bf16, (((long)b * p.n_q + r) * p.Hq + h) * D + lane * 4, z);
@@ -183,7 +248,7 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
   // last query row of the KV head's first query head, which sees them all
   const int len0 = AP ? p.seq_lens[b] : L;
   const int c0 = AP ? p.cu_new[b] : 0;
-  const bool app_writer = AP && r == p.n_q - 1 && h % p.G == 0;
+  const bool app_writer = AP && !paged_ap && r == p.n_q - 1 && h % p.G == 0;
   const int nparts = (L + p.P - 1) / p.P;
   if (part >= nparts) return;
   const int start = part * kTile;              // first tile of this partition
@@ -206,11 +271,14 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
     const typename Elem<T>::Q qv =
         Elem<T>::load_q(p.q, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
     // paged: lane i holds the block of the partition's tile number j * 64 + i
+    // (with the block table fused in, only tiles that start below the old
+    // length have one yet: the rest are new rows, read from k_new / v_new)
     const bool paged = p.table != nullptr;
     const int32_t* trow = paged ? p.table + (long)b * p.max_blocks : nullptr;
+    const int id_end = paged_ap ? min(end, len0) : end;
     auto load_ids = [&](int j) -> int {
       const int tk = start + (j * kWave + lane) * stride;
-      return tk < end ? trow[tk / p.bs] : 0;
+      return tk < id_end ? trow[tk / p.bs] : 0;
     };
     int ids = 0, ids_next = 0;
     if (paged) {
@@ -240,11 +308,14 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
             if (start + (ii + kWave) * stride < end) ids_next = load_ids(ii / kWave + 1);
           }
           const int blk = __builtin_amdgcn_readlane(ids, ii & (kWave - 1));
-          if (blk < 0 || blk >= p.N) {
+          if (paged_ap && ti >= len0) {
+            row0 = 0;  // every row of the tile is new: none is read from the cache
+          } else if (blk < 0 || blk >= p.N) {
             if (lane == 0) report(p.status, KVC_ERR_DATA);
             continue;
+          } else {
+            row0 = ((long)blk * p.Hkv + g) * p.bs + (ti % p.bs);
           }
-          row0 = ((long)blk * p.Hkv + g) * p.bs + (ti % p.bs);
         }
         nvalid[i] = min(kTile, end - ti);  // >= 1
 #pragma unroll
@@ -350,6 +421,8 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
     }
   }
 
+  if (book) bookkeeping();
+
   // Combine fused in: the row's last partition to finish merges the row's
   // partials and writes the row.  Lane (r0, c) takes partitions r0, r0 +
   // RPL, ... for its columns, and the row groups merge by shuffles.  Every
@@ -405,30 +478,41 @@ hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) 
   if (n_wg == 0) return hipSuccess;
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_wg), block(64);
-  if (p.cu_new) {  // fused append: bf16 and fp32 contiguous caches
+  if (p.cu_new) {  // fused append (bf16 and fp32 caches): contiguous, or paged with the table
+    const bool pg = p.free_list != nullptr;
     if (dtype == KVC_BF16) {
-      if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((partition_valu<uint16_t, 64, true>), grid, block, 0, s, p);
+      if (p.D == 128) {
+        if (pg) hipLaunchKernelGGL((partition_valu<uint16_t, 128, 2>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((partition_valu<uint16_t, 128, 1>), grid, block, 0, s, p);
+      } else {
+        if (pg) hipLaunchKernelGGL((partition_valu<uint16_t, 64, 2>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((partition_valu<uint16_t, 64, 1>), grid, block, 0, s, p);
+      }
     } else if (dtype == KVC_F32) {
-      if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((partition_valu<float, 64, true>), grid, block, 0, s, p);
+      if (p.D == 128) {
+        if (pg) hipLaunchKernelGGL((partition_valu<float, 128, 2>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((partition_valu<float, 128, 1>), grid, block, 0, s, p);
+      } else {
+        if (pg) hipLaunchKernelGGL((partition_valu<float, 64, 2>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((partition_valu<float, 64, 1>), grid, block, 0, s, p);
+      }
     } else {
       return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   if (dtype == KVC_BF16) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<uint16_t, 64, false>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<uint16_t, 128, 0>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<uint16_t, 64, 0>), grid, block, 0, s, p);
   } else if (dtype == KVC_FP8_E4M3) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 128, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 64, false>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 128, 0>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E4M3>, 64, 0>), grid, block, 0, s, p);
   } else if (dtype == KVC_FP8_E5M2) {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 128, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 64, false>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 128, 0>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<Fp8<kFp8E5M2>, 64, 0>), grid, block, 0, s, p);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((partition_valu<float, 64, false>), grid, block, 0, s, p);
+    if (p.D == 128) hipLaunchKernelGGL((partition_valu<float, 128, 0>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((partition_valu<float, 64, 0>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

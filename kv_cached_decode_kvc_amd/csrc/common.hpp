@@ -55,6 +55,19 @@ struct AttnParams {
   void* v_out;
   int32_t* seq_lens_out;
   int total_new;
+  // Block table fused in as well (paged cache with cu_new; free_list != NULL):
+  // sequence b's new rows go to the blocks its table already holds (the
+  // partly filled last one) or to blocks taken from the free list at
+  // *head_in + (new blocks of the sequences before b), all or nothing, as
+  // kvc_block_table_append does it; table_out (the same table as `table`),
+  // head_out, slots and seq_lens_out receive its outputs.  The partition's
+  // tiles never read a table entry this launch writes: rows from the old
+  // length on come from k_new / v_new.
+  const int32_t* free_list;
+  const int32_t* head_in;
+  int32_t* head_out;
+  int32_t* table_out;
+  int32_t* slots;
   // Combine fused into the partition launch of the vector-ALU kernel (cnt ==
   // NULL: the reduce kernel combines).  cnt[row] counts the row's finished
   // partitions; the one that completes the row merges all of its partials
@@ -114,6 +127,50 @@ __device__ __forceinline__ bool arrive_last(uint32_t* cnt, long unit, int n) {
   if ((threadIdx.x & (kWave - 1)) == 0)
     __hip_atomic_store(cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+
+// One wavefront's scan of a block-table step over the whole batch: the new
+// blocks of every sequence (total) and of the sequences before b (before),
+// the free-list head, and the step's error, all or nothing as in the block
+// table ("Inference-1", PagedAttention: blocks on demand when the last one
+// is full): KVC_ERR_DATA for a negative length or count, KVC_ERR_CAPACITY for
+// a sequence past max_blocks, KVC_ERR_NO_BLOCKS for too few free blocks.
+// Every lane must call it; the result is wave-uniform.
+struct AllocScan {
+  int head, total, before, err;
+};
+__device__ __forceinline__ AllocScan alloc_scan(const int32_t* seq_lens, const int32_t* cu_new,
+                                                const int32_t* head_in, int B, int bs,
+                                                int max_blocks, int N, int b) {
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  int total = 0, before = 0, bad = 0, over = 0;
+  for (int i = lane; i < B; i += kWave) {
+    const int len = seq_lens[i], n = cu_new[i + 1] - cu_new[i];
+    if (len < 0 || n < 0) {
+      bad = 1;
+      continue;
+    }
+    const long have = ((long)len + bs - 1) / bs, want = ((long)len + n + bs - 1) / bs;
+    if (want > max_blocks) {
+      over = 1;
+      continue;
+    }
+    total += (int)(want - have);
+    if (i < b) before += (int)(want - have);
+  }
+  for (int m = 1; m < kWave; m <<= 1) {
+    total += __shfl_xor(total, m);
+    before += __shfl_xor(before, m);
+  }
+  AllocScan s;
+  s.head = __builtin_amdgcn_readfirstlane(*head_in);
+  s.total = __builtin_amdgcn_readfirstlane(total);
+  s.before = __builtin_amdgcn_readfirstlane(before);
+  s.err = __any(bad) ? KVC_ERR_DATA
+          : __any(over) ? KVC_ERR_CAPACITY
+          : (s.head < 0 || (long)s.head + s.total > N) ? KVC_ERR_NO_BLOCKS
+          : 0;
+  return s;
 }
 
 // Online merge of partial (mj, lj, oj[0..N)) into (m, d, acc): the partials'

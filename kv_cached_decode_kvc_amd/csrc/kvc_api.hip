@@ -577,6 +577,66 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
                     stream);
 }
 
+int kvc_block_table_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens, const int32_t* cu_new, int32_t total_new,
+                                int32_t max_new, int32_t* block_table, const int32_t* free_list,
+                                const int32_t* free_head_in, int32_t* free_head_out,
+                                int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                int32_t* seq_lens_out, const void* q, int32_t n_q, float scale,
+                                void* out, int32_t out_dtype, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (d->block_size == 0) return KVC_ERR_ARG;  // contiguous caches: kvc_append_attn
+  if (total_new < 0 || max_new < 0) return KVC_ERR_ARG;
+  if (out_dtype != KVC_BF16 && out_dtype != KVC_F32) return KVC_ERR_UNSUPPORTED;
+  if (d->batch > kMaxFusedBatch) return KVC_ERR_UNSUPPORTED;
+  Plan pl{};
+  // the attention's checks, on the lengths after the append
+  st = check_attn(d, n_q, q, k_cache, v_cache, seq_lens_out, block_table, scale, workspace,
+                  workspace_bytes, &pl);
+  if (st != KVC_OK) return st;
+  if (d->batch == 0) return total_new == 0 ? KVC_OK : KVC_ERR_ARG;
+  if (!seq_lens || !cu_new || !free_list || !free_head_in || !free_head_out || !out ||
+      seq_lens_out == seq_lens)
+    return KVC_ERR_ARG;
+  if (total_new > 0 && (!k_new || !v_new || !slot_mapping)) return KVC_ERR_ARG;
+  if (!pl.mfma && !fp8_format(d)) {
+    // one partition launch takes the blocks, appends and attends (the
+    // combine inside it too, or a reduce over the same lengths)
+    AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
+                               workspace, dev_status, out, out_dtype);
+    p.cu_new = cu_new;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.k_out = k_cache;
+    p.v_out = v_cache;
+    p.seq_lens_out = seq_lens_out;
+    p.total_new = total_new;
+    p.free_list = free_list;
+    p.head_in = free_head_in;
+    p.head_out = free_head_out;
+    p.table_out = block_table;
+    p.slots = slot_mapping;
+    st = hip_status(launch_partition_valu(p, d->dtype, (hipStream_t)stream));
+    if (st != KVC_OK || p.cnt) return st;
+    ReduceParams r = reduce_params(d, pl, n_q, d->head_dim, seq_lens, workspace, out, dev_status);
+    r.cu_new = cu_new;
+    r.total_new = total_new;
+    return hip_status(launch_reduce(r, out_dtype, (hipStream_t)stream));
+  }
+  // grouped rows or FP8: block table and append in one launch, then attention
+  st = kvc_block_table_append(d, k_new, v_new, seq_lens, cu_new, total_new, max_new, block_table,
+                              free_list, free_head_in, free_head_out, slot_mapping, k_cache,
+                              v_cache, seq_lens_out, dev_status, stream);
+  if (st != KVC_OK) return st;
+  st = run_partition(d, pl, q, n_q, k_cache, v_cache, seq_lens_out, block_table, scale, workspace,
+                     dev_status, stream, out, out_dtype);
+  if (st != KVC_OK || pl.fused) return st;
+  return run_reduce(d, pl, n_q, d->head_dim, seq_lens_out, workspace, out, out_dtype, dev_status,
+                    stream);
+}
+
 int kvc_attn_partition(const kvc_cache_desc* d, const void* q, int32_t n_q, const void* k_cache,
                        const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
                        float scale, void* workspace, size_t workspace_bytes, int32_t* dev_status,

@@ -29,7 +29,7 @@ EXPORTS = ("kvc_block_table", "kvc_append", "kvc_decode_attn", "kvc_verify_attn"
            "kvc_attn_partition_tokens", "kvc_attn_launches", "kvc_cache_bytes",
            "kvc_mla_workspace_bytes", "kvc_mla_partition_tokens", "kvc_mla_attn_partition", "kvc_mla_attn_reduce",
            "kvc_mla_attn", "kvc_prefill_attn", "kvc_status_string", "kvc_verify_attn_noalloc",
-           "kvc_block_table_append", "kvc_append_attn")
+           "kvc_block_table_append", "kvc_append_attn", "kvc_block_table_append_attn")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KVC_NOALLOC_SCRATCH_BYTES
 
 
@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.kvc_append_attn.argtypes = [D, P, P, P, P, I, I, P, P, P, P, I, ctypes.c_float, P, I, P,
                                       ctypes.c_size_t, P, P]
         L.kvc_append_attn.restype = ctypes.c_int
+        L.kvc_block_table_append_attn.argtypes = [D, P, P, P, P, I, I, P, P, P, P, P, P, P, P, P,
+                                                  I, ctypes.c_float, P, I, P, ctypes.c_size_t, P,
+                                                  P]
+        L.kvc_block_table_append_attn.restype = ctypes.c_int
         L.kvc_verify_attn_noalloc.argtypes = [D, P, I, P, P, P, P, ctypes.c_float, P, I, P, P]
         L.kvc_verify_attn_noalloc.restype = ctypes.c_int
         L.kvc_attn_reduce.argtypes = [D, I, P, P, ctypes.c_size_t, P, I, P, P]
@@ -216,6 +220,22 @@ def kvc_append_attn(desc, k_new, v_new, seq_lens, cu_new, total_new, max_new, k_
         _ptr(out, "out"), _out_dtype(out, out_dtype), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(dev_status, "dev_status", I32),
         _stream(stream)))
+
+
+def kvc_block_table_append_attn(desc, k_new, v_new, seq_lens, cu_new, total_new, max_new,
+                                block_table, free_list, free_head_in, free_head_out, slot_mapping,
+                                k_cache, v_cache, seq_lens_out, q, n_q, scale, out, workspace,
+                                dev_status=None, stream=None, out_dtype=None):
+    _check("kvc_block_table_append_attn", lib().kvc_block_table_append_attn(
+        ctypes.byref(desc), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"),
+        _ptr(seq_lens, "seq_lens", I32), _ptr(cu_new, "cu_new", I32), int(total_new),
+        int(max_new), _ptr(block_table, "block_table", I32), _ptr(free_list, "free_list", I32),
+        _ptr(free_head_in, "free_head_in", I32), _ptr(free_head_out, "free_head_out", I32),
+        _ptr(slot_mapping, "slot_mapping", I32), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(seq_lens_out, "seq_lens_out", I32), _ptr(q, "q"),
+        int(n_q), float(scale), _ptr(out, "out"), _out_dtype(out, out_dtype),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(dev_status, "dev_status", I32), _stream(stream)))
 
 
 def kvc_verify_attn_noalloc(desc, q, n_q, k_cache, v_cache, seq_lens, block_table, scale, out,

@@ -2,10 +2,10 @@
 
 ``LayerCache`` owns the device buffers of a workload (cache or block pool,
 block table, free list, lengths, workspace) and runs the decode step the way a
-serving loop would: ``kvc_block_table_append`` (paged caches) ->
-``kvc_verify_attn`` (one launch: the partition kernel combines its own
-partials), or, for a contiguous cache, ``kvc_append_attn`` (append and
-attention in one call).  The two-stage calls ``kvc_attn_partition`` ->
+serving loop would: ``kvc_block_table_append_attn`` (paged caches: block
+table, append and attention in one call) or ``kvc_append_attn`` (contiguous);
+each runs as few launches as the library can (one for small multi-head
+batches).  The two-stage calls ``kvc_attn_partition`` ->
 ``kvc_attn_reduce`` remain available for timing the stages apart.  Every step of the computation
 runs in the library's kernels; this module only allocates tensors with torch
 and passes their addresses.
@@ -259,16 +259,23 @@ class LayerCache:
 
     @property
     def fused_step(self) -> bool:
-        """Contiguous decode / verify: the append runs inside the attention call
-        (kvc_append_attn)."""
-        return self.bs == 0 and not self.w.dv and not self.w.prefill
+        """Decode / verify: the append (and, paged, the block table) runs inside
+        the attention call (kvc_append_attn, kvc_block_table_append_attn)."""
+        return not self.w.dv and not self.w.prefill
 
     def step(self):
         if self.fused_step:
             w = self.w
-            kvc.kvc_append_attn(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu,
-                                self.s_total, w.n_q, self.k, self.v, self.s_len1, self.s_q, w.n_q,
-                                self.scale, self.s_out, self.s_ws, self.status)
+            if self.bs:
+                kvc.kvc_block_table_append_attn(
+                    self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu, self.s_total, w.n_q,
+                    self.table, self.free_list, self.s_head0, self.s_head1, self.s_slots, self.k,
+                    self.v, self.s_len1, self.s_q, w.n_q, self.scale, self.s_out, self.s_ws,
+                    self.status)
+            else:
+                kvc.kvc_append_attn(self.desc, self.s_k, self.s_v, self.s_len0, self.s_cu,
+                                    self.s_total, w.n_q, self.k, self.v, self.s_len1, self.s_q,
+                                    w.n_q, self.scale, self.s_out, self.s_ws, self.status)
             return self.s_out
         self.step_front()
         self.step_attn()
@@ -303,6 +310,13 @@ class DecodeLoop:
     def run(self):
         lc, w = self.lc, self.w
         for s in range(self.S):
+            if lc.bs and lc.fused_step:
+                kvc.kvc_block_table_append_attn(
+                    lc.desc, self.k[s], self.v[s], self.lens[s], self.cu, self.total, w.n_q,
+                    lc.table, lc.free_list, self.heads[s], self.heads[s + 1], self.slots[s], lc.k,
+                    lc.v, self.lens[s + 1], self.q[s], w.n_q, lc.scale, self.out[s], self.ws,
+                    lc.status)
+                continue
             if lc.bs:
                 kvc.kvc_block_table_append(lc.desc, self.k[s], self.v[s], self.lens[s], self.cu,
                                            self.total, w.n_q, lc.table, lc.free_list,
