@@ -375,17 +375,19 @@ __global__ __launch_bounds__(kMlaThreads, C == 1 ? 1 : 2) void partition_mla(Att
 // a SIMD and split the work evenly:
 //   scores: each half multiplies the tile by its half of the absorbed query
 //           (9 of the 18 steps of 32 along the 576 dims, so a wavefront holds
-//           36 query registers), the two 16 x 16 partial sums meet in LDS,
-//           and each half adds them (the same sum in both: a + b = b + a) and
-//           runs the same online softmax, so both hold the weights and the
-//           statistics without sending them;
+//           36 query registers), the two 16 x 16 partial sums of each 16-key
+//           half meet in LDS, and each half adds them (the same sum in both:
+//           a + b = b + a) and runs the same online softmax, so both hold the
+//           weights and the statistics without sending them;
 //   values: each half accumulates 256 of the 512 output columns.
 // A wavefront's accumulators (64 registers) and its other state then fit the
 // 256 vector registers of two wavefronts per SIMD.  (The one-wavefront form
 // held 16 rows x 512 columns in the accumulation registers, where the
 // compiler moved them on every tile, and left a lone wavefront per SIMD to
-// hide every latency.)  Tile n + 1's partial scores are issued alongside tile
-// n's value products; its softmax follows the barrier that publishes them.
+// hide every latency.)  A step covers 32 keys (two 16-key halves, each with
+// its own block id), so the two barriers of a step serve twice the keys of a
+// 16-key tile; tile n + 1's partial scores are issued alongside tile n's
+// value products, and its softmax follows the barrier that publishes them.
 constexpr int kPairWaves = 8;
 constexpr int kPairThreads = kPairWaves * kWave;
 
@@ -397,12 +399,14 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
   constexpr int KK = DK / 32;             // 18 QK^T steps
   constexpr int KH = KK / 2;              // 9 steps per half
   constexpr int DT = DV / 16 / 2;         // 16 output column tiles per half
+  constexpr int TK = 2 * kTile;           // 32 keys per tile: two 16-key halves
   constexpr int CPR = DK * 2 / 16;        // 72 16-byte chunks per row
-  constexpr int TCH = kTile * CPR;        // 1152 chunks per tile
+  constexpr int TCH = TK * CPR;           // 2304 chunks per tile
   constexpr int PER = (TCH + kPairThreads - 1) / kPairThreads;  // chunks per thread
   constexpr int ROWB = DK * 2 + 16;       // padded LDS row
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTile * ROWB];
-  __shared__ __attribute__((aligned(16))) f32x4_t s_ps[2][4][2][kWave];  // partial scores
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][TK * ROWB];
+  // partial scores: [slot][row block][half of the reduction][16-key half]
+  __shared__ __attribute__((aligned(16))) f32x4_t s_ps[2][4][2][2][kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -428,8 +432,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
     if (rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
     return;  // whole workgroup
   }
+  // partition part of n owns the 32-key tiles part, part + n, ...
   const int nparts = (L + P - 1) / P;
-  const int start = part * kTile, stride = nparts * kTile, end = L;
+  const int start = part * TK, stride = nparts * TK, end = L;
 
   // this wavefront's rows: i = r * Hq + h
   const int i_row = (rg * 4 + rbw) * 16 + col;
@@ -456,20 +461,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;  // running statistics of row col (the same in both halves)
 
-  const int n_tiles = (end - start + stride - 1) / stride;  // <= kMlaMaxTiles (plan)
+  const int n_tiles = (end - start + stride - 1) / stride;  // 2 * n_tiles <= kMlaMaxTiles (plan)
   const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  // block ids of each 16-key half of the partition's tiles (a 32-key tile
+  // may span two blocks of 16)
   __shared__ int s_blk[kMlaMaxTiles];
   if (p.table != nullptr) {
-    for (int n = tid; n < n_tiles; n += kPairThreads)
-      s_blk[n] = p.table[(long)b * p.max_blocks + ((start + n * stride) >> bs_shift)];
+    for (int x = tid; x < 2 * n_tiles; x += kPairThreads) {
+      const int key = start + (x >> 1) * stride + (x & 1) * kTile;
+      s_blk[x] = key < end ? p.table[(long)b * p.max_blocks + (key >> bs_shift)] : 0;
+    }
   }
   __syncthreads();
-  auto tile_base = [&](int n) -> long {  // element offset of tile n's first key; -1: bad block
-    const int tile = start + n * stride;
-    if (p.table == nullptr) return ((long)b * p.S_max + tile) * DK;
-    const int blk = s_blk[n];
+  // element offset of key `key` (a multiple of 16) whose half is s_blk[x]; -1: bad block
+  auto half_base = [&](int key, int x) -> long {
+    if (p.table == nullptr) return ((long)b * p.S_max + key) * DK;
+    const int blk = s_blk[x];
     if (blk < 0 || blk >= p.N) return -1;
-    return ((long)blk * p.bs + (tile & (p.bs - 1))) * DK;
+    return ((long)blk * p.bs + (key & (p.bs - 1))) * DK;
   };
   int frow[PER];
   uint32_t fchk[PER];
@@ -480,19 +489,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
     fchk[u] = (uint32_t)(idx % CPR) * 16;
   }
   uint4 stage[PF][PER];
-  long stb[PF];
+  bool sok[PF];
   // every stage issues PER loads whatever the tile (clamped rows), so the
-  // compiler can wait for one stage at a time
-  auto fetch = [&](uint4 (&st)[PER], long& tbs, int n) {
+  // compiler can wait for one stage at a time; rows 16..31 come from the
+  // second half's block
+  auto fetch = [&](uint4 (&st)[PER], bool& ok, int n) {
     const int tile = start + n * stride;
     const bool in = tile < end;
-    const long tb = tile_base(in ? n : 0);
-    tbs = in ? tb : -1;
-    const uint8_t* base = (const uint8_t*)p.k + (tbs >= 0 ? tb : 0) * 2;
-    const int last = tbs >= 0 ? min(kTile, end - tile) - 1 : 0;
+    const long b0 = in ? half_base(tile, 2 * n) : 0;
+    const long b1 = in && tile + kTile < end ? half_base(tile + kTile, 2 * n + 1) : b0;
+    ok = in && b0 >= 0 && b1 >= 0;
+    const int last = ok ? min(TK, end - tile) - 1 : 0;
+    const long c0 = ok ? b0 : 0, c1 = ok ? b1 - (long)kTile * DK : 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      st[u] = load_stream(base + ((uint32_t)min(frow[u], last) * (DK * 2) + fchk[u]));
+    for (int u = 0; u < PER; ++u) {
+      const int row = min(frow[u], last);
+      const long c = row >= kTile ? c1 : c0;
+      st[u] = load_stream((const uint8_t*)p.k + (c + (long)row * DK) * 2 + fchk[u]);
+    }
   };
   auto store_tile = [&](int buf, const uint4 (&st)[PER]) {
 #pragma unroll
@@ -503,34 +517,44 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
     }
   };
   constexpr float kLazy = 8.f;
-  // this half's partial S^T of the tile in `buf` (lane: keys grp*4 .. +3 of
-  // row col), published in slot `sl`
+  // this half's partial S^T of the tile in `buf`, both 16-key halves (lane:
+  // keys kh*16 + grp*4 .. +3 of row col), published in slot `sl`
   auto qk_half = [&](int buf, int sl) {
-    const uint8_t* ka = lds[buf] + col * ROWB + grp * 16 + half * KH * 64;
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    bf16x8_t kf[KH];
 #pragma unroll
-    for (int k = 0; k < KH; ++k)
-      kf[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + k * 64));
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint8_t* ka = lds[buf] + (kh * kTile + col) * ROWB + grp * 16 + half * KH * 64;
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      bf16x8_t kf[KH];
 #pragma unroll
-    for (int k = 0; k < KH; ++k) {
-      if (k & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s1, 0, 0, 0);
-      else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s0, 0, 0, 0);
+      for (int k = 0; k < KH; ++k)
+        kf[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ka + k * 64));
+#pragma unroll
+      for (int k = 0; k < KH; ++k) {
+        if (k & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s1, 0, 0, 0);
+        else s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], qf[k], s0, 0, 0, 0);
+      }
+      s_ps[sl][rbw][half][kh][lane] = s0 + s1;
     }
-    s_ps[sl][rbw][half][lane] = s0 + s1;
   };
-  // the whole scores of slot `sl` (half 0's part + half 1's part), online
-  // softmax: the weights (bf16 hi + lo) and the factor the accumulators must
-  // be rescaled by; rescale is wave-uniform
+  // the whole scores of slot `sl` (half 0's part + half 1's part), one
+  // online-softmax step over the tile's 32 keys: the weights of each 16-key
+  // half (bf16 hi + lo) and the factor the accumulators must be rescaled by;
+  // rescale is wave-uniform
   float alpha = 1.f;
   bool rescale = false;
-  auto softmax = [&](int sl, int tile, bool ok) -> bf16x8_t {
-    const f32x4_t s = s_ps[sl][rbw][0][lane] + s_ps[sl][rbw][1][lane];
-    const int key0 = tile + grp * 4;
-    float sv[4];
+  bf16x8_t pb[2] = {};
+  auto softmax = [&](int sl, int tile, bool ok) {
+    float sv[2][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sv[v] = ok && key0 + v < lvis ? s[v] * p.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    for (int kh = 0; kh < 2; ++kh) {
+      const f32x4_t s = s_ps[sl][rbw][0][kh][lane] + s_ps[sl][rbw][1][kh][lane];
+      const int key0 = tile + kh * kTile + grp * 4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        sv[kh][v] = ok && key0 + v < lvis ? s[v] * p.scale_log2 : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool move = mx > m + kLazy;
@@ -539,59 +563,67 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
     alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
     m = m_new;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const f32x2_t p01 = {fast_exp2(sv[0] - m_use), fast_exp2(sv[1] - m_use)};
-    const f32x2_t p23 = {fast_exp2(sv[2] - m_use), fast_exp2(sv[3] - m_use)};
-    l = l * alpha + ((p01[0] + p01[1]) + (p23[0] + p23[1]));
-    const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
-    const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
-    const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
-    const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
-    return __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
-                                   __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
-                                   0, 1, 2, 3, 4, 5, 6, 7);
+    float lsum = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const f32x2_t p01 = {fast_exp2(sv[kh][0] - m_use), fast_exp2(sv[kh][1] - m_use)};
+      const f32x2_t p23 = {fast_exp2(sv[kh][2] - m_use), fast_exp2(sv[kh][3] - m_use)};
+      lsum += (p01[0] + p01[1]) + (p23[0] + p23[1]);
+      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t);
+      const bf16x2_t h23 = __builtin_convertvector(p23, bf16x2_t);
+      const bf16x2_t lo01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+      const bf16x2_t lo23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+      pb[kh] = __builtin_shufflevector(__builtin_shufflevector(h01, h23, 0, 1, 2, 3),
+                                       __builtin_shufflevector(lo01, lo23, 0, 1, 2, 3),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    l = l * alpha + lsum;
   };
-  // O^T += V^T . P^T over this half's 256 columns
-  auto pv = [&](int buf, const bf16x8_t& pb) {
-    const uint8_t* va_ptr =
-        lds[buf] + (grp * 4 + (col >> 2)) * ROWB + (col & 3) * 8 + half * (DV / 2) * 2;
-    constexpr int VG = 8;
-    auto read_v = [&](bf16x4_t (&va)[VG], int g) {
+  // O^T += V^T . P^T over this half's 256 columns, one 16-key half at a time
+  auto pv = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < VG; ++i) {
-        lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
-            (__attribute__((address_space(3))) uint8_t*)(va_ptr + (g * VG + i) * 32));
-        va[i] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint8_t* va_ptr = lds[buf] + (kh * kTile + grp * 4 + (col >> 2)) * ROWB +
+                              (col & 3) * 8 + half * (DV / 2) * 2;
+      constexpr int VG = 8;
+      auto read_v = [&](bf16x4_t (&va)[VG], int g) {
+#pragma unroll
+        for (int i = 0; i < VG; ++i) {
+          lds_i16x4_t* a = reinterpret_cast<lds_i16x4_t*>(
+              (__attribute__((address_space(3))) uint8_t*)(va_ptr + (g * VG + i) * 32));
+          va[i] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a));
+        }
+      };
+      bf16x4_t vcur[VG], vnext[VG];
+      read_v(vcur, 0);
+#pragma unroll
+      for (int g = 0; g < DT / VG; ++g) {
+        if (g + 1 < DT / VG) read_v(vnext, g + 1);
+#pragma unroll
+        for (int i = 0; i < VG; ++i) {
+          const bf16x8_t va2 = __builtin_shufflevector(vcur[i], vcur[i], 0, 1, 2, 3, 0, 1, 2, 3);
+          oacc[g * VG + i] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb[kh], oacc[g * VG + i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < VG; ++i) vcur[i] = vnext[i];
       }
-    };
-    bf16x4_t vcur[VG], vnext[VG];
-    read_v(vcur, 0);
-#pragma unroll
-    for (int g = 0; g < DT / VG; ++g) {
-      if (g + 1 < DT / VG) read_v(vnext, g + 1);
-#pragma unroll
-      for (int i = 0; i < VG; ++i) {
-        const bf16x8_t va2 = __builtin_shufflevector(vcur[i], vcur[i], 0, 1, 2, 3, 0, 1, 2, 3);
-        oacc[g * VG + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2, pb, oacc[g * VG + i], 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < VG; ++i) vcur[i] = vnext[i];
     }
   };
 
   // prologue: tiles 0 and 1 in LDS, tiles 2 .. PF + 1 in flight; tile 0's
   // weights in registers
 #pragma unroll
-  for (int k = 0; k < PF; ++k) fetch(stage[k], stb[k], k);
+  for (int k = 0; k < PF; ++k) fetch(stage[k], sok[k], k);
   store_tile(0, stage[0]);
   store_tile(1, stage[1]);
-  bool bok[2] = {stb[0] >= 0, stb[1] >= 0};
+  bool bok[2] = {sok[0], sok[1]};
   __syncthreads();
-  fetch(stage[0], stb[0], PF);
-  fetch(stage[1], stb[1], PF + 1);
+  fetch(stage[0], sok[0], PF);
+  fetch(stage[1], sok[1], PF + 1);
   if (active) qk_half(0, 0);
   __syncthreads();
-  bf16x8_t pb = {};
-  if (active) pb = softmax(0, start, bok[0]);
+  if (active) softmax(0, start, bok[0]);
   for (int n0 = 0; n0 < n_tiles; n0 += PF) {
 #pragma unroll
     for (int jj = 0; jj < PF; ++jj) {  // tile n in buffer j, tile n + 1 in buffer 1 - j
@@ -606,15 +638,15 @@ __global__ __launch_bounds__(kPairThreads, 1) void partition_mla_pair(AttnParams
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
           }
-          if (bok[j]) pv(j, pb);  // a bad block's tile holds no usable rows
+          if (bok[j]) pv(j);  // a bad block's tile holds no usable rows
         }
         if (!bok[j] && tid == 0) report(p.status, KVC_ERR_DATA);
       }
       __syncthreads();  // partial scores of tile n + 1 published; buffer j read
-      if (n < n_tiles && more && active) pb = softmax(1 - j, start + (n + 1) * stride, bok[1 - j]);
+      if (n < n_tiles && more && active) softmax(1 - j, start + (n + 1) * stride, bok[1 - j]);
       store_tile(j, stage[sg]);  // tile n + 2
-      bok[j] = stb[sg] >= 0;
-      fetch(stage[sg], stb[sg], n + 2 + PF);
+      bok[j] = sok[sg];
+      fetch(stage[sg], sok[sg], n + 2 + PF);
       __syncthreads();
     }
   }
