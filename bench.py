@@ -43,9 +43,8 @@ CSRC = os.path.join(ROOT, "kv_cached_decode_kvc_amd", "csrc")
 
 def kernel_of(w, mfma: bool) -> tuple[str, list[str]]:
     """Name of the dominant kernel and the sources that define it."""
-    if w.dv:  # up to 16 rows: four wavefronts; more: the eight-wavefront form
-        name = "partition_mla" if w.Hq * w.n_q <= 16 else "partition_mla_pair"
-        return name, ["attn_mla.hip", "common.hpp"]
+    if w.dv:
+        return "partition_mla", ["attn_mla.hip", "common.hpp"]
     if w.prefill:
         return "prefill_mfma", ["attn_prefill.hip", "common.hpp"]
     if mfma:

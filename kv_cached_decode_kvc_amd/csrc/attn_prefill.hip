@@ -126,6 +126,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
     wave_vis = max(wave_vis, lvis[nt]);
   }
   for (int m = 1; m < kWave; m <<= 1) wave_vis = max(wave_vis, __shfl_xor(wave_vis, m));
+  // a scalar: it decides a branch around matrix-core work, and those
+  // instructions do not honour the lane mask
+  wave_vis = __builtin_amdgcn_readfirstlane(wave_vis);
   // keys every valid row of this wavefront sees: tiles below it need no mask
   int vis_min = 0x7fffffff;
 #pragma unroll

@@ -186,10 +186,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
 // MLA latent decode: one bf16 latent head of 576 (512 latent + 64 RoPE key),
 // values = the 512-wide latent.  Up to 16 rows, a workgroup of four
-// wavefronts covers the 16 rows (C = 4 wavefronts split the output columns)
-// and two workgroups fit per CU; more rows, a workgroup of eight wavefronts
-// covers 64 rows and fills a CU (C = 1 here); so a round of resident work is
-// 512 or 256 workgroups.  The partition length grows in steps of 256
+// wavefronts covers the 16 rows and several workgroups fit per CU; more
+// rows, a workgroup of eight wavefronts covers 64 rows and fills a CU; a
+// round of resident work is 256 CUs times the workgroups per CU
+// (mla_wgs_per_cu).  The partition length grows in steps of 256
 // keys until a full-capacity batch fits in one round (a workgroup then
 // streams its partition without a second round behind it; two rounds
 // measured 10-12% slower), and halves (down to 64) while it would not fill
@@ -206,12 +206,11 @@ int check_mla(const kvc_cache_desc* d, int n_q, int value_dim) {
 Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   Plan pl{};
   const int R = d->num_q_heads * n_q;
-  const int C = mla_col_split(R);
-  const long rows_wg = 16L * (4 / C);  // four wavefronts, C per 16-row block
+  const long rows_wg = mla_rows_per_wg(R);
   const long n_rg = (R + rows_wg - 1) / rows_wg;
   const long units = (long)d->batch * n_rg;
   const int cap = capacity(d);
-  const long one_round = C == 1 ? 256 : 512;  // workgroups resident at once
+  const long one_round = 256L * mla_wgs_per_cu(R);  // workgroups resident at once
   if (d->partition_tokens > 0) {
     pl.P = d->partition_tokens;
   } else {

@@ -81,8 +81,9 @@ constexpr int kMlaValueDim = 512;  // the latent part, which also serves as the 
 
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s);
-// MLA: wavefronts sharing one 16-row block (each takes 512 / C output columns)
-int mla_col_split(int rows);
+// MLA: rows one workgroup covers, and workgroups resident per CU, for `rows` rows
+int mla_rows_per_wg(int rows);
+int mla_wgs_per_cu(int rows);
 hipError_t launch_prefill(const PrefillParams& p, int out_dtype, hipStream_t s);
 hipError_t launch_partition_mfma(const AttnParams& p, int rows_per_item, int fp8, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s);
