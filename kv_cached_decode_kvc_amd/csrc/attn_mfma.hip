@@ -276,8 +276,7 @@ __global__ __launch_bounds__(64, MINW) void partition_mfma(AttnParams p) {
               for (int v = 0; v < 4; ++v) sv[v] = key0 + v < lvis[nt] ? sv[v] : -INFINITY;
             }
             float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = rows_max(mx);
             const bool move = mx > m[nt] + kLazy;  // false while the row has no visible key
             if (__any(move)) {
               const float m_new = move ? mx : m[nt];

@@ -293,8 +293,7 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh)
       mx = fmaxf(mx, fmaxf(fmaxf(sv[kh][0], sv[kh][1]), fmaxf(sv[kh][2], sv[kh][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     const bool move = mx > m + kLazy;
     rescale = __any(move);
     const float m_new = move ? mx : m;
