@@ -16,6 +16,39 @@
 
 namespace kvc {
 
+namespace {
+
+// Sum and maximum over the 64 lanes, the same bits in every lane: DPP steps
+// within each 16-lane row, then gfx950's permlane swaps across rows (each
+// returns, per lane, itself and its partner across the swap), every step
+// combining a pair of values commutatively.  No step goes through LDS.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+// lane j's value in every lane (j uniform): a scalar read, no LDS round trip
+__device__ __forceinline__ float lane_value(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+
+}  // namespace
+
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   constexpr int CPL = D / kWave;  // columns per lane
@@ -111,7 +144,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     float mstar = mine.x;
     for (int q0 = kWave; q0 < nparts; q0 += kWave)  // more than 64 partitions
       if (q0 + lane < nparts) mstar = fmaxf(mstar, ml[(q0 + lane) * ml_step].x);
-    for (int m = 1; m < kWave; m <<= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, m));
+    mstar = wave_max(mstar);
     for (int q0 = 0; q0 < nparts; q0 += kWave) {
       float2 mq = q0 == 0 ? mine : make_float2(-INFINITY, 0.f);
       if (q0 > 0 && q0 + lane < nparts) mq = ml[(q0 + lane) * ml_step];
@@ -122,7 +155,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
       if (q0 == 0) {
 #pragma unroll
         for (int u = 0; u < kEarly; ++u) {
-          const float wj = __shfl(wq, u);  // 0 beyond nparts: those lanes hold weight 0
+          const float wj = lane_value(wq, u);  // 0 beyond nparts: those lanes hold weight 0
 #pragma unroll
           for (int c = 0; c < CPL; ++c) acc[c] += wj * early[u][c];
         }
@@ -136,18 +169,18 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
           for (int c = 0; c < CPL; ++c) o[u][c] = po[(q0 + j + u) * o_step + c];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float wj = __shfl(wq, j + u);
+          const float wj = lane_value(wq, j + u);
 #pragma unroll
           for (int c = 0; c < CPL; ++c) acc[c] += wj * o[u][c];
         }
       }
       for (; j < cnt; ++j) {
-        const float wj = __shfl(wq, j);
+        const float wj = lane_value(wq, j);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[c] += wj * po[(q0 + j) * o_step + c];
       }
     }
-    for (int m = 1; m < kWave; m <<= 1) den += __shfl_xor(den, m);
+    den = wave_sum(den);
   }
   if (!valid && lane == 0 && h == 0 && r == 0) report(p.status, code);
   if (valid && n == 0 && lane == 0) report(p.status, KVC_ERR_DATA);
