@@ -239,12 +239,9 @@ __device__ __forceinline__ float amax8(const uint4& x) {
 // into cache row `row`: the row's D/8 lanes (aligned, all active together)
 // reduce its largest magnitude, and the lane of piece 0 stores the scales.
 template <int F>
-__device__ __forceinline__ void quantize_piece(const AppendArgs& a, long src_tok, int g, int w,
-                                               int vec_per_head, long row) {
+__device__ __forceinline__ void quantize_store(const AppendArgs& a, const uint4& kx, const uint4& vx,
+                                               int w, int vec_per_head, long row) {
   using Fm = Fp8Format<F>;
-  const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
-  const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
-  const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
   float km = amax8(kx), vm = amax8(vx);
   for (int off = 1; off < vec_per_head; off <<= 1) {
     km = fmaxf(km, __shfl_xor(km, off));
@@ -259,6 +256,14 @@ __device__ __forceinline__ void quantize_piece(const AppendArgs& a, long src_tok
     *reinterpret_cast<float*>(a.k_cache + so) = ks;
     *reinterpret_cast<float*>(a.v_cache + so) = vs;
   }
+}
+template <int F>
+__device__ __forceinline__ void quantize_piece(const AppendArgs& a, long src_tok, int g, int w,
+                                               int vec_per_head, long row) {
+  const long src = (src_tok * a.Hkv + g) * a.head_bytes + w * 16;
+  const uint4 kx = *reinterpret_cast<const uint4*>(a.k_new + src);
+  const uint4 vx = *reinterpret_cast<const uint4*>(a.v_new + src);
+  quantize_store<F>(a, kx, vx, w, vec_per_head, row);
 }
 
 template <int F>
@@ -322,6 +327,22 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
 // beyond its capacity, too few free blocks) are all or nothing, as in the
 // block table: nothing is written but the head, the unchanged lengths and the
 // status.
+// Sum over the 64 lanes, the same value in every lane: DPP steps within each
+// 16-lane row, then gfx950's permlane swaps across rows (each returns, per
+// lane, itself and its partner across the swap); no step goes through LDS.
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor1, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor2, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowHalfMirror, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowMirror, 0xF, 0xF, true);
+  const auto c = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = (int)(c[0] + c[1]);
+  const auto d = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)(d[0] + d[1]);
+}
+
+constexpr int kMaxTokPerWg = 4;  // tokens a workgroup of the append grids moves (launchers: 1 or 4)
+
 template <int F>
 __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(BlockTableArgs bt,
                                                                            AppendArgs a) {
@@ -329,17 +350,24 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int bs = bt.bs;
+  // Nothing about this workgroup's own sequence depends on the batch scan,
+  // so its loads go out first and their round trips overlap the scan's: the
+  // sequence's length and new-row offsets, then (where those are usable) its
+  // tokens' source pieces and the blocks it already holds.
+  const int len = bt.seq_lens[b];
+  const int c0 = bt.cu_new[b];
+  const int n = bt.cu_new[b + 1] - c0;
   const int head = *bt.head_in;
   int total = 0, before = 0, bad = 0, over = 0;
   for (int i = tid; i < bt.B; i += kAppendThreads) {
-    const int len = bt.seq_lens[i];
-    const int n = bt.cu_new[i + 1] - bt.cu_new[i];
-    if (len < 0 || n < 0) {
+    const int li = bt.seq_lens[i];
+    const int ni = bt.cu_new[i + 1] - bt.cu_new[i];
+    if (li < 0 || ni < 0) {
       bad = 1;
       continue;
     }
-    const long have = ((long)len + bs - 1) / bs;
-    const long want = ((long)len + n + bs - 1) / bs;
+    const long have = ((long)li + bs - 1) / bs;
+    const long want = ((long)li + ni + bs - 1) / bs;
     if (want > bt.max_blocks) {
       over = 1;
       continue;
@@ -347,10 +375,37 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
     total += (int)(want - have);
     if (i < b) before += (int)(want - have);
   }
-  for (int m = 1; m < kWave; m <<= 1) {
-    total += __shfl_xor(total, m);
-    before += __shfl_xor(before, m);
+  const int vec_per_head = a.head_bytes >> 4;
+  const int vec_per_tok = a.Hkv * vec_per_head;
+  const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
+  const int vchunk = blockIdx.x % n_vchunks;
+  const int tchunk = blockIdx.x / n_vchunks;
+  const int idx = vchunk * kAppendThreads + tid;
+  const int g = idx / vec_per_head;
+  const int w = idx - g * vec_per_head;
+  const int t0 = tchunk * a.tok_per_wg;
+  const bool rows_ok = len >= 0 && n >= 0 && c0 >= 0 && (long)c0 + n <= bt.total_new;
+  const int t1 = rows_ok ? min(t0 + a.tok_per_wg, n) : t0;  // tokens whose rows exist
+  const int have = len >= 0 ? (int)min(((long)len + bs - 1) / bs, (long)bt.max_blocks) : 0;
+  int32_t* row = bt.table + (long)b * bt.max_blocks;
+  uint4 kx[kMaxTokPerWg], vx[kMaxTokPerWg];
+  int held[kMaxTokPerWg];  // the block of a token that lands in a block the sequence holds
+#pragma unroll
+  for (int u = 0; u < kMaxTokPerWg; ++u) {
+    const int t = t0 + u;
+    kx[u] = vx[u] = make_uint4(0, 0, 0, 0);
+    held[u] = -1;
+    if (u >= a.tok_per_wg || t >= t1) continue;
+    if (idx < vec_per_tok) {
+      const long src = ((long)(c0 + t) * a.Hkv + g) * a.head_bytes + w * 16;
+      kx[u] = *reinterpret_cast<const uint4*>(a.k_new + src);
+      if (a.v_cache) vx[u] = *reinterpret_cast<const uint4*>(a.v_new + src);
+    }
+    const long lb = ((long)len + t) / bs;
+    if (lb < have) held[u] = row[lb];
   }
+  total = wave_sum_int(total);
+  before = wave_sum_int(before);
   bad = __any(bad) ? 1 : 0;
   over = __any(over) ? 1 : 0;
   if ((tid & (kWave - 1)) == 0) {
@@ -371,9 +426,6 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
   if (flags & 1) err = KVC_ERR_DATA;
   else if (flags & 2) err = KVC_ERR_CAPACITY;
   else if (head < 0 || (long)head + total > bt.N) err = KVC_ERR_NO_BLOCKS;
-  const int len = bt.seq_lens[b];
-  const int c0 = bt.cu_new[b];
-  const int n = bt.cu_new[b + 1] - c0;
   if (err != 0) {
     if (blockIdx.x == 0 && tid == 0) {
       a.seq_lens_out[b] = len;
@@ -384,10 +436,8 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
     }
     return;
   }
-  const int have = (len + bs - 1) / bs;
   const int need = (int)(((long)len + n + bs - 1) / bs) - have;
   const int first = head + before;
-  int32_t* row = bt.table + (long)b * bt.max_blocks;
   if (blockIdx.x == 0) {
     for (int j = tid; j < need; j += kAppendThreads) row[have + j] = bt.free_list[first + j];
     if (tid == 0) {
@@ -395,26 +445,19 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
       if (b == 0) *bt.head_out = head + total;
     }
   }
-  if (n > 0 && c0 + n > bt.total_new) {  // cu_new points past the new-row buffers
+  if (n > 0 && !rows_ok) {  // cu_new points outside the new-row buffers
     if (blockIdx.x == 0 && tid == 0) report(bt.status, KVC_ERR_DATA);
     return;
   }
-  const int vec_per_head = a.head_bytes >> 4;
-  const int vec_per_tok = a.Hkv * vec_per_head;
-  const int n_vchunks = (vec_per_tok + kAppendThreads - 1) / kAppendThreads;
-  const int vchunk = blockIdx.x % n_vchunks;
-  const int tchunk = blockIdx.x / n_vchunks;
   if (blockIdx.x == 0 && tid == 0 && n > (long)(gridDim.x / n_vchunks) * a.tok_per_wg)
     report(bt.status, KVC_ERR_DATA);  // more new tokens than max_new promised
-  const int idx = vchunk * kAppendThreads + tid;
-  const int g = idx / vec_per_head;
-  const int w = idx - g * vec_per_head;
-  const int t0 = tchunk * a.tok_per_wg;
-  const int t1 = min(t0 + a.tok_per_wg, n);
-  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+  for (int u = 0; u < kMaxTokPerWg; ++u) {
+    const int t = t0 + u;
+    if (u >= a.tok_per_wg || t >= t1) break;
     const int pos = len + t;
     const int lb = pos / bs;
-    const long blk = lb < have ? row[lb] : bt.free_list[first + lb - have];
+    const long blk = lb < have ? held[u] : bt.free_list[first + lb - have];
     const long slot = blk * bs + pos % bs;
     if (vchunk == 0 && tid == 0) bt.slots[c0 + t] = (int32_t)slot;
     if (slot < 0 || slot >= (long)bt.N * bs) {
@@ -423,8 +466,13 @@ __global__ __launch_bounds__(kAppendThreads) void block_table_append_kernel(Bloc
     }
     if (idx >= vec_per_tok) continue;
     const long prow = ((slot / bs) * a.Hkv + g) * bs + slot % bs;  // cache row of (token, head)
-    if constexpr (F == 0) copy_piece(a, (long)c0 + t, g, w, prow * a.head_bytes + w * 16);
-    else quantize_piece<F>(a, (long)c0 + t, g, w, vec_per_head, prow);
+    if constexpr (F == 0) {
+      const long dst = prow * a.head_bytes + w * 16;
+      *reinterpret_cast<uint4*>(a.k_cache + dst) = kx[u];
+      if (a.v_cache) *reinterpret_cast<uint4*>(a.v_cache + dst) = vx[u];
+    } else {
+      quantize_store<F>(a, kx[u], vx[u], w, vec_per_head, prow);
+    }
   }
 }
 
