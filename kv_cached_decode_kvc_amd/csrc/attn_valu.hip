@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
       const int first = as.head + as.before;
       int32_t* trow_out = p.table_out + (long)b * p.max_blocks;
       for (int j = lane; j < need; j += kWave) trow_out[have + j] = p.free_list[first + j];
-      if (n > 0 && c0b + n <= p.total_new) {
+      if (n > 0 && c0b >= 0 && c0b + n <= p.total_new) {
         for (int t = lane; t < n; t += kWave) {
           const int pos = len + t, lb = pos / p.bs;
           const long blk = lb < have ? p.table[(long)b * p.max_blocks + lb]

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kBtThreads) void block_table_kernel(BlockTableArgs 
       s_first[b] = first;
       if (b == a.B - 1) s_cu[a.B] = c0 + n;
     }
-    if (n > 0 && c0 + n > a.total_new) {  // cu_new points past the slot buffer
+    if (n > 0 && (c0 < 0 || c0 + n > a.total_new)) {  // cu_new points outside the slot buffer
       report(a.status, KVC_ERR_DATA);
       continue;
     }
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int t1 = min(t0 + tok_per_wg, n);
   for (int t = t0; t < t1; ++t) {
     const long src_tok = (long)c0 + t;
-    if (src_tok >= a.total_new) {  // cu_new points past the new-row buffers
+    if (src_tok < 0 || src_tok >= a.total_new) {  // cu_new points outside the new-row buffers
       report(a.status, KVC_ERR_DATA);
       break;
     }
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_fp8_kernel(AppendArgs a
   const int t1 = min(t0 + tok_per_wg, n);
   for (int t = t0; t < t1; ++t) {  // every lane of a row takes the same branches
     const long src_tok = (long)c0 + t;
-    if (src_tok >= a.total_new) {
+    if (src_tok < 0 || src_tok >= a.total_new) {
       report(a.status, KVC_ERR_DATA);
       break;
     }

@@ -181,3 +181,48 @@ def test_block_table_batch_above_one_workgroup(ref):
     assert st == 0 and st2 == 0
     assert np.array_equal(gc.table.cpu().numpy(), t) and int(gc.head.item()) == h
     assert np.array_equal(slots.cpu().numpy(), s2)
+
+
+@pytest.mark.parametrize("entry", ["block_table", "append", "block_table_append",
+                                   "block_table_append_attn"])
+def test_negative_new_row_offset_reported_not_used(entry):
+    """cu_new starting below zero (sequence 0's new rows would begin before the
+    buffers): the entry point reports KVC_ERR_DATA and reads and writes nothing
+    outside its buffers -- the guard cells around the slot buffer keep their
+    values, and no guard row in front of the new-row buffers reaches the cache."""
+    w = synth.custom(seed=6, B=2, Hq=2, Hkv=2, D=64, dtype="bf16", block_size=16, len_lo=1, len_hi=1)
+    gc = GpuCache(w, block_size=16, capacity=64)
+    gc.prefill([5, 7])
+    assert gc.dev_status() == 0
+    cu = i32([-2, 0, 1])  # sequence 0: two rows from -2; sequence 1: one row from 0
+    total, guard = 1, 8
+    slots_full = torch.full((total + 2 * guard,), -7, dtype=torch.int32, device="cuda")
+    slots = slots_full[guard:guard + total]
+    marker, row = 0x7FC3, 0x4000  # a NaN payload the cache never holds in the guard rows; 2.0
+    k_full = torch.full((total + guard, w.Hkv, w.D), marker, dtype=torch.int16, device="cuda")
+    k_full[guard:] = row
+    k_new = k_full[guard:].view(torch.bfloat16)
+    v_new = k_full[guard:].clone().view(torch.bfloat16)
+    head_out = torch.empty_like(gc.head)
+    lens_out = torch.empty_like(gc.seq_lens)
+    if entry == "block_table":
+        kvc.kvc_block_table(gc.desc, gc.seq_lens, cu, total, gc.table, gc.free_list, gc.head,
+                            head_out, slots, gc.status)
+    elif entry == "append":
+        slots_full[guard] = int(gc.table[1, 0].item()) * 16 + 7  # sequence 1's next slot
+        kvc.kvc_append(gc.desc, k_new, v_new, gc.seq_lens, cu, total, 2, slots, gc.k, gc.v,
+                       lens_out, gc.status)
+    elif entry == "block_table_append":
+        kvc.kvc_block_table_append(gc.desc, k_new, v_new, gc.seq_lens, cu, total, 2, gc.table,
+                                   gc.free_list, gc.head, head_out, slots, gc.k, gc.v, lens_out,
+                                   gc.status)
+    else:
+        q = torch.zeros((w.B, 1, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((w.B, 1, w.Hq, w.D), dtype=torch.float32, device="cuda")
+        kvc.kvc_block_table_append_attn(gc.desc, k_new, v_new, gc.seq_lens, cu, total, 2, gc.table,
+                                        gc.free_list, gc.head, head_out, slots, gc.k, gc.v,
+                                        lens_out, q, 1, 0.125, out, gc.workspace(1), gc.status)
+    assert gc.dev_status() == -8
+    assert torch.all(slots_full[:guard] == -7) and torch.all(slots_full[guard + total:] == -7)
+    assert int((gc.k.view(torch.int16) == marker).sum().item()) == 0
+    assert int((gc.v.view(torch.int16) == marker).sum().item()) == 0
