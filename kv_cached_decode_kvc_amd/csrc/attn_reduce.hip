@@ -7,8 +7,10 @@
 // domain: m* = max_p m_p, w_p = 2^(m_p - m*) (0 for an empty partition),
 // out = sum_p w_p O_p / sum_p w_p l_p, then one rounding to the output type.
 //
-// One wavefront per output row (sequence, query head, query row); each lane
-// owns D/64 consecutive columns and, for the statistics, one partition.  The
+// One wavefront per output row (sequence, query head, query row), two for a
+// 512-wide row (each takes half the columns and works out the row's
+// statistics itself, identically); each lane owns consecutive columns and,
+// for the statistics, one partition.  The
 // partials are either a row's fixed partitions or, for the matrix-core
 // kernel's stream-K split, the pieces of the workers that covered the row's
 // segment.
@@ -51,20 +53,23 @@ __device__ __forceinline__ float lane_value(float x, int j) {
 
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
-  constexpr int CPL = D / kWave;  // columns per lane
-  const long row = blockIdx.x;    // (b * Hq + h) * n_q + r
+  constexpr int HALVES = D > 256 ? 2 : 1;  // wavefronts per row
+  constexpr int DW = D / HALVES;           // columns of one wavefront
+  constexpr int CPL = DW / kWave;          // columns per lane
+  const long row = blockIdx.x / HALVES;    // (b * Hq + h) * n_q + r
+  const int col0 = (int)(blockIdx.x % HALVES) * DW + (int)threadIdx.x * CPL;  // this lane's first column
   const int lane = threadIdx.x;
   const int r = (int)(row % p.n_q);
   const long bh = row / p.n_q;
   const int h = (int)(bh % p.Hq);
   const int b = (int)(bh / p.Hq);
-  const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + lane * CPL;
+  const long ooff = (((long)b * p.n_q + r) * p.Hq + h) * D + col0;
 
   // Where this row's partials are: partial j's statistics at ml[j * ml_step]
   // and its outputs at po[j * o_step] (this lane's columns).  Fixed
   // partitions: the row's max_parts slots, in order.  Stream-K: the pieces
   // (segment + worker) of the workers sk_meta names for the row's segment.
-  constexpr int kEarly = D <= 128 ? 16 : 4;  // registers: kEarly * D / 64
+  constexpr int kEarly = DW <= 128 ? 16 : 8;  // registers: kEarly * DW / 64
   const float2* ml;
   const float* po;
   long ml_step, o_step;
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
   int n = 0;  // partials of the row
   if (p.sk_meta == nullptr) {
     ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.max_parts;
-    po = p.ws_o + row * p.max_parts * D + lane * CPL;
+    po = p.ws_o + row * p.max_parts * D + col0;
     ml_step = 1;
     o_step = D;
     // With few partition slots, one round trip: the length, the first kEarly
@@ -96,8 +101,11 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     // discarded by selection, never multiplied, once the length is known).
     // With more slots than that, fetching every slot's outputs would move
     // several times the bytes the sequence has, so the outputs wait for the
-    // length (a second round trip) and only its partitions are read.
-    const bool speculate = p.max_parts <= (kEarly > 8 ? 8 : kEarly);
+    // length (a second round trip) and only its partitions are read.  The
+    // wide rows (1 KiB of outputs per slot and wavefront) speculate over at
+    // most four slots: reading all of seven measured slower than the second
+    // round trip.
+    const bool speculate = p.max_parts <= (DW > 128 ? 4 : kEarly > 8 ? 8 : kEarly);
     if (speculate) {
 #pragma unroll
       for (int j = 0; j < kEarly; ++j)
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
     n = valid ? wr.y - wr.x + 1 : 0;
     const long first = (seg_sk + wr.x) * p.sk_rows + i_sk % p.rows_item;  // workspace row of piece 0
     ml = reinterpret_cast<const float2*>(p.ws_ml) + first;
-    po = p.ws_o + first * D + lane * CPL;
+    po = p.ws_o + first * D + col0;
     ml_step = p.sk_rows;
     o_step = (long)p.sk_rows * D;
     if (lane < n) mine_raw = ml[lane * ml_step];
@@ -174,10 +182,19 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceParams p) {
           for (int c = 0; c < CPL; ++c) acc[c] += wj * o[u][c];
         }
       }
-      for (; j < cnt; ++j) {
-        const float wj = lane_value(wq, j);
+      if (j < cnt) {  // the last 1 .. 7 partitions: their loads in flight together
+        float o[8][CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] += wj * po[(q0 + j) * o_step + c];
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) o[u][c] = j + u < cnt ? po[(q0 + j + u) * o_step + c] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j + u >= cnt) break;
+          const float wj = lane_value(wq, j + u);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] += wj * o[u][c];
+        }
       }
     }
     den = wave_sum(den);
@@ -201,9 +218,10 @@ hipError_t launch_reduce(const ReduceParams& p, int out_dtype, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)rows), block(kWave);
   const bool bf = out_dtype == KVC_BF16;
-  if (p.D == 512) {  // MLA: weighted latents
-    if (bf) hipLaunchKernelGGL((reduce_kernel<512, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((reduce_kernel<512, false>), grid, block, 0, s, p);
+  if (p.D == 512) {  // MLA: weighted latents, two wavefronts per row
+    const dim3 grid2((unsigned)(2 * rows));
+    if (bf) hipLaunchKernelGGL((reduce_kernel<512, true>), grid2, block, 0, s, p);
+    else hipLaunchKernelGGL((reduce_kernel<512, false>), grid2, block, 0, s, p);
   } else if (p.D == 128) {
     if (bf) hipLaunchKernelGGL((reduce_kernel<128, true>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((reduce_kernel<128, false>), grid, block, 0, s, p);
