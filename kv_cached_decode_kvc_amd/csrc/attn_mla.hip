@@ -252,11 +252,7 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
   constexpr float kLazy = 8.f;
   // this split's partial S^T of the tile in `buf`, every 16-key half (lane:
   // keys kh*16 + grp*4 .. +3 of row col), published in s_ps
-  // The matrix-core blocks (scores here, values below) run at raised issue
-  // priority, so that the SIMD's other wavefront's vector work fills in
-  // around them rather than delaying them (16 heads 127 -> 120 us).
   auto qk_part = [&](int buf) {
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) {
       const uint8_t* ka = lds[buf] + (kh * kTile + col) * ROWB + grp * 16 + k_lo * 64;
@@ -273,7 +269,6 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
       }
       s_ps[rbw][sp][kh][lane] = s0 + s1;
     }
-    __builtin_amdgcn_s_setprio(0);
   };
   // the whole scores of the tile (the splits' parts added in split order),
   // one online-softmax step over its TK keys: the weights of each 16-key half
@@ -323,7 +318,6 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
   };
   // O^T += V^T . P^T over this split's columns, one 16-key half at a time
   auto pv = [&](int buf) {
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kh = 0; kh < NH; ++kh) {
       const uint8_t* va_ptr = lds[buf] + (kh * kTile + grp * 4 + (col >> 2)) * ROWB +
@@ -352,7 +346,6 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
         for (int i = 0; i < VG; ++i) vcur[i] = vnext[i];
       }
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // prologue: tiles 0 and 1 in LDS, tiles 2 .. PF + 1 in flight; tile 0's
