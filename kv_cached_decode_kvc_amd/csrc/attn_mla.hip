@@ -13,28 +13,23 @@
 //
 // Every query row of a sequence (Hq heads x n_q verify rows) reads the same
 // latent rows, so a workgroup owns one (sequence, group of rows, partition):
-// its threads load each 16-key tile (16 x 1152 bytes, one contiguous run)
-// cooperatively into one LDS tile, and its wavefronts contract 16-row blocks
-// against it on the matrix cores:
-//   S^T = K . Q^T   (18 steps of v_mfma_f32_16x16x32_bf16, Q^T in registers)
+// its threads load each tile of 16 or 32 keys (rows of 1152 bytes, one
+// contiguous run per 16 keys) cooperatively into an LDS tile, and its
+// wavefronts contract 16-row blocks against it on the matrix cores:
+//   S^T = K . Q^T   (the 18 steps of 32 along the 576 dims on
+//                    v_mfma_f32_16x16x32_bf16, Q^T in registers, the steps
+//                    split between the wavefronts of a row block);
 //   O^T += V^T . P^T (column tiles of the 512; V^T via ds_read_b64_tr_b16;
 //                     the weights as bf16 hi + lo pairs along the reduction
 //                     index, as in the grouped-query kernel).
 // Online softmax per row as in the other partition kernels; verify row r
-// sees keys 0 .. L - n_q + r.
-//
-// Two forms.  Up to 16 rows (e.g. 16 heads, partition_mla with C = 4): four
-// wavefronts share the one row block, each computes its scores and softmax
-// itself and accumulates 128 of the 512 columns.  More rows (e.g. 128 heads,
-// partition_mla_pair): eight wavefronts, two per SIMD, cover four row blocks;
-// the two wavefronts of a row block split the columns, and one of them
-// computes the block's scores and softmax and passes the weights to the
-// other through LDS.  Two LDS tiles let the score products of tile n + 1 run
-// beside the value products of tile n; a ring of PF register stages keeps
-// the following tiles in flight.  Row groups of the same (sequence,
-// partition) get workgroup ids 8 apart: launches place workgroup i on XCD i
-// mod 8, so they share one XCD's L2 and run at the same time, and the tile
-// comes from HBM once.
+// sees keys 0 .. L - n_q + r.  The workgroup shapes (four wavefronts for up
+// to 16 rows, eight for more) are described at the kernel.  Two LDS tiles
+// let the score products of tile n + 1 run beside the value products of
+// tile n; a ring of PF register stages keeps the following tiles in flight.
+// Row groups of the same (sequence, partition) get workgroup ids 8 apart:
+// launches place workgroup i on XCD i mod 8, so they share one XCD's L2 and
+// run at the same time.
 #include "launch.hpp"
 
 namespace kvc {
