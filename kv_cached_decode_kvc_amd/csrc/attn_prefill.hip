@@ -16,7 +16,9 @@
 // the grouped heads share every K/V tile ("Efficient Inference", GQA passage).
 // The threads load each 32-key tile of K and V (one contiguous run per
 // tensor) cooperatively into two LDS buffers through a two-stage register
-// ring (one barrier per tile); each
+// ring (one barrier per tile), with buffer loads of the default cache policy
+// so that the pair's other row blocks (placement below) find the rows in
+// their XCD's L2; each
 // wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 (S^T =
 // K.Q^T with Q^T in registers, two 16-key halves; one online-softmax step
 // per 32 keys; O^T += V^T.P^T with V^T via ds_read_b64_tr_b16 and the weights
@@ -36,6 +38,17 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfKeys = 32;  // keys per LDS tile (two 16-key MFMA tiles)
 constexpr int kPfMaxIds = 4096;  // block ids of one sequence staged in LDS
+
+// 16-byte load at byte `off` of the wave-uniform address `base`, through a
+// buffer resource with the default cache policy: the line stays in the XCD's
+// L2 for the other row blocks of the pair, which read it soon after.  (The
+// decode kernels, whose rows are read once, use non-temporal loads; cached
+// loads cost the streaming MLA kernel 68%.)
+__device__ __forceinline__ uint4 load_shared_l2(const void* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 // Work placement.  A launch places workgroup i on XCD i mod 8, and each XCD
 // has its own L2, so the row blocks of one (sequence, KV head) pair, which
@@ -83,6 +96,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   constexpr int CPR = D * 2 / 16;              // 16-byte chunks per row
   constexpr int TCH = kPfKeys * CPR;           // chunks per tile and tensor
   constexpr int PER = (TCH + kPfThreads - 1) / kPfThreads;
+  static_assert(kWave % CPR == 0 && 16 % (kWave / CPR) == 0 && TCH % kPfThreads == 0,
+                "a wavefront's chunks of one stage lie in one 16-key half");
   constexpr int ROWB = D * 2 + 16;   // K rows: 4 banks apart
   constexpr int VROWB = D * 2 + 32;  // V rows: 8 banks apart, for the transposed reads
   constexpr int PF = 2;
@@ -213,10 +228,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int row = min(frow[u], last);
-      const long c = frow[u] >= 16 && last >= 16 ? c1 : c0;
+      // a wavefront's chunks of one stage lie in one 16-key half (64 chunks
+      // are 4 rows of 128 or 8 rows of 64): the half's base is uniform
+      const bool h1 = __builtin_amdgcn_readfirstlane(frow[u] >= 16 ? 1 : 0) != 0;
+      const long c = h1 && last >= 16 ? c1 : c0;
       const uint32_t lane_off = (uint32_t)(row * D + fchk[u]) * 2;  // bytes
-      s.k[u] = load_stream((const uint8_t*)p.k + c * 2 + lane_off);
-      s.v[u] = load_stream((const uint8_t*)p.v + c * 2 + lane_off);
+      s.k[u] = load_shared_l2((const uint8_t*)p.k + c * 2, lane_off);
+      s.v[u] = load_shared_l2((const uint8_t*)p.v + c * 2, lane_off);
     }
   };
   auto store = [&](const Stage& s, int buf) {
