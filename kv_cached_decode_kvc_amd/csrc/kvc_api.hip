@@ -136,8 +136,8 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
     // bf16 tiles: one worker per SIMD; FP8 tiles carry half the bytes, so a
     // full round of resident wavefronts keeps enough of them in flight
     // (measured on the full-size GQA and verify workloads: bf16 GQA 372 us
-    // at 1024 workers against 371 at 2048 and 380 at 3072, FP8 GQA 208 us
-    // at 3072 against 345 at 1024)
+    // at 1024 workers against 380 at 3072, and 369 against 371 at 2048 in a
+    // later pair of runs; FP8 GQA 208 us at 3072 against 345 at 1024)
     pl.sk_workers = resident_simds() * (!fp8_format(d) ? 1 : pl.rows_per_item == 32 ? 2 : 3);
     pl.sk_rows = std::min(pl.rows_per_item, R);
     pl.grid = pl.sk_workers;
