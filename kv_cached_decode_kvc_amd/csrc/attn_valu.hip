@@ -473,7 +473,212 @@ __global__ __launch_bounds__(64, (valu_min_waves<T, D>())) void partition_valu(A
   }
 }
 
+// Stream-K form (paged bf16 and fp32 caches whose work items would take more
+// than one round of resident wavefronts): the batch's 16-key tiles are shared
+// out evenly over a fixed number of workers, as in the matrix-core kernel
+// (attn_mfma.hip), so that every worker streams the same number of tiles
+// (+-1) and the launch does not end with a ragged last round of items of
+// different lengths ("Inference-1", "FlashDecoding": any split of the keys
+// combines exactly).  A segment is one query row (sequence b, KV head g, row
+// i = r * G + hh of the KV head's G * n_q rows) with T_b = ceil(L_b / 16)
+// tile-units; the segments lie end to end in (b, g, i) order and worker w of
+// NW takes the contiguous units [w W / NW, (w + 1) W / NW) of the W in total,
+// a run that may end one segment and start the next.  Each (segment, worker)
+// piece leaves one partial at workspace row segment + worker (unique, since
+// both grow along the run), and the worker holding a segment's first tile
+// records which workers cover it, for the reduce.  A row r < n_q - 1 sees
+// fewer keys than the segment's tiles: its pieces past them leave empty
+// partials (m = -inf).  The tile loop is the fixed-partition kernel's, one
+// tile at a time.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void partition_valu_sk(AttnParams p) {
+  using S = ValuShape<T, D>;
+  constexpr int VE = S::VE, LPR = S::LPR, RPL = S::RPL, U = S::U;
+  static_assert(IsFp8<T>::kFormat == 0, "bf16 and fp32 caches");
+  const int lane = threadIdx.x;
+  const int c = lane % LPR;   // which 16-byte column chunk of a key row
+  const int r0 = lane / LPR;  // which row of a wave load
+  const int Gq = p.G * p.n_q;  // query rows of a KV head
+  const int SU = p.Hkv * Gq;   // segments of a sequence
+  const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
+  const bool paged = p.table != nullptr;
+
+  auto run_piece = [&](int b, int u, int L, int t0, int t1, long slot) {
+    const int g = u / Gq, i = u % Gq, r = i / p.G, h = g * p.G + i % p.G;
+    const int end = L - p.n_q + r + 1;           // visible keys of row r
+    const int k_end = min(t1 * kTile, end);
+    float o[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) o[j] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    if (t0 * kTile < k_end) {
+      const T* kbase = (const T*)p.k;
+      const T* vbase = (const T*)p.v;
+      const typename Elem<T>::Q qv =
+          Elem<T>::load_q(p.q, (((long)b * p.n_q + r) * p.Hq + h) * D + c * VE);
+      const int32_t* trow = paged ? p.table + (long)b * p.max_blocks : nullptr;
+      auto load_ids = [&](int j0) -> int {
+        const int tk = (t0 + j0 + lane) * kTile;
+        return tk < k_end ? trow[tk >> bs_shift] : 0;
+      };
+      int ids = 0, ids_next = 0;
+      if (paged) {
+        ids = load_ids(0);
+        if ((t0 + kWave) * kTile < k_end) ids_next = load_ids(kWave);
+      }
+      int idx = 0;
+      for (int tile = t0 * kTile; tile < k_end; tile += kTile, ++idx) {
+        long row0;
+        if (!paged) {
+          row0 = ((long)b * p.Hkv + g) * p.S_max + tile;
+        } else {
+          if (idx > 0 && (idx & (kWave - 1)) == 0) {
+            ids = ids_next;
+            if ((t0 + idx + kWave) * kTile < k_end) ids_next = load_ids(idx + kWave);
+          }
+          const int blk = __builtin_amdgcn_readlane(ids, idx & (kWave - 1));
+          if (blk < 0 || blk >= p.N) {
+            if (lane == 0) report(p.status, KVC_ERR_DATA);
+            continue;
+          }
+          row0 = ((long)blk * p.Hkv + g) * p.bs + (tile & (p.bs - 1));
+        }
+        const int nvalid = min(kTile, end - tile);  // >= 1
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          int tt = uu * RPL + r0;
+          tt = tt < nvalid ? tt : nvalid - 1;  // masked lanes re-read a visible row
+          kr[uu] = load_stream(kbase + (row0 + tt) * D + c * VE);
+          vr[uu] = load_stream(vbase + (row0 + tt) * D + c * VE);
+        }
+        float sc[U];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          const float dotp = group_sum<LPR>(Elem<T>::dot(qv, kr[uu]));
+          sc[uu] = uu * RPL + r0 < nvalid ? dotp * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[uu]);
+        }
+        mx = cross_max<LPR>(mx);
+        if (mx == -INFINITY) continue;  // no finite score in the tile
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - m_new);  // 0 on the first tile
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < VE; ++j) o[j] *= alpha;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          const float pu = fast_exp2(sc[uu] - m_new);
+          l += pu;
+          Elem<T>::axpy(pu, vr[uu], o);
+        }
+        m = m_new;
+      }
+      l = cross_sum<LPR>(l);
+#pragma unroll
+      for (int j = 0; j < VE; ++j) o[j] = cross_sum<LPR>(o[j]);
+    }
+    if (r0 == 0) {
+#pragma unroll
+      for (int j = 0; j < VE; j += 4)
+        *reinterpret_cast<f32x4_t*>(p.ws_o + slot * D + c * VE + j) =
+            f32x4_t{o[j], o[j + 1], o[j + 2], o[j + 3]};
+    }
+    if (lane == 0) {
+      p.ws_ml[slot * 2] = m;
+      p.ws_ml[slot * 2 + 1] = l;
+    }
+  };
+
+  // the lengths give T_b tiles per sequence (0 for an invalid length, which
+  // worker 0 reports), W = SU * sum T_b tile-units in all
+  const int w = blockIdx.x;
+  long W = 0;
+  int bad = 0;
+  for (int first = 0; first < p.B; first += kWave) {
+    const int i = first + lane;
+    int tiles = 0;
+    if (i < p.B) {
+      const int Li = p.seq_lens[i];
+      if (Li >= p.n_q && Li <= p.cap) tiles = (Li + kTile - 1) / kTile;
+      else bad = 1;
+    }
+    for (int mm = 1; mm < kWave; mm <<= 1) tiles += __shfl_xor(tiles, mm);
+    W += tiles;
+  }
+  if (w == 0 && __any(bad) && lane == 0) report(p.status, KVC_ERR_DATA);
+  W *= SU;
+  if (W == 0) return;
+  const long NW = min((long)gridDim.x, max(1L, W / p.sk_min_tiles));
+  if (w >= NW) return;
+  const long s0 = (long)w * W / NW, s1 = (long)(w + 1) * W / NW;
+  if (s0 >= s1) return;
+  // the sequence holding tile-unit s0: first b with (units before b + its units) > s0
+  int b = 0;
+  long pre = 0;  // tile-units before sequence b
+  for (int first = 0; first < p.B; first += kWave) {
+    const int i = first + lane;
+    long n = 0;
+    if (i < p.B) {
+      const int Li = p.seq_lens[i];
+      if (Li >= p.n_q && Li <= p.cap) n = (long)SU * ((Li + kTile - 1) / kTile);
+    }
+    long incl = n;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const long t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const unsigned long long hit = __ballot(s0 < pre + incl);
+    if (hit != 0) {
+      const int j = __ffsll((long long)hit) - 1;
+      b = first + j;
+      pre += __shfl(incl - n, j);
+      break;
+    }
+    pre += __shfl(incl, kWave - 1);
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+  int tiles = (L + kTile - 1) / kTile;
+  long pos = s0;
+  while (pos < s1) {
+    while (pos >= pre + (long)SU * tiles) {  // past sequence b: the next one with tiles
+      pre += (long)SU * tiles;
+      ++b;
+      L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+      tiles = (L >= p.n_q && L <= p.cap) ? (L + kTile - 1) / kTile : 0;
+    }
+    const long local = pos - pre;
+    const int u = (int)(local / tiles), t0 = (int)(local % tiles);
+    const int t1 = (int)min((long)tiles, t0 + (s1 - pos));
+    const int seg = b * SU + u;
+    if (t0 == 0 && lane == 0) {  // this worker starts the segment: record its workers
+      const long x_last = pre + (long)u * tiles + tiles - 1;
+      const int w_last = (int)(((x_last + 1) * NW - 1) / W);
+      p.sk_meta[seg] = make_int2(w, w_last);
+    }
+    run_piece(b, u, L, t0, t1, (long)seg + w);
+    pos += t1 - t0;
+  }
+}
+
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s) {
+  if (p.sk_meta) {  // stream-K: one workgroup per worker
+    if (p.cu_new) return hipErrorInvalidValue;  // no append fused into this form
+    if (p.sk_workers <= 0) return hipSuccess;
+    const dim3 grid((unsigned)p.sk_workers), block(64);
+    if (dtype == KVC_BF16) {
+      if (p.D == 128) hipLaunchKernelGGL((partition_valu_sk<uint16_t, 128>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((partition_valu_sk<uint16_t, 64>), grid, block, 0, s, p);
+    } else if (dtype == KVC_F32) {
+      if (p.D == 128) hipLaunchKernelGGL((partition_valu_sk<float, 128>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((partition_valu_sk<float, 64>), grid, block, 0, s, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const long n_wg = xcd_grid(p.B, p.Hq * p.n_q, p.max_parts);
   if (n_wg == 0) return hipSuccess;
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;

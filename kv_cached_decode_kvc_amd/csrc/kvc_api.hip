@@ -77,7 +77,8 @@ struct Plan {
   size_t bytes;       // workspace size
 };
 
-constexpr int kSkMinTiles = 8;  // stream-K: fewest 16-key tiles a worker streams
+constexpr int kSkMinTiles = 8;     // stream-K: fewest 16-key tiles a worker streams
+constexpr int kValuSkPerSimd = 2;  // stream-K workers per SIMD of the vector-ALU kernel
 
 // Every attention workspace starts with kCntBytes of piece counters for the
 // combine fused into the partition launch (one per output row); the partials
@@ -103,11 +104,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // fewer than 1024 wavefronts, and doubled (up to 8192) while it would give
 // more than 65536.
 //
-// The matrix-core path (grouped rows) uses no partition length by default:
-// the stream-K split shares the batch's tiles out evenly over a fixed number
-// of workers (one per SIMD for bf16 caches; for FP8 caches one round of
-// resident wavefronts, 2 per SIMD with 32-row blocks, 3 with 16-row blocks),
-// each taking at least kSkMinTiles tiles.  Its workspace holds one partial
+// The matrix-core path (grouped rows), and the vector-ALU path on paged
+// bf16 / fp32 caches too large for one round of work items, use no partition
+// length by default: the stream-K split shares the batch's tiles out evenly
+// over a fixed number of workers (matrix cores: one per SIMD for bf16
+// caches, for FP8 caches one round of resident wavefronts, 2 per SIMD with
+// 32-row blocks, 3 with 16-row blocks; vector ALUs: 2 per SIMD), each taking
+// at least kSkMinTiles tiles.  Its workspace holds one partial
 // per row of every piece: at most segments + workers pieces (a piece starts
 // at a segment start or a worker start), sk_rows rows each.
 // SIMDs of the current device (4 per compute unit); 1024 on MI355X.
@@ -179,6 +182,28 @@ Plan make_plan(const kvc_cache_desc* d, int n_q) {
   // matrix-core kernel's stream-K workers would pay the wait on every piece
   // and keep the separate reduce.
   pl.fused = !pl.mfma && (long)rows <= kMaxCounters && pl.grid <= 4L * resident_simds();
+  // A paged bf16 or fp32 cache whose work items would take more than that one
+  // round uses the vector-ALU kernel's stream-K form instead: the items of
+  // unequal lengths (short sequences, short last partitions) otherwise end
+  // the launch with a ragged last round.  Two workers per SIMD, one partial
+  // per piece, the records as in the matrix-core split (measured on the
+  // 64-sequence paged MHA batch: 412 us with fixed 512-key partitions,
+  // 395 us stream-K with two or three workers per SIMD, 400 with four, 425
+  // with five; more loads in flight per worker measured slower).
+  if (!pl.mfma && !pl.fused && d->block_size > 0 && !fp8_format(d) &&
+      d->partition_tokens == 0) {
+    pl.sk = true;
+    pl.P = pl.P_lo = pl.max_parts = 0;
+    pl.rows_per_item = 1;  // a segment is one query row
+    pl.sk_workers = resident_simds() * kValuSkPerSimd;
+    pl.sk_rows = 1;
+    pl.grid = pl.sk_workers;
+    const size_t pieces = (size_t)units + pl.sk_workers;
+    pl.o_offset = kCntBytes;
+    pl.ml_offset = align256(pl.o_offset + pieces * d->head_dim * sizeof(float));
+    pl.meta_offset = align256(pl.ml_offset + pieces * 2 * sizeof(float));
+    pl.bytes = pl.meta_offset + (size_t)units * 2 * sizeof(int32_t);
+  }
   return pl;
 }
 
@@ -600,7 +625,7 @@ int kvc_block_table_append_attn(const kvc_cache_desc* d, const void* k_new, cons
       seq_lens_out == seq_lens)
     return KVC_ERR_ARG;
   if (total_new > 0 && (!k_new || !v_new || !slot_mapping)) return KVC_ERR_ARG;
-  if (!pl.mfma && !fp8_format(d)) {
+  if (!pl.mfma && !pl.sk && !fp8_format(d)) {
     // one partition launch takes the blocks, appends and attends (the
     // combine inside it too, or a reduce over the same lengths)
     AttnParams p = attn_params(d, pl, n_q, q, k_cache, v_cache, seq_lens, block_table, scale,
@@ -624,7 +649,8 @@ int kvc_block_table_append_attn(const kvc_cache_desc* d, const void* k_new, cons
     r.total_new = total_new;
     return hip_status(launch_reduce(r, out_dtype, (hipStream_t)stream));
   }
-  // grouped rows or FP8: block table and append in one launch, then attention
+  // grouped rows, stream-K or FP8: block table and append in one launch, then
+  // attention
   st = kvc_block_table_append(d, k_new, v_new, seq_lens, cu_new, total_new, max_new, block_table,
                               free_list, free_head_in, free_head_out, slot_mapping, k_cache,
                               v_cache, seq_lens_out, dev_status, stream);

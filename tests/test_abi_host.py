@@ -125,9 +125,9 @@ def test_workspace_and_partition_sizes(lib):
     assert kvc.kvc_attn_partition_tokens(desc(partition_tokens=48), 1) == 48
     assert kvc.kvc_attn_workspace_bytes(desc(head_dim=80), 1) == 0
     assert kvc.kvc_attn_partition_tokens(desc(head_dim=80), 1) == -3
-    # paged: the power of two nearest an eighth of the capacity (4000 tokens);
-    # grouped rows (GQA decode, verify) use the stream-K split: no length (0)
-    for name, want in (("C2", 1024), ("C3", 512), ("C4", 0), ("C5", 0)):
+    # grouped rows (GQA decode, verify) and a paged MHA batch too large for one
+    # round of work items use the stream-K split: no length (0)
+    for name, want in (("C2", 1024), ("C3", 0), ("C4", 0), ("C5", 0)):
         w = synth.get(name)
         dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
                   block_size=w.block_size, max_seq_len=synth.capacity_tokens(w),
@@ -187,6 +187,34 @@ def test_stream_k_workspace(lib):
     assert kvc.kvc_attn_partition_tokens(dd, w.n_q) == 512
     rows = w.B * w.Hq * w.n_q
     assert kvc.kvc_attn_workspace_bytes(dd, w.n_q) == _ws_bytes(rows, -(-cap // 512), w.D)
+
+
+def test_valu_stream_k_plan(lib):
+    # paged MHA: a batch whose fixed partitions (the power of two nearest an
+    # eighth of the capacity) fit one round of resident work items combines
+    # inside its partition launch; a larger one (C3: 64 x 40 rows, 512-key
+    # partitions) takes the vector-ALU stream-K split, 2 workers per SIMD,
+    # one partial row per piece and a record per segment (query row)
+    w = synth.get("C3")
+    cap = synth.capacity_tokens(w)
+
+    def paged(batch, dtype="bf16", **kw):
+        return desc(batch=batch, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                    dtype=kvc.DTYPE_CODES[dtype], block_size=w.block_size, max_seq_len=cap,
+                    max_blocks_per_seq=synth.max_blocks_per_seq(w), num_blocks=synth.pool_blocks(w),
+                    **kw)
+    small = paged(8)  # 8 x 40 rows x 9 partitions: 2880 items, one round
+    assert kvc.kvc_attn_partition_tokens(small, 1) == 512
+    assert kvc.kvc_attn_launches(small, 1) == 1
+    for dtype in ("bf16", "f32"):
+        dd = paged(w.B, dtype)
+        assert kvc.kvc_attn_partition_tokens(dd, 1) == 0
+        assert kvc.kvc_attn_launches(dd, 1) == 2
+        segs = w.B * w.Hq
+        assert kvc.kvc_attn_workspace_bytes(dd, 1) == _sk_bytes(segs + 2048, 1, w.D, segs)
+    # FP8 caches and an explicit partition length keep fixed partitions
+    assert kvc.kvc_attn_partition_tokens(paged(w.B, "fp8_e4m3"), 1) == 512
+    assert kvc.kvc_attn_partition_tokens(paged(w.B, partition_tokens=256), 1) == 256
 
 
 def test_mla_workspace_covers_launch_time_partitions(lib):

@@ -326,3 +326,52 @@ def test_stream_k_split(ref, B, n_q, lo, hi, bs):
     got = out.cpu().numpy()
     for b in range(B):
         assert_close(got[b], want[b], "sk B=%d b=%d L=%d" % (B, b, lengths[b]))
+
+
+# (dtype, D, Hq, Hkv, n_q, len_lo, len_hi, B, block_size): paged batches whose
+# fixed partitions would need more than one round of work items
+VALU_SK = [
+    ("bf16", 128, 16, 16, 1, 1, 2000, 70, 16),   # two 64-sequence chunks of the scans
+    ("f32", 64, 8, 4, 3, 3, 2000, 40, 32),       # grouped fp32 heads, verify rows
+    ("bf16", 64, 12, 12, 1, 1, 40, 400, 16),     # workers spanning many short segments
+]
+
+
+@pytest.mark.parametrize("case", VALU_SK, ids=["-".join(map(str, c)) for c in VALU_SK])
+def test_valu_stream_k_split(ref, case):
+    """The vector-ALU kernel's stream-K split (paged bf16 / fp32 caches too
+    large for one round of work items): lengths of 1, 15, 16, 17, 31 and 32
+    keys among random ones, rows of a KV head in (query row, head) order,
+    every row against the oracle."""
+    dtype, D, Hq, Hkv, n_q, lo, hi, B, bs = case
+    w = synth.custom(name="vsk", seed=950 + B, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
+                     block_size=bs, n_q=n_q, len_lo=lo, len_hi=hi)
+    cached = synth.final_lengths(w) - n_q
+    edge = np.array([1, 15, 16, 17, 31, 32]) - n_q
+    cached[:len(edge)] = np.maximum(edge, 0)
+    gc = GpuCache(w, block_size=bs)
+    assert kvc.kvc_attn_partition_tokens(gc.desc, n_q) == 0
+    gc.prefill(cached)
+    gc.step_rows(0)
+    out = gc.attend(queries_dev(w), n_q)
+    assert gc.dev_status() == 0
+    want = oracle_outputs(ref, w, range(B), cached)
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert_close(got[b], want[b], "vsk %s b=%d L=%d" % (dtype, b, cached[b] + n_q))
+
+
+def test_valu_stream_k_bad_block_reports_and_does_not_fault():
+    dtype, D, Hq, Hkv, n_q, lo, hi, B, bs = VALU_SK[0]
+    w = synth.custom(name="vskbad", seed=960, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
+                     block_size=bs, n_q=n_q, len_lo=lo, len_hi=hi)
+    cached = synth.final_lengths(w) - n_q
+    cached[3] = 100
+    gc = GpuCache(w, block_size=bs)
+    assert kvc.kvc_attn_partition_tokens(gc.desc, n_q) == 0
+    gc.prefill(cached)
+    gc.step_rows(0)
+    gc.table[3, 2] = gc.N + 5  # outside the pool
+    out = gc.attend(queries_dev(w), n_q)
+    assert gc.dev_status() == -8
+    assert bool(torch.isfinite(out).all())
