@@ -41,15 +41,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kv_cached_decode_kvc_amd", "csrc")
 
 
-def kernel_of(w, mfma: bool) -> tuple[str, list[str]]:
-    """Name of the dominant kernel and the sources that define it."""
+def kernel_of(w, mfma: bool, stream_k: bool = False) -> tuple[str, list[str]]:
+    """Name of the dominant kernel and the sources that define it (stream_k:
+    the plan has no partition length)."""
     if w.dv:
         return "partition_mla", ["attn_mla.hip", "common.hpp"]
     if w.prefill:
         return "prefill_mfma", ["attn_prefill.hip", "common.hpp"]
     if mfma:
         return "partition_mfma", ["attn_mfma.hip", "common.hpp"]
-    return "partition_valu", ["attn_valu.hip", "common.hpp"]
+    return ("partition_valu_sk" if stream_k else "partition_valu"), ["attn_valu.hip", "common.hpp"]
 
 
 def source_hash(files) -> str:
@@ -726,7 +727,7 @@ def main():
     value = kv_bytes / (step_us * 1e-6) / 1e9
     achieved = kv_bytes / (part_us * 1e-6) / 1e9
     steady_ms = wall / K * 1e3
-    kname, ksrc = kernel_of(w, mfma)
+    kname, ksrc = kernel_of(w, mfma, stream_k=P == 0)
     shash = source_hash(ksrc)
     traffic = stored_traffic(w.name, kname, shash)
 

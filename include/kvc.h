@@ -96,8 +96,8 @@ typedef struct {
                                  max_blocks_per_seq * block_size tokens                 */
   int32_t num_blocks;         /* paged: pool size N                                     */
   int32_t partition_tokens;   /* split-KV partition length in tokens: 0 = library
-                                 default (stream-K for grouped rows), else a multiple
-                                 of 16                                                  */
+                                 default (stream-K for grouped rows and large paged
+                                 batches), else a multiple of 16                        */
 } kvc_cache_desc;
 
 /*
@@ -215,12 +215,14 @@ int kvc_append_attn(const kvc_cache_desc* d, const void* k_new, const void* v_ne
  * kvc_verify_attn over the lengths after the append, for a paged cache
  * ([I1] PagedAttention: blocks on demand; [EI] lists "KV cache write +
  * attention" among the fused kernels serving systems ship).  With one query
- * row per KV row (MHA, every fp32 cache; not FP8) the partition launch does
- * it all: its tiles read the new rows from k_new / v_new (never a table
- * entry this call writes), and one work item per sequence repeats the
- * batch's block count, takes the sequence's blocks from the free list and
- * writes the table entries, slots, new rows and length (sequence 0 the
- * head).  Grouped rows and FP8 caches run kvc_block_table_append first.
+ * row per KV row (MHA, every fp32 cache; not FP8) and a batch whose work
+ * items fit one round of resident wavefronts the partition launch does it
+ * all: its tiles read the new rows from k_new / v_new (never a table entry
+ * this call writes), and one work item per sequence repeats the batch's
+ * block count, takes the sequence's blocks from the free list and writes
+ * the table entries, slots, new rows and length (sequence 0 the head).
+ * Grouped bf16 rows, larger batches (the stream-K split) and FP8 caches run
+ * kvc_block_table_append first.
  * Arguments as kvc_block_table_append (B <= 8192) and kvc_verify_attn (its
  * seq_lens are seq_lens_out and its block_table the updated table; the
  * workspace is sized by kvc_attn_workspace_bytes).  On success outputs,
@@ -340,8 +342,12 @@ size_t kvc_attn_workspace_bytes(const kvc_cache_desc* d, int32_t n_q);
  * sequence by sequence and KV head by KV head, are shared out evenly over a
  * fixed set of workers (one per SIMD of the device for bf16 caches, one
  * round of resident wavefronts for FP8), so every worker streams the same
- * number of tiles whatever the lengths.  An explicit desc.partition_tokens
- * is always used as given (fixed partitions). */
+ * number of tiles whatever the lengths.  The vector-ALU rows (one query row
+ * per KV row, fp32 caches) of a paged bf16 or fp32 cache use the same split
+ * (two workers per SIMD, a segment per query row) when their fixed
+ * partitions would take more than one round of resident work items.  An
+ * explicit desc.partition_tokens is always used as given (fixed
+ * partitions). */
 int32_t kvc_attn_partition_tokens(const kvc_cache_desc* d, int32_t n_q);
 
 /* Kernel launches kvc_decode_attn / kvc_verify_attn make for this desc and
