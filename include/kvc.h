@@ -468,7 +468,12 @@ int kvc_copy_blocks(const kvc_cache_desc* d, const int32_t* src, const int32_t* 
  * of resident workgroups, it is an upper bound: each launch then picks a
  * length between half of it and it from the lengths in device memory, the
  * same in the partition and reduce calls, and the workspace covers the
- * shortest.  An explicit partition_tokens is used as given.
+ * shortest.  With more than 16 rows (Hq * n_q) and partition_tokens 0 it
+ * returns 0: the stream-K split, in which one round of workgroups shares the
+ * batch's 32-key steps out evenly (every row group of a worker takes the same
+ * run), as kvc_attn_partition_tokens describes for grouped rows; it falls back
+ * to partitions when a worker's run could exceed 16384 keys of one sequence.
+ * An explicit partition_tokens is used as given.
  */
 size_t kvc_mla_workspace_bytes(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);
 int32_t kvc_mla_partition_tokens(const kvc_cache_desc* d, int32_t n_q, int32_t value_dim);

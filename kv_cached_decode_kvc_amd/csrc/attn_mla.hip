@@ -12,7 +12,9 @@
 // latent, combined across partitions by the usual reduce.
 //
 // Every query row of a sequence (Hq heads x n_q verify rows) reads the same
-// latent rows, so a workgroup owns one (sequence, group of rows, partition):
+// latent rows, so a workgroup owns one (sequence, group of rows, partition),
+// or with more than 16 rows by default one row group of a stream-K worker's
+// run of steps across sequences (the pieces are described at the kernel):
 // its threads load each tile of 16 or 32 keys (rows of 1152 bytes, one
 // contiguous run per 16 keys) cooperatively into an LDS tile, and its
 // wavefronts contract 16-row blocks against it on the matrix cores:
@@ -27,9 +29,9 @@
 // to 16 rows, eight for more) are described at the kernel.  Two LDS tiles
 // let the score products of tile n + 1 run beside the value products of
 // tile n; a ring of PF register stages keeps the following tiles in flight.
-// Row groups of the same (sequence, partition) get workgroup ids 8 apart:
-// launches place workgroup i on XCD i mod 8, so they share one XCD's L2 and
-// run at the same time.
+// Row groups of the same (sequence, partition), or of the same worker, get
+// workgroup ids 8 apart: launches place workgroup i on XCD i mod 8, so they
+// share one XCD's L2 and run at the same time.
 #include "launch.hpp"
 
 namespace kvc {
@@ -38,8 +40,6 @@ namespace {
 
 typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-constexpr int kMlaMaxTiles = 1024;  // 16-key halves of one partition: partition length <= 16384
 
 }  // namespace
 
@@ -103,7 +103,7 @@ __device__ __forceinline__ int2 nth_pair(const int32_t* seq_lens, int B, int n_q
 //     wavefronts, the two splits of a row block on one SIMD, 256 columns
 //     each, so the accumulators (64 registers) and the rest fit the 256
 //     vector registers of two wavefronts per SIMD; one workgroup per CU.
-template <int PF, int RB, int SP, int NH, int MINW>
+template <int PF, int RB, int SP, int NH, int MINW, bool SK>
 __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnParams p) {
   static_assert(PF % 2 == 0, "tile n sits in LDS buffer n % 2");
   static_assert(NH == 1 || NH == 2, "16 or 32 keys per step");
@@ -137,33 +137,31 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
   const int R = p.Hq * p.n_q;                 // rows sharing the latent cache
   constexpr int rows_wg = 16 * RB;
   const int n_rg = (R + rows_wg - 1) / rows_wg;
-  // workgroup id = (chunk * n_rg + rg) * 8 + j: unit (sequence, partition)
-  // = chunk * 8 + j, so its row groups sit 8 ids apart on one XCD
+  // workgroup id = (chunk * n_rg + rg) * 8 + j: unit = chunk * 8 + j (a
+  // (sequence, partition) pair, or a stream-K worker), so the row groups of
+  // a unit sit 8 ids apart on one XCD and share its tiles through one L2
   const long wg = blockIdx.x;
   const int rg = (int)((wg / 8) % n_rg);
-  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);  // the unit-th live pair
-  if (unit >= (long)p.B * p.max_parts) return;
-  const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
-  const int2 bp = nth_pair(p.seq_lens, p.B, p.n_q, p.cap, P, (int)unit);
-  if (bp.x < 0) return;  // past the last live pair: whole workgroup
-  const int b = bp.x, part = bp.y;
-  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
-  if (L < p.n_q || L > p.cap) {
-    if (rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
-    return;  // whole workgroup
-  }
-  // partition part of n owns the steps (TK keys each) part, part + n, ...
-  const int nparts = (L + P - 1) / P;
-  const int start = part * TK, stride = nparts * TK, end = L;
+  const long unit = (wg / (8L * n_rg)) * 8 + (wg % 8);
 
+  __shared__ int s_blk[kMlaMaxTiles];
+
+  // One piece of work: the steps start, start + stride, ... below end (keys)
+  // of sequence b (L keys attended).  Its partials go, stream-K, to
+  // workspace row slot + i (i = r * Hq + h, the row within the sequence's R
+  // rows), else to row ((b * Hq + h) * n_q + r) * max_parts + slot (slot:
+  // the partition).  Every wavefront of the workgroup runs every piece (the
+  // barriers inside count all of them).
+  auto run_piece = [&](int b, int L, int start, int stride, int end, long slot) {
   // this wavefront's rows: i = r * Hq + h
   const int i_row = (rg * RB + rbw) * 16 + col;
   const bool rvalid = i_row < R;
   const int r_q = rvalid ? i_row / p.Hq : 0;
   const int h_q = rvalid ? i_row % p.Hq : 0;
-  const int lvis = rvalid ? L - p.n_q + r_q + 1 : L;
-  const long wrow = ((long)b * p.Hq + h_q) * p.n_q + r_q;
   const bool active = __any(rvalid);  // wave-uniform: the row block has rows
+  const int lvis = rvalid ? L - p.n_q + r_q + 1 : L;
+  const long orow = SK ? slot + i_row
+                       : (((long)b * p.Hq + h_q) * p.n_q + r_q) * p.max_parts + slot;
 
   bf16x8_t qf[KS];  // this split's steps of the absorbed queries (B operand of S^T)
   {
@@ -187,7 +185,7 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
   // load behind it.
   const int n_tiles = (end - start + stride - 1) / stride;  // NH * n_tiles <= kMlaMaxTiles (plan)
   const int bs_shift = __builtin_ctz((unsigned)(p.bs > 0 ? p.bs : 1));
-  __shared__ int s_blk[kMlaMaxTiles];
+  if constexpr (SK) __syncthreads();  // the previous piece's reads of s_blk, the tiles and s_ps are done
   if (p.table != nullptr) {
     for (int x = tid; x < NH * n_tiles; x += NTH) {
       const int key = start + (x / NH) * stride + (x % NH) * kTile;
@@ -384,17 +382,114 @@ __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnP
     }
   }
 
-  if (!rvalid) return;
-  float* wo = p.ws_o + (wrow * p.max_parts + part) * DV + sp * (DV / SP);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4_t*>(wo + dt * 16 + grp * 4) = oacc[dt];
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  if (sp == 0 && grp == 0) {  // every split holds the same statistics
-    float* wml = p.ws_ml + (wrow * p.max_parts + part) * 2;
-    wml[0] = m;
-    wml[1] = lt;
+  if (rvalid) {
+    float* wo = p.ws_o + orow * DV + sp * (DV / SP);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(wo + dt * 16 + grp * 4) = oacc[dt];
+    if (sp == 0 && grp == 0) {  // every split holds the same statistics
+      float* wml = p.ws_ml + orow * 2;
+      wml[0] = m;
+      wml[1] = lt;
+    }
+  }
+  };  // run_piece
+
+  // The pieces of this workgroup (one call site of run_piece in each form:
+  // the piece's code is large).
+  //   fixed partitions: the unit-th live (sequence, partition) pair;
+  //   partition part of n owns the steps part, part + n, ...;
+  //   stream-K: the lengths give T_b = ceil(L_b / TK) steps per sequence (0
+  //   for an invalid length, which worker 0 reports), W in all; worker w of
+  //   NW takes the steps [w W / NW, (w + 1) W / NW), a contiguous run that
+  //   may end one sequence and start the next, and every row group of the
+  //   worker takes the same run.  The piece (sequence b, worker w) leaves
+  //   its rows' partials at workspace rows (b + w) * R + i (unique: b and w
+  //   both grow along the runs); the worker holding a sequence's first step
+  //   records which workers cover it.
+  if constexpr (!SK) {
+    if (unit >= (long)p.B * p.max_parts) return;
+    const int P = part_tokens(p.seq_lens, p.B, p.cap, p.slots_u, p.P_lo, p.P);
+    const int2 bp = nth_pair(p.seq_lens, p.B, p.n_q, p.cap, P, (int)unit);
+    if (bp.x < 0) return;  // past the last live pair: whole workgroup
+    const int b = bp.x, part = bp.y;
+    const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+    if (L < p.n_q || L > p.cap) {
+      if (rg == 0 && tid == 0) report(p.status, KVC_ERR_DATA);
+      return;  // whole workgroup
+    }
+    const int nparts = (L + P - 1) / P;
+    run_piece(b, L, part * TK, nparts * TK, L, part);
+  } else {
+    if (unit >= p.sk_workers) return;
+    long W = 0;
+    int bad = 0;
+    for (int first = 0; first < p.B; first += kWave) {
+      const int i = first + lane;
+      int t = 0;
+      if (i < p.B) {
+        const int Li = p.seq_lens[i];
+        if (Li >= p.n_q && Li <= p.cap) t = (Li + TK - 1) / TK;
+        else bad = 1;
+      }
+      for (int mm = 1; mm < kWave; mm <<= 1) t += __shfl_xor(t, mm);
+      W += t;
+    }
+    if (unit == 0 && rg == 0 && __any(bad) && tid == 0) report(p.status, KVC_ERR_DATA);
+    W = __builtin_amdgcn_readfirstlane((int)W);
+    if (W == 0) return;
+    const long NW = min((long)p.sk_workers, max(1L, W / p.sk_min_tiles));
+    if (unit >= NW) return;
+    long pos = unit * W / NW;
+    const long s1 = (unit + 1) * W / NW;
+    if (pos >= s1) return;
+    // the sequence holding step pos: the first b with (steps before b + its steps) > pos
+    int b = 0;
+    long pre = 0;  // steps before sequence b
+    for (int first = 0; first < p.B; first += kWave) {
+      const int i = first + lane;
+      long n = 0;
+      if (i < p.B) {
+        const int Li = p.seq_lens[i];
+        if (Li >= p.n_q && Li <= p.cap) n = (Li + TK - 1) / TK;
+      }
+      long incl = n;
+      for (int d = 1; d < kWave; d <<= 1) {
+        const long t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+      }
+      const unsigned long long hit = __ballot(pos < pre + incl);
+      if (hit != 0) {
+        const int j = __ffsll((long long)hit) - 1;
+        b = first + j;
+        pre += __shfl(incl - n, j);
+        break;
+      }
+      pre += __shfl(incl, kWave - 1);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    pre = __builtin_amdgcn_readfirstlane((int)pre);
+    int L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+    int T = (L + TK - 1) / TK;  // >= 1: sequence b holds step pos
+    while (pos < s1) {
+      while (pos >= pre + T) {  // past sequence b: the next one with steps
+        pre += T;
+        ++b;
+        L = __builtin_amdgcn_readfirstlane(p.seq_lens[b]);
+        T = (L >= p.n_q && L <= p.cap) ? (L + TK - 1) / TK : 0;
+      }
+      const int t0 = (int)(pos - pre);
+      const int t1 = (int)min((long)T, t0 + (s1 - pos));
+      if (t0 == 0 && rg == 0 && tid == 0) {  // this worker starts the sequence: record its workers
+        const long x_last = pre + T - 1;
+        const int w_last = (int)(((x_last + 1) * NW - 1) / W);
+        p.sk_meta[b] = make_int2((int)unit, w_last);
+      }
+      run_piece(b, L, t0 * TK, TK, min(t1 * TK, L), (long)(b + unit) * R);
+      pos += t1 - t0;
+    }
   }
 }
 
@@ -411,15 +506,19 @@ hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s) {
   const int R = p.Hq * p.n_q;
   const long rows_wg = mla_rows_per_wg(R);
   const long n_rg = (R + rows_wg - 1) / rows_wg;
-  const long units = (long)p.B * p.max_parts;
+  const long units = p.sk_meta ? (long)p.sk_workers : (long)p.B * p.max_parts;
   const long n_wg = (units + 7) / 8 * 8 * n_rg;
   if (units == 0) return hipSuccess;
   if (n_wg > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n_wg);
-  if (R <= 16)
-    hipLaunchKernelGGL((partition_mla<kSmallPF, 1, 4, 1, kSmallWgs>), grid, dim3(4 * kWave), 0, s, p);
-  else
-    hipLaunchKernelGGL((partition_mla<2, 4, 2, 2, 1>), grid, dim3(8 * kWave), 0, s, p);
+  if (R <= 16) {
+    if (p.sk_meta) return hipErrorInvalidValue;  // the 16-row form has fixed partitions only
+    hipLaunchKernelGGL((partition_mla<kSmallPF, 1, 4, 1, kSmallWgs, false>), grid, dim3(4 * kWave), 0, s, p);
+  } else if (p.sk_meta) {
+    hipLaunchKernelGGL((partition_mla<2, 4, 2, 2, 1, true>), grid, dim3(8 * kWave), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((partition_mla<2, 4, 2, 2, 1, false>), grid, dim3(8 * kWave), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -259,6 +259,34 @@ Plan make_mla_plan(const kvc_cache_desc* d, int n_q) {
   pl.o_offset = kCntBytes;  // the counters of other calls sharing the workspace stay untouched
   pl.ml_offset = align256(pl.o_offset + o_bytes);
   pl.bytes = pl.ml_offset + rows * pl.max_parts * 2 * sizeof(float);
+  // More than 16 rows: by default the stream-K split, one round of
+  // workgroups, the same run of steps for every row group of a worker (so
+  // the row groups still share each tile through one L2), every worker the
+  // same number of steps.  With the partitions above the live (sequence,
+  // partition) pairs carry unequal numbers of steps (a sequence's last
+  // partition is short) and leave part of the round idle (128 heads, 32
+  // sequences of 1024-4096 keys: 226 of 256 workgroups, the longest 896
+  // keys against 759 on average; 87.5 -> 81.2 us stream-K).  The 16-row form
+  // measured slower stream-K (16 heads: 121.4 -> 125.5 us) and keeps the
+  // partitions.  A worker's run must fit the kernel's LDS staging of block
+  // ids: otherwise, and with an explicit length, fixed partitions.
+  const int tk = 2 * kTile;                // keys per step of the eight-wavefront kernel
+  const long w_round = one_round / n_rg;   // workers of one row group
+  const long max_steps = std::max((d->batch * ((cap + tk - 1) / tk) + w_round - 1) / w_round,
+                                  2L * kSkMinTiles);
+  if (R > 16 && d->partition_tokens == 0 && w_round >= 1 &&
+      max_steps * (tk / kTile) <= kMlaMaxTiles) {
+    pl.sk = true;
+    pl.P = pl.P_lo = pl.max_parts = pl.slots_u = 0;
+    pl.sk_workers = (int)w_round;
+    pl.rows_per_item = R;  // a segment is a whole sequence's rows
+    pl.sk_rows = R;
+    const size_t pieces = (size_t)d->batch + pl.sk_workers;
+    pl.o_offset = kCntBytes;
+    pl.ml_offset = align256(pl.o_offset + pieces * R * kMlaValueDim * sizeof(float));
+    pl.meta_offset = align256(pl.ml_offset + pieces * R * 2 * sizeof(float));
+    pl.bytes = pl.meta_offset + (size_t)d->batch * 2 * sizeof(int32_t);
+  }
   return pl;
 }
 

@@ -78,6 +78,10 @@ hipError_t launch_block_table_append(const BlockTableArgs& bt, const AppendArgs&
 // dtype: KVC_BF16 / KVC_F32; D: 64 / 128; mfma selects the grouped-rows kernel (bf16 only)
 constexpr int kMlaKeyDim = 576;    // MLA cache row: latent (512) + decoupled RoPE key (64)
 constexpr int kMlaValueDim = 512;  // the latent part, which also serves as the value
+// 16-key halves of one MLA piece of work whose block ids the kernel stages in
+// LDS: a partition, or a stream-K worker's run in one sequence, of at most
+// 16384 keys
+constexpr int kMlaMaxTiles = 1024;
 
 hipError_t launch_partition_valu(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mla(const AttnParams& p, hipStream_t s);

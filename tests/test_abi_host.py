@@ -220,12 +220,15 @@ def test_valu_stream_k_plan(lib):
 def test_mla_workspace_covers_launch_time_partitions(lib):
     # MLA whose full-capacity batch fits one round of resident workgroups:
     # launches may use partitions down to half the planned length, so the
-    # workspace holds twice the partitions; an explicit length keeps the count
-    for alias, planned in (("M1", 1024), ("M2", 2048)):
+    # workspace holds twice the partitions; an explicit length keeps the count.
+    # 16 rows (M2) use these partitions by default; more rows (M1, given an
+    # explicit length here) are checked for the explicit case only.
+    for alias, planned, explicits in (("M1", 1024, ((1024, 1),)),
+                                      ("M2", 2048, ((0, 2), (2048, 1)))):
         w = synth.get(alias)
         cap = synth.capacity_tokens(w)
         rows = w.B * w.Hq * w.n_q
-        for explicit, factor in ((0, 2), (planned, 1)):
+        for explicit, factor in explicits:
             dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
                       dtype=kvc.DTYPE_CODES[w.dtype], block_size=w.block_size, max_seq_len=cap,
                       max_blocks_per_seq=synth.max_blocks_per_seq(w),
@@ -234,6 +237,29 @@ def test_mla_workspace_covers_launch_time_partitions(lib):
             assert P == planned, (alias, P)
             parts = -(-cap // (P // factor))
             assert kvc.kvc_mla_workspace_bytes(dd, w.n_q, w.dv) == _ws_bytes(rows, parts, w.dv), alias
+
+
+def test_mla_stream_k_plan(lib):
+    # more than 16 rows by default: the stream-K split, one round of 256
+    # workgroups shared by the row groups (128 heads: two 64-row groups, 128
+    # workers), one partial per row of every (sequence, worker) piece (at
+    # most sequences + workers pieces) and one worker record per sequence
+    w = synth.get("M1")
+    cap = synth.capacity_tokens(w)
+    rows = w.Hq * w.n_q
+    for n_q, workers in ((1, 128), (2, 64)):  # 256 rows: four row groups
+        dd = desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                  dtype=kvc.DTYPE_CODES[w.dtype], block_size=w.block_size, max_seq_len=cap,
+                  max_blocks_per_seq=synth.max_blocks_per_seq(w), num_blocks=synth.pool_blocks(w))
+        assert kvc.kvc_mla_partition_tokens(dd, n_q, w.dv) == 0
+        assert kvc.kvc_mla_workspace_bytes(dd, n_q, w.dv) == _sk_bytes(
+            w.B + workers, rows * n_q, w.dv, w.B)
+    # a sequence too long for one worker's run in the kernel's block-id
+    # staging (128 workers of 16384 keys at most): fixed partitions
+    big = desc(batch=4096, num_q_heads=128, num_kv_heads=1, head_dim=576,
+               dtype=kvc.DTYPE_CODES["bf16"], block_size=64, max_seq_len=8192,
+               max_blocks_per_seq=128, num_blocks=4096 * 128)
+    assert kvc.kvc_mla_partition_tokens(big, 1, 512) > 0
 
 
 def test_status_strings(lib):

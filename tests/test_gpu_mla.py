@@ -1,7 +1,7 @@
 """GPU parity of MLA latent decode: attention of every head's absorbed query
 over the shared latent rows (keys = whole 576-wide rows, values = their first
 512 dims) against the oracle, for decode and verify rows, contiguous and
-paged caches; the full-size workloads are sampled."""
+paged caches, fixed partitions and the stream-K split."""
 import math
 
 import numpy as np
@@ -28,7 +28,12 @@ CASES = [
     # launch-time lengths with the live pairs packed: 24 sequences, and 70 (two
     # chunks of 64 lengths in the numbering)
     ("h16-paged16-b24-packed", 16, 1, 16, 24, 900, 0, None),
-    ("h128-paged64-b70-packed", 128, 1, 64, 70, 260, 0, None),
+    # more than 16 rows: the stream-K split by default (70 sequences: two
+    # chunks of 64 lengths in its scans; 300 short sequences: workers whose
+    # runs cross many sequences), fixed partitions with an explicit length
+    ("h128-paged64-b70-stream-k", 128, 1, 64, 70, 260, 0, None),
+    ("h32-paged16-b300-short-stream-k", 32, 1, 16, 300, 100, 0, None),
+    ("h128-paged64-P256-fixed", 128, 1, 64, 5, 900, 256, None),
 ]
 
 
