@@ -103,6 +103,8 @@ __device__ __forceinline__ int2 nth_pair(const int32_t* seq_lens, int B, int n_q
 //     wavefronts, the two splits of a row block on one SIMD, 256 columns
 //     each, so the accumulators (64 registers) and the rest fit the 256
 //     vector registers of two wavefronts per SIMD; one workgroup per CU.
+// SK: the workgroups are stream-K workers (the pieces are described below),
+// else (sequence, partition) pairs; the launch passes sk_meta exactly when SK.
 template <int PF, int RB, int SP, int NH, int MINW, bool SK>
 __global__ __launch_bounds__((RB * SP * kWave), (MINW)) void partition_mla(AttnParams p) {
   static_assert(PF % 2 == 0, "tile n sits in LDS buffer n % 2");

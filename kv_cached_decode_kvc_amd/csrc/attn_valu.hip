@@ -10,7 +10,9 @@
 // 0 .. L - n_q + r ("Inference-1", "KV cache": shifted causal mask).
 //
 // Used for MHA (one query row per KV row, so there is no dense contraction to
-// give to the matrix cores) and for every fp32 cache.  FP8 caches ("Inference
+// give to the matrix cores) and for every fp32 cache.  Paged bf16 and fp32
+// batches too large for one round of such work items run the stream-K form
+// instead (partition_valu_sk, at the end of this file).  FP8 caches ("Inference
 // o quy mo lon", 03 "KV cache quantization"; "Inference-2", "KV cache
 // quantization") hold one code per element and one scale per row: the row's
 // key scale multiplies the reduced dot product and its value scale joins the
