@@ -510,6 +510,10 @@ int kvc_mla_attn(const kvc_cache_desc* d, const void* q, int32_t n_q, const void
  * bf16 caches with head_dim 64 or 128 (others KVC_ERR_UNSUPPORTED); paged
  * caches with max_blocks_per_seq <= 4096.  No workspace: each query block
  * covers all its keys.  Bad lengths or offsets: KVC_ERR_DATA, rows skipped.
+ * Precision: scores in fp32 from bf16 products; the value products take the
+ * value entries as fp16 (exact for magnitudes up to 65504; larger value
+ * entries are outside the supported range and are not reported) and the
+ * softmax weights as fp16, with fp32 accumulation.
  */
 int kvc_prefill_attn(const kvc_cache_desc* d, const void* q, const int32_t* cu_q, int32_t total_q,
                      int32_t max_q, const void* k_cache, const void* v_cache,

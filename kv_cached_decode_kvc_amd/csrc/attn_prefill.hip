@@ -19,11 +19,17 @@
 // ring (one barrier per tile), with buffer loads of the default cache policy
 // so that the pair's other row blocks (placement below) find the rows in
 // their XCD's L2; each
-// wavefront contracts its 16 * NT rows on v_mfma_f32_16x16x32_bf16 (S^T =
-// K.Q^T with Q^T in registers, two 16-key halves; one online-softmax step
-// per 32 keys; O^T += V^T.P^T with V^T via ds_read_b64_tr_b16 and the weights
-// as bf16 hi and lo parts) and skips the tiles that lie entirely above its
-// rows' diagonal.  Outputs are normalised and written directly: there is no
+// wavefront contracts its 16 * NT rows on the matrix cores: S^T = K.Q^T on
+// v_mfma_f32_16x16x32_bf16 (Q^T in registers, two 16-key halves), one
+// online-softmax step per 32 keys, then O^T += V^T.P^T on
+// v_mfma_f32_16x16x32_f16 with V^T via ds_read_b64_tr_b16.  The value rows
+// are converted from bf16 to fp16 as they are stored to LDS (exact for
+// magnitudes up to 65504: fp16 carries more significand bits than bf16;
+// below 2^-14 the absolute error stays under 2^-24, and larger magnitudes
+// are outside the supported range), so the weights enter as one fp16 operand,
+// 2^-11 relative rounding, where bf16 weights would need a hi and a lo part.
+// A wavefront skips the tiles that lie entirely above its rows'
+// diagonal.  Outputs are normalised and written directly: there is no
 // split over keys.
 #include "launch.hpp"
 
@@ -32,6 +38,9 @@ namespace kvc {
 namespace {
 
 typedef short i16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kPfWaves = 4;
@@ -237,12 +246,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       s.v[u] = load_shared_l2((const uint8_t*)p.v + c * 2, lane_off);
     }
   };
+  // eight bf16 values -> eight fp16 values (round toward zero: exact in range)
+  auto to_f16 = [](uint4 x) -> uint4 {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[k]), bf16_hi(w[k])));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
   auto store = [&](const Stage& s, int buf) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       if (TCH % kPfThreads == 0 || u * kPfThreads + tid < TCH) {
         *reinterpret_cast<uint4*>(k_lds[buf] + lofs[u]) = s.k[u];
-        *reinterpret_cast<uint4*>(v_lds[buf] + vofs[u]) = s.v[u];
+        *reinterpret_cast<uint4*>(v_lds[buf] + vofs[u]) = to_f16(s.v[u]);
       }
     }
   };
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
   // 32 keys, then the value products.  A lane holds keys grp*4 .. +3 of each
   // half, so its value operand is the transposed read of those rows of half
   // 0 followed by the same rows of half 1 -- eight distinct keys -- and the
-  // weights enter as two products, bf16 hi parts then lo parts.
+  // weights enter as one fp16 operand.
   auto compute32 = [&](int t, int buf) {
     const uint8_t* ka_ptr = k_lds[buf] + col * ROWB + grp * 16;
     const uint8_t* va_ptr = v_lds[buf] + (grp * 4 + (col >> 2)) * VROWB + (col & 3) * 8;
@@ -262,7 +280,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
       for (int kk = 0; kk < KK; ++kk)
         ka[h][kk] = __builtin_bit_cast(bf16x8_t,
                                        *reinterpret_cast<const uint4*>(ka_ptr + h * 16 * ROWB + kk * 64));
-    bf16x8_t ph[NT], pl[NT];
+    f16x8_t ph[NT];
     f32x4_t sa[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sa[nt][0] = sa[nt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -310,40 +328,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
         pp[v] = f32x2_t{fast_exp2(sv[2 * v] - m_use), fast_exp2(sv[2 * v + 1] - m_use)};
       l[nt] += ((pp[0][0] + pp[0][1]) + (pp[1][0] + pp[1][1])) +
                ((pp[2][0] + pp[2][1]) + (pp[3][0] + pp[3][1]));
-      bf16x2_t hi[4], lo[4];
+      f16x2_t hh[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        hi[v] = __builtin_convertvector(pp[v], bf16x2_t);
-        lo[v] = __builtin_convertvector(pp[v] - __builtin_convertvector(hi[v], f32x2_t), bf16x2_t);
-      }
-      ph[nt] = __builtin_shufflevector(__builtin_shufflevector(hi[0], hi[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(hi[2], hi[3], 0, 1, 2, 3),
-                                       0, 1, 2, 3, 4, 5, 6, 7);
-      pl[nt] = __builtin_shufflevector(__builtin_shufflevector(lo[0], lo[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(lo[2], lo[3], 0, 1, 2, 3),
+      for (int v = 0; v < 4; ++v) hh[v] = __builtin_convertvector(pp[v], f16x2_t);
+      ph[nt] = __builtin_shufflevector(__builtin_shufflevector(hh[0], hh[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(hh[2], hh[3], 0, 1, 2, 3),
                                        0, 1, 2, 3, 4, 5, 6, 7);
     }
-    bf16x8_t vas[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       lds_i16x4_t* a0 = reinterpret_cast<lds_i16x4_t*>(
           (__attribute__((address_space(3))) uint8_t*)(va_ptr + dt * 32));
       lds_i16x4_t* a1 = reinterpret_cast<lds_i16x4_t*>(
           (__attribute__((address_space(3))) uint8_t*)(va_ptr + 16 * VROWB + dt * 32));
-      const bf16x4_t v0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0));
-      const bf16x4_t v1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1));
-      const bf16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      vas[dt] = va;
+      const f16x4_t v0 = __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0));
+      const f16x4_t v1 = __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1));
+      const f16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[nt], oacc[nt][dt], 0, 0, 0);
+        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph[nt], oacc[nt][dt], 0, 0, 0);
     }
-    // the lo products a full pass later: no accumulator is used twice in a row
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        oacc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vas[dt], pl[nt], oacc[nt][dt], 0, 0, 0);
   };
 
   // Tile k lives in register stage k % 2 and then LDS buffer k % 2.  Step n

@@ -23,7 +23,7 @@ CASES = [
 ]
 
 
-def _chunk_case(ref, name, out_dtype, D, Hq, Hkv, bs, B, chunk_hi, cached_hi, seed=0):
+def _chunk_case(ref, name, out_dtype, D, Hq, Hkv, bs, B, chunk_hi, cached_hi, seed=0, v_scale=1.0):
     rng = np.random.default_rng(5000 + D + Hq + seed)
     w = synth.custom(name=name, seed=5100 + seed, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
                      block_size=bs, n_q=1, len_lo=1, len_hi=chunk_hi + cached_hi + 1,
@@ -39,6 +39,10 @@ def _chunk_case(ref, name, out_dtype, D, Hq, Hkv, bs, B, chunk_hi, cached_hi, se
     total = int(chunk.sum())
     kr = synth.normal(w, (total, Hkv, D), synth.S_KNEW, 55, seed)
     vr = synth.normal(w, (total, Hkv, D), synth.S_VNEW, 55, seed)
+    if v_scale != 1.0:  # scaled new value rows, re-encoded as bf16 bits
+        f = (vr.astype(np.uint32) << 16).view(np.float32)
+        f = np.clip(f * np.float32(v_scale), -6e4, 6e4).astype(np.float32)
+        vr = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     q = synth.normal(w, (total, Hq, D), synth.S_Q, 55, seed)
     gc.add_tokens(kr, vr, chunk)
     cu = synth.cu_from_counts(chunk)
@@ -58,13 +62,23 @@ def _chunk_case(ref, name, out_dtype, D, Hq, Hkv, bs, B, chunk_hi, cached_hi, se
         want = ref.attention(q[cu[b]:cu[b + 1]], k.transpose(1, 0, 2).copy(),
                              v.transpose(1, 0, 2).copy(), scale, "bf16")
         g = got[cu[b]:cu[b + 1]]
-        assert_close(g, want, "%s b=%d cached=%d chunk=%d" % (name, b, cached[b], n),
+        # attention is linear in the values: compare in units of the value scale
+        assert_close(g / v_scale, want / v_scale,
+                     "%s b=%d cached=%d chunk=%d" % (name, b, cached[b], n),
                      bf16_out=out_dtype == "bf16")
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_prefill_parity(ref, case):
     _chunk_case(ref, *case)
+
+
+def test_prefill_large_value_entries(ref):
+    """Value entries up to 6e4 in magnitude (prompt rows only, so every value
+    row is scaled): the kernel's fp16 value operand holds every bf16 value of
+    magnitude up to 65504 exactly, so the outputs, in units of the value scale
+    (attention is linear in the values), keep the usual tolerance."""
+    _chunk_case(ref, "mha-d128-paged-large-v", "f32", 128, 4, 4, 16, 3, 260, 0, v_scale=2e4)
 
 
 def test_prefill_chunks_equal_one_pass(ref):
