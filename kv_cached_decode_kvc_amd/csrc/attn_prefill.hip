@@ -405,7 +405,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_mfma(PrefillParams p) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int out_dtype, hipStream_t s) {
-  constexpr int NT = 2;
+  // 48 rows per wavefront (192 per workgroup): each K/V tile staged and read
+  // from LDS serves 1.5x the rows of 32 at 252 registers, still two
+  // wavefronts per SIMD
+  constexpr int NT = 3;
   const long rows_wg = kPfWaves * 16 * NT;
   const long n_rt = ((long)p.max_q * p.G + rows_wg - 1) / rows_wg;
   if (n_rt == 0 || p.B == 0 || p.Hkv == 0) return hipSuccess;
